@@ -1,0 +1,208 @@
+"""Benchmark: chunked exact causal attention forward + backward on one MI355X.
+
+One step is one pass of the whole hot path over one sequence: the forward of
+every chunk in ascending order (SeCO's inference-mode pass), then the backward
+of every chunk in descending order into zeroed float32 dK/dV accumulators (for
+the sparse workload: the t selected chunks, scaled by k/t). Inputs are resident
+in HBM before timing starts. Prints one JSON line on stdout.
+
+FLOPs are causal only: 4*d per visible (query, key) pair and q head for the
+forward (S and PV) and 10*d for the backward (S recompute, dP, dV, dQ, dK).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunked causal attn fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(start: int, length: int) -> int:
+    """Visible (query, key) pairs of one chunk for one head."""
+    return length * start + length * (length + 1) // 2
+
+
+def flop_plan(wl, selected):
+    d, hq = wl.head_dim, wl.n_q_heads
+    chunks = [wl.chunk_bounds(i) for i in range(wl.n_chunks)]
+    fwd_pairs = sum(causal_pairs(s, c) for s, c in chunks)
+    bwd_chunks = selected if selected is not None else range(wl.n_chunks)
+    bwd_pairs = sum(causal_pairs(*chunks[i]) for i in bwd_chunks)
+    return {
+        "fwd": 4 * d * hq * fwd_pairs,
+        "bwd": 10 * d * hq * bwd_pairs,
+        "dkdv": 8 * d * hq * bwd_pairs,     # S recompute, dP, dV, dK
+        "bwd_pairs": bwd_pairs,
+        "fwd_pairs": fwd_pairs,
+    }
+
+
+def cpu_baseline(wl, inp_raw):
+    """The float64 oracle on a bounded sample, extrapolated by causal FLOPs."""
+    import numpy as np
+    from oracle import attention as A
+    from sequence_chunked_exact_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+
+    def head(name, h):
+        a = inp_raw[name][:, h:h + 1]
+        return W.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+    q, k, v, do = head("q", 0), head("k", 0), head("v", 0), head("do", 0)
+    s, c = wl.chunk_bounds(wl.n_chunks - 1)
+    rows = np.arange(s + c - min(c, 512), s + c)
+    t0 = time.perf_counter()
+    A.forward(q, k, v, wl.softmax_scale, rows=rows)
+    A.backward(q, k, v, do, wl.softmax_scale, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = int(sum(int(r) + 1 for r in rows))
+    sample_flops = 14 * wl.head_dim * pairs
+    rate = sample_flops / dt
+    plan = flop_plan(wl, None)
+    total = plan["fwd"] + plan["bwd"]
+    tokens_per_s = wl.seq_len * rate / total
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle forward+backward of query rows [{rows[0]}, {rows[-1] + 1}) of one "
+                      f"query head against its full causal prefix ({pairs} visible pairs, {dt:.1f} s, "
+                      f"{rate / 1e9:.2f} GFLOP/s), extrapolated to the whole workload by causal FLOPs",
+            "seconds": dt, "gflops": rate / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="8b_layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sequence_chunked_exact_amd import binding as B
+    from sequence_chunked_exact_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {wl.name} inputs")
+    inp = W.make_inputs(wl, keep_f64=False)
+    q, k, v, do = (W.to_torch(inp.raw[n], dev) for n in ("q", "k", "v", "do"))
+    T, C = wl.seq_len, wl.chunk
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    desc = B.make_desc(q, k, chunk_start=0, chunk_len=C, softmax_scale=wl.softmax_scale)
+    ws = torch.empty(max(B.chunk_attn_workspace_size(desc, B.CA_OP_SPARSE_BWD), 256), dtype=torch.uint8,
+                     device=dev)
+    sparse = wl.sparse_t > 0
+    t_sel = wl.sparse_t if sparse else wl.n_chunks      # t = k: every chunk, scale 1
+    seed = wl.select_seed
+
+    def step():
+        B.chunked_forward(q, k, v, o, lse, chunk=C, softmax_scale=wl.softmax_scale)
+        return B.sparse_chunk_bwd(q, k, v, o, lse, do, dq, dk, dv, seq_len=T, chunk=C, t=t_sel, seed=seed,
+                                  softmax_scale=wl.softmax_scale, workspace=ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        selected = step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    B.profile_start()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        selected = step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    B.profile_stop()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = B.profile_read()
+    log(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms/step)")
+
+    plan = flop_plan(wl, selected if sparse else None)
+    total_flops = plan["fwd"] + plan["bwd"]
+    tflops = total_flops / (ms * 1e-3) / 1e12
+    kernels = {}
+    for name, (n, tot) in prof.items():
+        if n:
+            kernels[name] = {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps,
+                             "avg_us": tot / n * 1e3}
+    log("[bench] kernels " + json.dumps(kernels))
+    # roofline for the kernel with the most GPU time
+    dom = max(kernels, key=lambda n_: kernels[n_]["ms_per_step"])
+    dom_flops = {"fwd": plan["fwd"], "dkdv": plan["dkdv"]}.get(dom)
+    n_launch, tot_ms = prof[dom]
+    if dom_flops is not None:
+        per_launch_flops = dom_flops / (n_launch / args.steps)
+        avg_s = tot_ms / n_launch * 1e-3
+        achieved = per_launch_flops / avg_s / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_launch_us": avg_s * 1e6, "flops_per_launch": per_launch_flops}
+    else:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": None, "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": T, "chunk": C,
+                   "n_chunks": wl.n_chunks, "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "softmax_scale": wl.softmax_scale,
+                   "key_spike": (f"rank {wl.spike_rank} amplitude {wl.spike_amp}" if wl.spike_rank else None),
+                   "sparse_t": wl.sparse_t or None, "selected_chunks": selected if sparse else None,
+                   "causal_flops_per_step": total_flops},
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(wl, inp.raw)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

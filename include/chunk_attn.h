@@ -1,0 +1,171 @@
+/*
+ * chunk_attn.h - exact causal attention for one sequence chunk on MI355X (gfx950).
+ *
+ * The operation. A long sequence of T positions is cut into chunks; chunk i
+ * starts at global position s_i and holds C_i positions. Its queries Q^(i)
+ * attend to the cached key/value prefix K^(:i), V^(:i) (rows [0, s_i + C_i))
+ * under the causal mask, query row r (global position s_i + r) seeing key j
+ * iff j <= s_i + r. StreamBP's Property 3.1 says that chunk i's backward needs
+ * only O^(i), Q^(i), K^(:i), V^(:i), and its Eq. (1) says that summing the
+ * per-chunk contributions gives the full-sequence gradient (StreamBP review,
+ * "What carries the argument"; Eqs. (12)-(14) for the partitioned attention).
+ * SeCO keeps the K/V caches as checkpoints and backpropagates one chunk at a
+ * time; SpaCO backpropagates only t of the k chunks and scales them by k/t
+ * (SeCO/SpaCO review, "What carries the argument" and Referee Report summary).
+ *
+ * Per query head h (kv head h / (Hq/Hkv)):
+ *   S = scale * Q^(i) K^(:i)^T (masked), LSE = ln sum exp S, P = exp(S - LSE),
+ *   O^(i) = P V^(:i);  backward: dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+ *   dQ^(i) = scale dS K,  dK^(:i) += scale dS^T Q^(i),  dV^(:i) += P^T dO.
+ *
+ * Tensor layout. All tensors are row-major [batch][heads][rows][head_dim] with
+ * head_dim contiguous: q, o, dout, dq have n_q_heads heads and q_capacity rows;
+ * k, v, dk_acc, dv_acc have n_kv_heads heads and kv_capacity rows; lse is
+ * [batch][n_q_heads][q_capacity]. The chunk's rows inside the q-side tensors
+ * begin at q_row_offset (0 for per-chunk tensors, s_i for whole-sequence ones).
+ * q, k, v, o, dout are float32 or bfloat16 (dtype); lse, dq, dk_acc, dv_acc
+ * are always float32. Device pointers must be 16-byte aligned.
+ *
+ * Ownership and ordering. The caller allocates and owns every buffer,
+ * including the workspace; the library keeps no device memory of its own and
+ * frees nothing. Work is enqueued on the caller's HIP stream (a hipStream_t
+ * passed as void*; NULL is the default stream) and returns before it runs.
+ * Outputs must not alias inputs or each other.
+ *
+ * Errors. Every function returns 0 on success or a negative CA_ERR_* code. All
+ * argument checks happen before any device call, so a rejected call enqueues
+ * nothing. chunk_attn_last_error() gives a detail string for the calling
+ * thread. No C++ exception crosses this boundary.
+ */
+#ifndef CHUNK_ATTN_H
+#define CHUNK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CA_OK = 0,
+  CA_ERR_NULL = -1,        /* a required pointer is NULL */
+  CA_ERR_SHAPE = -2,       /* sizes out of range or inconsistent */
+  CA_ERR_DTYPE = -3,       /* dtype is not CA_F32 or CA_BF16 */
+  CA_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
+  CA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  CA_ERR_UNSUPPORTED = -6, /* head_dim other than 64 or 128 */
+  CA_ERR_HIP = -7          /* the HIP runtime reported an error */
+};
+
+enum { CA_F32 = 0, CA_BF16 = 1 };
+
+enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2 };
+
+typedef struct {
+  int32_t batch;         /* >= 1 */
+  int32_t n_q_heads;     /* Hq >= 1, a multiple of n_kv_heads */
+  int32_t n_kv_heads;    /* Hkv >= 1; q head h reads kv head h / (Hq/Hkv) */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t kv_capacity;   /* rows per head in k, v, dk_acc, dv_acc; >= chunk_start + chunk_len */
+  int32_t q_capacity;    /* rows per head in q, o, dout, dq, lse; >= q_row_offset + chunk_len */
+  int32_t q_row_offset;  /* row of the chunk's first query in the q-side tensors */
+  int32_t chunk_start;   /* s_i: global position of the chunk's first query, >= 0 */
+  int32_t chunk_len;     /* C_i >= 1 */
+  float softmax_scale;   /* multiplies Q K^T; any finite value */
+  int32_t dtype;         /* CA_F32 or CA_BF16: type of q, k, v, o, dout */
+} chunk_attn_desc;
+
+/* Bytes of workspace the op needs for this descriptor (0 if none; the op then
+ * accepts ws == NULL). op is CA_OP_*. For CA_OP_SPARSE_BWD the descriptor is
+ * the whole-sequence one that sparse_chunk_bwd takes and chunk_len must be the
+ * chunk size. Returns 0 for an invalid descriptor. */
+size_t chunk_attn_workspace_size(const chunk_attn_desc* desc, int32_t op);
+
+/* Forward of one chunk (the inference-mode pass that fills the caches in SeCO,
+ * SeCO/SpaCO review Referee Report summary; StreamBP Eq. (13) partitioned
+ * softmax). Writes o rows [q_row_offset, +chunk_len) in dtype and lse (natural
+ * log of the row's sum of exp(S)) in float32. Reads k, v rows [0, chunk_start +
+ * chunk_len). ws may be NULL (no workspace needed). */
+int chunk_attn_fwd(const chunk_attn_desc* desc, const void* q, const void* k, const void* v,
+                   void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of one chunk (StreamBP Property 3.1: needs only O^(i), Q^(i),
+ * K^(:i), V^(:i); Eq. (1): chunk contributions add up to the full gradient).
+ * o and lse are this chunk's forward outputs. dq rows of the chunk are
+ * OVERWRITTEN with grad_scale * dQ^(i); dk_acc and dv_acc rows
+ * [0, chunk_start + chunk_len) are INCREMENTED by grad_scale * dK^(:i) and
+ * grad_scale * dV^(:i) without atomics (each element has one writer), so the
+ * caller zeroes them before the first chunk of a sweep and chunks of one sweep
+ * must be issued in stream order. grad_scale is SpaCO's k/t for a sparse sweep
+ * and 1 otherwise. Workspace: chunk_attn_workspace_size(desc, CA_OP_BWD). */
+int chunk_attn_bwd(const chunk_attn_desc* desc, const void* q, const void* k, const void* v,
+                   const void* o, const float* lse, const void* dout, float grad_scale,
+                   float* dq, float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* acc[b][h][r][:] += scale * src[b][h][r][:] for r < prefix_len (float32,
+ * device pointers). This is the relay of an accumulated cache gradient,
+ * m_i.grad <- (k/t) * m'_i.grad in SpaCO (SeCO/SpaCO review, Referee Report
+ * major comments on Section 5 and Algorithm 2). acc has acc_capacity rows per
+ * head, src has src_capacity; both need prefix_len <= capacity. */
+int prefix_grad_accumulate(float* acc, const float* src, int32_t batch, int32_t n_heads,
+                           int32_t acc_capacity, int32_t src_capacity, int32_t head_dim,
+                           int32_t prefix_len, float scale, void* stream);
+
+/* SpaCO's chunk sample: t distinct indices out of [0, k), without replacement
+ * (SeCO/SpaCO review, Referee Report major comment 1). The random source is
+ * SplitMix64 seeded with seed, driving a partial Fisher-Yates shuffle of
+ * 0..k-1 stopped after t swaps (swap position i with i + next() mod (k - i));
+ * the chosen indices are written to the host array out_sorted[t] in ascending
+ * order. Pure host code. Errors: CA_ERR_NULL, CA_ERR_SHAPE (t < 1 or t > k). */
+int chunk_select(int32_t k, int32_t t, uint64_t seed, int32_t* out_sorted);
+
+/* Sparse chunk backward over a whole sequence of seq_len positions cut into
+ * k = ceil(seq_len / chunk_len) chunks of desc->chunk_len (the last may be
+ * short). Selects t chunks with chunk_select(k, t, seed), zeroes dq, dk, dv,
+ * then runs chunk_attn_bwd on the selected chunks in descending order with
+ * grad_scale = k/t, the compensation factor SpaCO applies to the selected
+ * chunks (SeCO/SpaCO review, "What carries the argument"). With t = k it is
+ * the exact chunked backward (SeCO). q, o, dout, dq, lse are whole-sequence
+ * tensors (q_capacity >= seq_len) and o, lse come from forwards of all
+ * chunks; desc->chunk_start and q_row_offset are ignored. The selected indices
+ * go to the host array selected_out[t]. Workspace:
+ * chunk_attn_workspace_size(desc, CA_OP_SPARSE_BWD). */
+int sparse_chunk_bwd(const chunk_attn_desc* desc, int32_t seq_len, int32_t t, uint64_t seed,
+                     const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                     int32_t* selected_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel timing for benchmarks (instrumentation only; results are unchanged).
+ * chunk_attn_profile_start() clears the record and, until
+ * chunk_attn_profile_stop(), brackets every kernel this library launches with
+ * two HIP events recorded on the launching stream. chunk_attn_profile_read()
+ * waits for the recorded events and returns, for one kernel id, the number of
+ * launches and their summed GPU time in milliseconds. Events are created on
+ * first use and reused; start/stop/read are serialized by a lock. Returns
+ * CA_ERR_SHAPE for an unknown kernel id and CA_ERR_HIP on a runtime error. */
+enum {
+  CA_KERNEL_FWD = 0,        /* chunk forward */
+  CA_KERNEL_DELTA = 1,      /* rowsum(dO * O) */
+  CA_KERNEL_DKDV = 2,       /* dK/dV accumulation over the prefix */
+  CA_KERNEL_DQ = 3,         /* dQ of the chunk */
+  CA_KERNEL_ACCUMULATE = 4, /* prefix_grad_accumulate */
+  CA_KERNEL_ZERO = 5,       /* zero fill used by sparse_chunk_bwd */
+  CA_KERNEL_COUNT = 6
+};
+int chunk_attn_profile_start(void);
+int chunk_attn_profile_stop(void);
+int chunk_attn_profile_read(int32_t kernel, int64_t* launches, double* total_ms);
+
+/* Static name of an error code. */
+const char* chunk_attn_strerror(int code);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* chunk_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNK_ATTN_H */

@@ -1,0 +1,223 @@
+"""ctypes binding over libchunk_attn.so (the C ABI in include/chunk_attn.h).
+
+Argument marshalling only: tensors are torch tensors on the GPU, passed by
+data pointer together with torch's current HIP stream. Every step of the
+computation runs in the library's HIP kernels. If the library is missing the
+import fails; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libchunk_attn.so")
+
+CA_F32, CA_BF16 = 0, 1
+CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD = 0, 1, 2
+KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5}
+ERRORS = {0: "CA_OK", -1: "CA_ERR_NULL", -2: "CA_ERR_SHAPE", -3: "CA_ERR_DTYPE", -4: "CA_ERR_ALIGN",
+          -5: "CA_ERR_WORKSPACE", -6: "CA_ERR_UNSUPPORTED", -7: "CA_ERR_HIP"}
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("kv_capacity", ctypes.c_int32),
+        ("q_capacity", ctypes.c_int32),
+        ("q_row_offset", ctypes.c_int32),
+        ("chunk_start", ctypes.c_int32),
+        ("chunk_len", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class ChunkAttnError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {detail}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python sequence_chunked_exact_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, U64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
+    D = ctypes.POINTER(Desc)
+    sig = {
+        "chunk_attn_workspace_size": (SZ, [D, I32]),
+        "chunk_attn_fwd": (ctypes.c_int, [D, P, P, P, P, P, P, SZ, P]),
+        "chunk_attn_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, F, P, P, P, P, SZ, P]),
+        "prefix_grad_accumulate": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, I32, F, P]),
+        "chunk_select": (ctypes.c_int, [I32, I32, U64, ctypes.POINTER(I32)]),
+        "sparse_chunk_bwd": (ctypes.c_int, [D, I32, I32, U64, P, P, P, P, P, P, P, P, P,
+                                            ctypes.POINTER(I32), P, SZ, P]),
+        "chunk_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "chunk_attn_last_error": (ctypes.c_char_p, []),
+        "chunk_attn_profile_start": (ctypes.c_int, []),
+        "chunk_attn_profile_stop": (ctypes.c_int, []),
+        "chunk_attn_profile_read": (ctypes.c_int, [I32, ctypes.POINTER(ctypes.c_int64),
+                                                   ctypes.POINTER(ctypes.c_double)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise ChunkAttnError(rc, lib.chunk_attn_last_error().decode())
+
+
+def _ptr(t) -> int:
+    return t.data_ptr()
+
+
+def _stream(t) -> Optional[int]:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CA_BF16
+    if t.dtype == torch.float32:
+        return CA_F32
+    raise TypeError(f"q/k/v/o/dout must be float32 or bfloat16, got {t.dtype}")
+
+
+def make_desc(q, k, *, chunk_start: int, chunk_len: int, q_row_offset: int = 0,
+              softmax_scale: float = 1.0) -> Desc:
+    """Descriptor from [B, Hq, q_capacity, d] queries and [B, Hkv, kv_capacity, d] keys."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D [batch, heads, rows, head_dim]")
+    B, Hq, Tq, d = q.shape
+    _, Hkv, Tk, _ = k.shape
+    return Desc(B, Hq, Hkv, d, Tk, Tq, q_row_offset, chunk_start, chunk_len, float(softmax_scale),
+                _dtype_code(q))
+
+
+def _contig(*ts):
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def chunk_attn_workspace_size(desc: Desc, op: int) -> int:
+    return int(lib.chunk_attn_workspace_size(ctypes.byref(desc), op))
+
+
+def _workspace(desc: Desc, op: int, like, ws):
+    import torch
+    need = chunk_attn_workspace_size(desc, op)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=like.device)
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
+def chunk_attn_fwd(q, k, v, o, lse, *, chunk_start: int, chunk_len: int, q_row_offset: int = 0,
+                   softmax_scale: float = 1.0):
+    """Forward of one chunk; writes o and lse rows [q_row_offset, +chunk_len)."""
+    _contig(q, k, v, o, lse)
+    desc = make_desc(q, k, chunk_start=chunk_start, chunk_len=chunk_len, q_row_offset=q_row_offset,
+                     softmax_scale=softmax_scale)
+    _check(lib.chunk_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              None, 0, _stream(q)))
+
+
+def chunk_attn_bwd(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, *, chunk_start: int, chunk_len: int,
+                   q_row_offset: int = 0, softmax_scale: float = 1.0, grad_scale: float = 1.0,
+                   workspace=None):
+    """Backward of one chunk: dq rows overwritten, dk_acc/dv_acc prefix rows incremented."""
+    _contig(q, k, v, o, lse, dout, dq, dk_acc, dv_acc)
+    desc = make_desc(q, k, chunk_start=chunk_start, chunk_len=chunk_len, q_row_offset=q_row_offset,
+                     softmax_scale=softmax_scale)
+    ws, nbytes = _workspace(desc, CA_OP_BWD, q, workspace)
+    _check(lib.chunk_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              _ptr(dout), float(grad_scale), _ptr(dq), _ptr(dk_acc), _ptr(dv_acc),
+                              None if ws is None else _ptr(ws), nbytes, _stream(q)))
+
+
+def prefix_grad_accumulate(acc, src, prefix_len: int, scale: float = 1.0):
+    """acc[:, :, :prefix_len] += scale * src[:, :, :prefix_len] (float32, [B, H, rows, d])."""
+    _contig(acc, src)
+    B, H, Ta, d = acc.shape
+    Ts = src.shape[2]
+    _check(lib.prefix_grad_accumulate(_ptr(acc), _ptr(src), B, H, Ta, Ts, d, int(prefix_len),
+                                      float(scale), _stream(acc)))
+
+
+def chunk_select(k: int, t: int, seed: int) -> list:
+    out = (ctypes.c_int32 * max(t, 1))()
+    _check(lib.chunk_select(int(k), int(t), ctypes.c_uint64(seed & (2**64 - 1)), out))
+    return list(out[:t])
+
+
+def sparse_chunk_bwd(q, k, v, o, lse, dout, dq, dk, dv, *, seq_len: int, chunk: int, t: int, seed: int,
+                     softmax_scale: float = 1.0, workspace=None) -> list:
+    """SpaCO backward over t of the k chunks (scaled by k/t); returns the selected chunks."""
+    _contig(q, k, v, o, lse, dout, dq, dk, dv)
+    desc = make_desc(q, k, chunk_start=0, chunk_len=chunk, softmax_scale=softmax_scale)
+    ws, nbytes = _workspace(desc, CA_OP_SPARSE_BWD, q, workspace)
+    sel = (ctypes.c_int32 * t)()
+    _check(lib.sparse_chunk_bwd(ctypes.byref(desc), int(seq_len), int(t),
+                                ctypes.c_uint64(seed & (2**64 - 1)), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), sel,
+                                None if ws is None else _ptr(ws), nbytes, _stream(q)))
+    return list(sel)
+
+
+def chunked_forward(q, k, v, o, lse, *, chunk: int, seq_len: Optional[int] = None,
+                    softmax_scale: float = 1.0, chunks: Optional[Sequence[int]] = None):
+    """SeCO's inference-mode pass: chunk_attn_fwd on every chunk in ascending order."""
+    T = q.shape[2] if seq_len is None else seq_len
+    n = -(-T // chunk)
+    for i in (range(n) if chunks is None else chunks):
+        s = i * chunk
+        chunk_attn_fwd(q, k, v, o, lse, chunk_start=s, chunk_len=min(chunk, T - s), q_row_offset=s,
+                       softmax_scale=softmax_scale)
+
+
+def chunked_backward(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, *, chunk: int,
+                     seq_len: Optional[int] = None, softmax_scale: float = 1.0, workspace=None):
+    """Exact chunked backward (SeCO): every chunk, descending, into zeroed accumulators."""
+    T = q.shape[2] if seq_len is None else seq_len
+    n = -(-T // chunk)
+    if workspace is None:
+        desc = make_desc(q, k, chunk_start=0, chunk_len=chunk, softmax_scale=softmax_scale)
+        workspace, _ = _workspace(desc, CA_OP_BWD, q, None)
+    for i in reversed(range(n)):
+        s = i * chunk
+        chunk_attn_bwd(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, chunk_start=s,
+                       chunk_len=min(chunk, T - s), q_row_offset=s, softmax_scale=softmax_scale,
+                       workspace=workspace)
+
+
+def profile_start():
+    """Bracket every later kernel launch with HIP events (see chunk_attn.h)."""
+    _check(lib.chunk_attn_profile_start())
+
+
+def profile_stop():
+    _check(lib.chunk_attn_profile_stop())
+
+
+def profile_read() -> dict:
+    """{kernel name: (launches, total GPU ms)} for the launches since profile_start()."""
+    out = {}
+    for name, kid in KERNELS.items():
+        n, ms = ctypes.c_int64(), ctypes.c_double()
+        _check(lib.chunk_attn_profile_read(kid, ctypes.byref(n), ctypes.byref(ms)))
+        out[name] = (int(n.value), float(ms.value))
+    return out

@@ -1,0 +1,803 @@
+// Chunked exact causal attention for gfx950 (CDNA4): forward, and the
+// backward split into a row-delta pass, a dK/dV pass and a dQ pass.
+//
+// What is computed (StreamBP review, "What carries the argument": Property 3.1
+// and the partitioned attention of Eqs. (12)-(14)): chunk i's queries, at
+// global positions start + r, attend to keys [0, start + len) with key j
+// visible iff j <= start + r. Per q head h and kv head h / (Hq/Hkv):
+//   S = scale Q K^T, P = softmax over visible keys, O = P V, LSE = ln sum exp S
+//   dS = P * (dO V^T - delta), delta_r = dO_r . O_r
+//   dQ = scale dS K,  dK += scale dS^T Q,  dV += P^T dO   (summed over the group)
+//
+// Matrix products run on v_mfma_f32_16x16x32_bf16 (bf16 storage) or
+// v_mfma_f32_16x16x4_f32 (float32 storage, eight of them per 32-deep step),
+// always accumulating in float32. For a 16x16 output tile, lane l (n = l % 16,
+// g = l / 16) holds rows 4g..4g+3 of column n. A and B operands give each lane
+// 8 contraction slots; lane l feeds row/column n. Two slot orders are used:
+//   contiguous: slot s <-> index 8g + s (operands read straight from memory)
+//   tile order: slot s <-> 4g + s for s < 4, 16 + 4g + (s - 4) for s >= 4,
+// the second being what a lane already holds from two stacked output tiles, so
+// P and dS feed the next product from registers with no data movement. Both
+// operands of a product always use the same order, which is all a k-reduction
+// needs.
+//
+// Layout choices:
+//  * forward / dQ: S^T = K Q^T per key tile, so each lane owns one query column
+//    and softmax statistics need no shuffles except the 4-lane max.
+//  * dK/dV: S = Q K^T per query tile, so P and dS are already key-major for
+//    dV = P^T dO and dK = dS^T Q; Q and dO are staged in LDS both row-major and
+//    transposed.
+//  * every dK/dV element is owned by one lane of one workgroup, which adds its
+//    total into the float32 accumulator once: no atomics.
+#include "launch.h"
+
+#include "chunk_attn.h"
+
+#include <math.h>
+
+namespace ca {
+namespace {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kInf = __builtin_huge_valf();
+
+template <typename T>
+struct Elt;
+
+template <>
+struct Elt<bf16> {
+  using frag = bf16x8;  // a lane's 8 contraction slots
+  using vec = bf16x8;   // 16-byte memory vector
+  using quad = bf16x4;
+  static constexpr int VEC = 8;
+  static __device__ __forceinline__ void mma(f32x4& c, const frag& a, const frag& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Elt<float> {
+  using frag = f32x8;
+  using vec = f32x4;
+  using quad = f32x4;
+  static constexpr int VEC = 4;
+  static __device__ __forceinline__ void mma(f32x4& c, const frag& a, const frag& b) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 8 consecutive elements -> fragment (contiguous slot order).
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ f32x8 ld8(const float* p) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// elements p[0..3] and p[16..19] -> fragment (tile slot order).
+__device__ __forceinline__ bf16x8 ld44(const bf16* p) {
+  const bf16x4 a = *(const bf16x4*)p, b = *(const bf16x4*)(p + 16);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x8 ld44(const float* p) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 16);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Two stacked output tiles' registers -> fragment in tile slot order.
+template <typename T>
+__device__ __forceinline__ typename Elt<T>::frag pack44(const f32x4& lo, const f32x4& hi) {
+  typename Elt<T>::frag f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = (T)lo[i];
+    f[4 + i] = (T)hi[i];
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, const f32x4& x, float mul) {
+  typename Elt<T>::quad v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (T)(x[i] * mul);
+  *(typename Elt<T>::quad*)dst = v;
+}
+
+__device__ __forceinline__ uint32_t bits16(bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+
+// Store R consecutive elements (R * sizeof(T) bytes, naturally aligned up to 16).
+template <typename T, int R>
+__device__ __forceinline__ void store_run(T* dst, const T (&x)[R]) {
+  if constexpr (sizeof(T) == 2) {
+    static_assert(R % 2 == 0, "bf16 runs hold an even count");
+    uint32_t w[R / 2];
+#pragma unroll
+    for (int i = 0; i < R / 2; ++i) w[i] = bits16(x[2 * i]) | (bits16(x[2 * i + 1]) << 16);
+    if constexpr (R == 2) {
+      *(uint32_t*)dst = w[0];
+    } else if constexpr (R == 4) {
+      *(u32x2*)dst = u32x2{w[0], w[1]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < R / 8; ++i)
+        *((u32x4*)dst + i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    }
+  } else {
+    static_assert(R % 4 == 0, "float runs hold a multiple of four");
+#pragma unroll
+    for (int i = 0; i < R / 4; ++i)
+      *((f32x4*)dst + i) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+  }
+}
+
+// A [ROWS][D] tile of a row-major head, staged through registers. Thread tid
+// reads ROWS/GROUPS consecutive rows of one 16-byte column vector; rows at or
+// beyond `limit` read as zero. The same registers are written to LDS
+// row-major ([ROWS][ld]) and/or transposed ([D][ld]).
+template <typename T, int ROWS, int D, int NT>
+struct Tile {
+  using V = typename Elt<T>::vec;
+  static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int NDV = D / VEC;        // column vectors per row
+  static constexpr int GROUPS = NT / NDV;    // row groups
+  static constexpr int R = ROWS / GROUPS;    // rows per thread
+  static_assert(NT % NDV == 0 && ROWS % GROUPS == 0 && R >= 1, "tile/thread shape");
+  V r[R];
+
+  __device__ __forceinline__ void load(const T* head, int row0, int limit, int tid) {
+    const int dv = tid % NDV, grp = tid / NDV;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int row = row0 + grp * R + i;
+      if (row < limit)
+        r[i] = *(const V*)(head + (size_t)row * D + dv * VEC);
+      else
+        r[i] = V{};
+    }
+  }
+  __device__ __forceinline__ void store_rows(T* lds, int ld, int tid) const {
+    const int dv = tid % NDV, grp = tid / NDV;
+#pragma unroll
+    for (int i = 0; i < R; ++i) *(V*)(lds + (grp * R + i) * ld + dv * VEC) = r[i];
+  }
+  __device__ __forceinline__ void store_cols(T* lds, int ld, int tid) const {
+    const int dv = tid % NDV, grp = tid / NDV;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      T run[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) run[i] = r[i][e];
+      store_run<T, R>(lds + (dv * VEC + e) * ld + grp * R, run);
+    }
+  }
+};
+
+// ----------------------------------------------------------------------------
+// Forward. Grid (query tiles, Hq, batch); NW waves, each owning NQT*16 query
+// rows. Key tiles of BK rows are streamed through LDS (K row-major for
+// S^T = K Q^T, V transposed for O^T = V^T P^T) with the next tile's global
+// loads in flight during the current tile's math. Tiles past a wave's last
+// visible key are skipped; only tiles that cross its diagonal are masked.
+// ----------------------------------------------------------------------------
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int hq, hkv, q_cap, kv_cap, q_off, start, len;
+  float c2;  // softmax scale * log2(e)
+};
+
+template <typename T, int D, int NQT, int BK, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
+  using E = Elt<T>;
+  using frag = typename E::frag;
+  constexpr int NT = NW * 64, BQ = NW * NQT * 16;
+  constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
+  constexpr int PAD = 16 / sizeof(T), KS = D + PAD, VS = BK + PAD;
+  __shared__ __attribute__((aligned(16))) T Ks[BK * KS];
+  __shared__ __attribute__((aligned(16))) T Vt[D * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (p.hq / p.hkv);
+  const T* Q = (const T*)p.q + ((size_t)(b * p.hq + h) * p.q_cap + p.q_off) * D;
+  const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const T* V = (const T*)p.v + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const int L = p.start + p.len;
+  const int r0 = qt * BQ;
+  const int n_tiles = (p.start + min(r0 + BQ, p.len) - 1) / BK + 1;
+  const int wr0 = r0 + wave * NQT * 16;
+  const bool active = wr0 < p.len;
+  const int wq_lo = p.start + wr0;
+  const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
+
+  frag qf[NQT][DK];
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    const int row = wr0 + nt * 16 + n;
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb)
+      qf[nt][kb] = row < p.len ? ld8(Q + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+  }
+  f32x4 oacc[MD][NQT];
+  float mrun[NQT], lrun[NQT];
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    mrun[nt] = -kInf;
+    lrun[nt] = 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) oacc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  Tile<T, BK, D, NT> kt, vt;
+  kt.load(K, 0, L, tid);
+  vt.load(V, 0, L, tid);
+  for (int j = 0; j < n_tiles; ++j) {
+    const int kb0 = j * BK;
+    __syncthreads();
+    kt.store_rows(Ks, KS, tid);
+    vt.store_cols(Vt, VS, tid);
+    __syncthreads();
+    if (j + 1 < n_tiles) {
+      kt.load(K, kb0 + BK, L, tid);
+      vt.load(V, kb0 + BK, L, tid);
+    }
+    if (!active || kb0 > wq_hi) continue;
+
+    f32x4 s[MK][NQT];
+#pragma unroll
+    for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) s[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk) {
+        const frag a = ld8(&Ks[(mk * 16 + n) * KS + kb * 32 + 8 * g]);
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) E::mma(s[mk][nt], a, qf[nt][kb]);
+      }
+
+    const bool need_mask = kb0 + BK - 1 > wq_lo;
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      const int qp = wq_lo + nt * 16 + n;
+      float mx = -kInf;
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[mk][nt][i] * p.c2;
+          if (need_mask && kb0 + mk * 16 + 4 * g + i > qp) x = -kInf;
+          s[mk][nt][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrun[nt], mx);
+      const float alpha = fexp2(mrun[nt] - mnew);
+      mrun[nt] = mnew;
+      float lsum = 0.f;
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fexp2(s[mk][nt][i] - mnew);
+          s[mk][nt][i] = e;
+          lsum += e;
+        }
+      lrun[nt] = lrun[nt] * alpha + lsum;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;
+    }
+
+#pragma unroll
+    for (int kb2 = 0; kb2 < KB2; ++kb2) {
+      frag pf[NQT];
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) pf[nt] = pack44<T>(s[2 * kb2][nt], s[2 * kb2 + 1][nt]);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const frag a = ld44(&Vt[(md * 16 + n) * VS + kb2 * 32 + 4 * g]);
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) E::mma(oacc[md][nt], a, pf[nt]);
+      }
+    }
+  }
+
+  if (!active) return;
+  T* O = (T*)p.o + ((size_t)(b * p.hq + h) * p.q_cap + p.q_off) * D;
+  float* LSE = p.lse + (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    float l = lrun[nt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int row = wr0 + nt * 16 + n;
+    if (row < p.len) {
+      const float inv = 1.f / l;
+#pragma unroll
+      for (int md = 0; md < MD; ++md) store4<T>(O + (size_t)row * D + md * 16 + 4 * g, oacc[md][nt], inv);
+      if (g == 0) LSE[row] = (mrun[nt] + __builtin_amdgcn_logf(l)) * kLn2;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// delta_r = sum_c dO_rc O_rc in float32; LPR lanes share one row.
+// ----------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(const T* o, const T* dout, float* delta, int q_cap,
+                                                    int q_off, int len, int rows) {
+  using V = typename Elt<T>::vec;
+  constexpr int VEC = Elt<T>::VEC, LPR = D / VEC;
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = gid / LPR, sub = gid % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const int bh = row / len, r = row % len;
+    const size_t off = ((size_t)bh * q_cap + q_off + r) * D + sub * VEC;
+    const V a = *(const V*)(o + off), c = *(const V*)(dout + off);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc += (float)a[e] * (float)c[e];
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && sub == 0) delta[row] = acc;
+}
+
+// ----------------------------------------------------------------------------
+// Backward parameters shared by the dQ and dK/dV passes.
+// ----------------------------------------------------------------------------
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* delta;  // [batch*hq][len]
+  float* dq;
+  float* dk;
+  float* dv;
+  int hq, hkv, q_cap, kv_cap, q_off, start, len;
+  float c2;        // softmax scale * log2(e)
+  float dq_scale;  // grad_scale * softmax scale
+  float dk_scale;  // grad_scale * softmax scale
+  float dv_scale;  // grad_scale
+};
+
+// dQ pass. Same walk as the forward (grid over query tiles, key tiles through
+// LDS): S^T = K Q^T and dP^T = V dO^T from row-major K, V; P from the stored
+// LSE; dQ^T += K^T dS^T from a transposed copy of K made from the same loads.
+template <typename T, int D, int NQT, int BK, int NW>
+__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
+  using E = Elt<T>;
+  using frag = typename E::frag;
+  constexpr int NT = NW * 64, BQ = NW * NQT * 16;
+  constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
+  constexpr int PAD = 16 / sizeof(T), KS = D + PAD, VS = BK + PAD;
+  __shared__ __attribute__((aligned(16))) T Ks[BK * KS];
+  __shared__ __attribute__((aligned(16))) T Vs[BK * KS];
+  __shared__ __attribute__((aligned(16))) T Kt[D * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int qt = gridDim.x - 1 - blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (p.hq / p.hkv);
+  const size_t qhead = ((size_t)(b * p.hq + h) * p.q_cap + p.q_off);
+  const T* Q = (const T*)p.q + qhead * D;
+  const T* dO = (const T*)p.dout + qhead * D;
+  const float* LSE = p.lse + qhead;
+  const float* DL = p.delta + (size_t)(b * p.hq + h) * p.len;
+  const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const T* V = (const T*)p.v + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const int L = p.start + p.len;
+  const int r0 = qt * BQ;
+  const int n_tiles = (p.start + min(r0 + BQ, p.len) - 1) / BK + 1;
+  const int wr0 = r0 + wave * NQT * 16;
+  const bool active = wr0 < p.len;
+  const int wq_lo = p.start + wr0;
+  const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
+
+  frag qf[NQT][DK], df[NQT][DK];
+  float lse2[NQT], dl[NQT];
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    const int row = wr0 + nt * 16 + n;
+    const bool ok = row < p.len;
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb) {
+      qf[nt][kb] = ok ? ld8(Q + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+      df[nt][kb] = ok ? ld8(dO + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+    }
+    lse2[nt] = ok ? LSE[row] * kLog2e : kInf;
+    dl[nt] = ok ? DL[row] : 0.f;
+  }
+  f32x4 acc[MD][NQT];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  Tile<T, BK, D, NT> kt, vt;
+  kt.load(K, 0, L, tid);
+  vt.load(V, 0, L, tid);
+  for (int j = 0; j < n_tiles; ++j) {
+    const int kb0 = j * BK;
+    __syncthreads();
+    kt.store_rows(Ks, KS, tid);
+    kt.store_cols(Kt, VS, tid);
+    vt.store_rows(Vs, KS, tid);
+    __syncthreads();
+    if (j + 1 < n_tiles) {
+      kt.load(K, kb0 + BK, L, tid);
+      vt.load(V, kb0 + BK, L, tid);
+    }
+    if (!active || kb0 > wq_hi) continue;
+
+    f32x4 s[MK][NQT], dp[MK][NQT];
+#pragma unroll
+    for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) {
+        s[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk) {
+        const frag ak = ld8(&Ks[(mk * 16 + n) * KS + kb * 32 + 8 * g]);
+        const frag av = ld8(&Vs[(mk * 16 + n) * KS + kb * 32 + 8 * g]);
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+          E::mma(s[mk][nt], ak, qf[nt][kb]);
+          E::mma(dp[mk][nt], av, df[nt][kb]);
+        }
+      }
+
+    const bool need_mask = kb0 + BK - 1 > wq_lo;
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      const int qp = wq_lo + nt * 16 + n;
+#pragma unroll
+      for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float pr = fexp2(s[mk][nt][i] * p.c2 - lse2[nt]);
+          if (need_mask && kb0 + mk * 16 + 4 * g + i > qp) pr = 0.f;
+          dp[mk][nt][i] = pr * (dp[mk][nt][i] - dl[nt]);
+        }
+    }
+
+#pragma unroll
+    for (int kb2 = 0; kb2 < KB2; ++kb2) {
+      frag dsf[NQT];
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) dsf[nt] = pack44<T>(dp[2 * kb2][nt], dp[2 * kb2 + 1][nt]);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const frag a = ld44(&Kt[(md * 16 + n) * VS + kb2 * 32 + 4 * g]);
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], a, dsf[nt]);
+      }
+    }
+  }
+
+  if (!active) return;
+  float* DQ = p.dq + qhead * D;
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    const int row = wr0 + nt * 16 + n;
+    if (row < p.len) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+        *(f32x4*)(DQ + (size_t)row * D + md * 16 + 4 * g) = acc[md][nt] * p.dq_scale;
+    }
+  }
+}
+
+// dK/dV pass. Grid (key tiles of NW*NKT*16 rows, Hkv, batch); each wave keeps
+// its NKT*16 keys' K and V fragments and dK, dV sums in registers and walks
+// every (q head of the group, query tile) that can see them. Query tiles are
+// staged in LDS row-major (A operand of S = Q K^T and dP = dO V^T) and
+// transposed (B operand of dK = dS^T Q and dV = P^T dO).
+template <typename T, int D, int NKT, int BQ, int NW>
+__global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
+  using E = Elt<T>;
+  using frag = typename E::frag;
+  constexpr int NT = NW * 64, BKV = NW * NKT * 16;
+  constexpr int DK = D / 32, MD = D / 16, MQ = BQ / 16, KQ = BQ / 32;
+  constexpr int PAD = 16 / sizeof(T), KS = D + PAD, QS = BQ + PAD;
+  __shared__ __attribute__((aligned(16))) T Qs[BQ * KS];
+  __shared__ __attribute__((aligned(16))) T Ds[BQ * KS];
+  __shared__ __attribute__((aligned(16))) T Qt[D * QS];
+  __shared__ __attribute__((aligned(16))) T Dt[D * QS];
+  __shared__ float lse_s[BQ], dl_s[BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int kt = gridDim.x - 1 - blockIdx.x;  // keys with the most queries first
+  const int hk = blockIdx.y, b = blockIdx.z;
+  const int G = p.hq / p.hkv;
+  const int L = p.start + p.len;
+  const int kb0 = kt * BKV;
+  const int wk0 = kb0 + wave * NKT * 16;
+  const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const T* V = (const T*)p.v + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+
+  frag kf[NKT][DK], vf[NKT][DK];
+#pragma unroll
+  for (int nk = 0; nk < NKT; ++nk) {
+    const int key = wk0 + nk * 16 + n;
+    const bool ok = key < L;
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb) {
+      kf[nk][kb] = ok ? ld8(K + (size_t)key * D + kb * 32 + 8 * g) : frag{};
+      vf[nk][kb] = ok ? ld8(V + (size_t)key * D + kb * 32 + 8 * g) : frag{};
+    }
+  }
+  f32x4 dka[NKT][MD], dva[NKT][MD];
+#pragma unroll
+  for (int nk = 0; nk < NKT; ++nk)
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      dka[nk][md] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dva[nk][md] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // Query rows that can see key kb0: chunk rows r with start + r >= kb0.
+  const int qt0 = max(0, kb0 - p.start) / BQ;
+  const int nq = (p.len + BQ - 1) / BQ - qt0;
+  const int iters = G * nq;
+
+  Tile<T, BQ, D, NT> qtile, dtile;
+  float lse_r = 0.f, dl_r = 0.f;
+  auto load = [&](int it) {
+    const int h = hk * G + it / nq, q0 = (qt0 + it % nq) * BQ;
+    const size_t qhead = (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
+    qtile.load((const T*)p.q + qhead * D, q0, p.len, tid);
+    dtile.load((const T*)p.dout + qhead * D, q0, p.len, tid);
+    if (tid < BQ) {
+      const int r = q0 + tid;
+      lse_r = r < p.len ? p.lse[qhead + r] * kLog2e : kInf;
+      dl_r = r < p.len ? p.delta[(size_t)(b * p.hq + h) * p.len + r] : 0.f;
+    }
+  };
+  if (iters > 0) load(0);
+  for (int it = 0; it < iters; ++it) {
+    const int q0 = (qt0 + it % nq) * BQ;
+    __syncthreads();
+    qtile.store_rows(Qs, KS, tid);
+    qtile.store_cols(Qt, QS, tid);
+    dtile.store_rows(Ds, KS, tid);
+    dtile.store_cols(Dt, QS, tid);
+    if (tid < BQ) {
+      lse_s[tid] = lse_r;
+      dl_s[tid] = dl_r;
+    }
+    __syncthreads();
+    if (it + 1 < iters) load(it + 1);
+
+    const int q_lo = p.start + q0;
+    const int q_hi = p.start + min(q0 + BQ, p.len) - 1;
+    if (wk0 >= L || wk0 > q_hi) continue;
+    const bool need_mask = q_lo < wk0 + NKT * 16 - 1;
+
+    f32x4 s[MQ][NKT], dp[MQ][NKT];
+#pragma unroll
+    for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+      for (int nk = 0; nk < NKT; ++nk) {
+        s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq) {
+        const frag aq = ld8(&Qs[(mq * 16 + n) * KS + kb * 32 + 8 * g]);
+        const frag ad = ld8(&Ds[(mq * 16 + n) * KS + kb * 32 + 8 * g]);
+#pragma unroll
+        for (int nk = 0; nk < NKT; ++nk) {
+          E::mma(s[mq][nk], aq, kf[nk][kb]);
+          E::mma(dp[mq][nk], ad, vf[nk][kb]);
+        }
+      }
+
+#pragma unroll
+    for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = mq * 16 + 4 * g + i;
+        const float l2 = lse_s[rr], dlt = dl_s[rr];
+#pragma unroll
+        for (int nk = 0; nk < NKT; ++nk) {
+          float pr = fexp2(s[mq][nk][i] * p.c2 - l2);
+          if (need_mask && wk0 + nk * 16 + n > q_lo + rr) pr = 0.f;
+          s[mq][nk][i] = pr;
+          dp[mq][nk][i] = pr * (dp[mq][nk][i] - dlt);
+        }
+      }
+
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) {
+      frag pf[NKT], dsf[NKT];
+#pragma unroll
+      for (int nk = 0; nk < NKT; ++nk) {
+        pf[nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
+        dsf[nk] = pack44<T>(dp[2 * kq][nk], dp[2 * kq + 1][nk]);
+      }
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const frag bd = ld44(&Dt[(md * 16 + n) * QS + kq * 32 + 4 * g]);
+        const frag bq = ld44(&Qt[(md * 16 + n) * QS + kq * 32 + 4 * g]);
+#pragma unroll
+        for (int nk = 0; nk < NKT; ++nk) {
+          E::mma(dva[nk][md], pf[nk], bd);
+          E::mma(dka[nk][md], dsf[nk], bq);
+        }
+      }
+    }
+  }
+
+  float* DKp = p.dk + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  float* DVp = p.dv + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+#pragma unroll
+  for (int nk = 0; nk < NKT; ++nk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = wk0 + nk * 16 + 4 * g + i;
+      if (key < L) {
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const size_t idx = (size_t)key * D + md * 16 + n;
+          DKp[idx] += p.dk_scale * dka[nk][md][i];
+          DVp[idx] += p.dv_scale * dva[nk][md][i];
+        }
+      }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// acc += scale * src over the first `rows` rows of every head (float4 lanes).
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void accumulate_kernel(float* acc, const float* src, int heads_total,
+                                                         int acc_cap, int src_cap, int hd4, int rows,
+                                                         float scale) {
+  const size_t per_head = (size_t)rows * hd4;
+  const size_t total = per_head * heads_total;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t bh = i / per_head, rem = i % per_head;
+    f32x4* a = (f32x4*)acc + bh * (size_t)acc_cap * hd4 + rem;
+    const f32x4 s = *((const f32x4*)src + bh * (size_t)src_cap * hd4 + rem);
+    *a += scale * s;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
+  const size_t n4 = n / 4;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x)
+    ((f32x4*)p)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (blockIdx.x == 0 && threadIdx.x < n % 4) p[n4 * 4 + threadIdx.x] = 0.f;
+}
+
+// ----------------------------------------------------------------------------
+// Tile configurations per (type, head_dim).
+// ----------------------------------------------------------------------------
+template <typename T, int D>
+struct Cfg {
+  static constexpr int FWD_NQT = 2, FWD_BK = 64, FWD_NW = 4;
+  static constexpr int DQ_NQT = 2, DQ_BK = 64, DQ_NW = 4;
+  static constexpr int KV_NKT = 2, KV_BQ = 64, KV_NW = 4;
+};
+
+template <typename T, int D>
+hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse,
+                    hipStream_t st) {
+  using C = Cfg<T, D>;
+  constexpr int BQ = C::FWD_NW * C::FWD_NQT * 16;
+  FwdParams p{q, k, v, o, lse, s.hq, s.hkv, s.q_cap, s.kv_cap, s.q_off, s.start, s.len, s.scale * kLog2e};
+  dim3 grid((s.len + BQ - 1) / BQ, s.hq, s.batch);
+  prof_begin(CA_KERNEL_FWD, st);
+  hipLaunchKernelGGL((fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), grid, dim3(C::FWD_NW * 64), 0,
+                     st, p);
+  prof_end(CA_KERNEL_FWD, st);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
+                    float* delta, hipStream_t st) {
+  using C = Cfg<T, D>;
+  constexpr int LPR = D / Elt<T>::VEC;
+  const int rows = s.batch * s.hq * s.len;
+  const int threads = rows * LPR;
+  prof_begin(CA_KERNEL_DELTA, st);
+  hipLaunchKernelGGL((delta_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0, st, (const T*)o,
+                     (const T*)dout, delta, s.q_cap, s.q_off, s.len, rows);
+  prof_end(CA_KERNEL_DELTA, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BwdParams p{q, k, v, dout, lse, delta, dq, dk, dv, s.hq, s.hkv, s.q_cap, s.kv_cap, s.q_off, s.start,
+              s.len, s.scale * kLog2e, gs * s.scale, gs * s.scale, gs};
+  constexpr int BKV = C::KV_NW * C::KV_NKT * 16;
+  const int L = s.start + s.len;
+  prof_begin(CA_KERNEL_DKDV, st);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NW>), dim3((L + BKV - 1) / BKV, s.hkv, s.batch),
+                     dim3(C::KV_NW * 64), 0, st, p);
+  prof_end(CA_KERNEL_DKDV, st);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int BQ = C::DQ_NW * C::DQ_NQT * 16;
+  prof_begin(CA_KERNEL_DQ, st);
+  hipLaunchKernelGGL((dq_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW>), dim3((s.len + BQ - 1) / BQ, s.hq, s.batch),
+                     dim3(C::DQ_NW * 64), 0, st, p);
+  prof_end(CA_KERNEL_DQ, st);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse,
+                      hipStream_t st) {
+  if (s.dtype == 1) {
+    return s.head_dim == 128 ? fwd_impl<bf16, 128>(s, q, k, v, o, lse, st)
+                             : fwd_impl<bf16, 64>(s, q, k, v, o, lse, st);
+  }
+  return s.head_dim == 128 ? fwd_impl<float, 128>(s, q, k, v, o, lse, st)
+                           : fwd_impl<float, 64>(s, q, k, v, o, lse, st);
+}
+
+hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
+                      float* delta, hipStream_t st) {
+  if (s.dtype == 1) {
+    return s.head_dim == 128 ? bwd_impl<bf16, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st)
+                             : bwd_impl<bf16, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st);
+  }
+  return s.head_dim == 128 ? bwd_impl<float, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st)
+                           : bwd_impl<float, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st);
+}
+
+hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap, int src_cap,
+                             int head_dim, int rows, float scale, hipStream_t st) {
+  const size_t total = (size_t)batch * heads * rows * (head_dim / 4);
+  if (total == 0) return hipSuccess;
+  const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  prof_begin(CA_KERNEL_ACCUMULATE, st);
+  hipLaunchKernelGGL(accumulate_kernel, dim3(blocks), dim3(256), 0, st, acc, src, batch * heads, acc_cap,
+                     src_cap, head_dim / 4, rows, scale);
+  prof_end(CA_KERNEL_ACCUMULATE, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t want = (n / 4 + 255) / 256;
+  const int blocks = (int)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+  prof_begin(CA_KERNEL_ZERO, st);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, st, p, n);
+  prof_end(CA_KERNEL_ZERO, st);
+  return hipGetLastError();
+}
+
+}  // namespace ca

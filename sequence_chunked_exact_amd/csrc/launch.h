@@ -1,0 +1,40 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels
+// (kernels.hip). Arguments are already validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ca {
+
+struct Shape {
+  int batch, hq, hkv, head_dim;
+  int kv_cap, q_cap, q_off;
+  int start, len;       // chunk: first global position and number of rows
+  float scale;          // softmax scale
+  int dtype;            // CA_F32 / CA_BF16
+};
+
+// Forward: o, lse for the chunk's rows.
+hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v, void* o,
+                      float* lse, hipStream_t st);
+
+// Backward: delta (workspace, batch*hq*len floats) = rowsum(dout * o), then dq
+// (overwritten, times grad_scale) and dk/dv accumulators (incremented).
+hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, float grad_scale,
+                      float* dq, float* dk, float* dv, float* delta, hipStream_t st);
+
+// acc[b][h][r][:] += scale * src[b][h][r][:], r < rows.
+hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap,
+                             int src_cap, int head_dim, int rows, float scale, hipStream_t st);
+
+// Timing hooks around each launch (no-ops unless profiling is on).
+void prof_begin(int kernel, hipStream_t st);
+void prof_end(int kernel, hipStream_t st);
+
+// Fill n floats with zero (a kernel, so it is safe inside captured graphs).
+hipError_t launch_zero(float* p, size_t n, hipStream_t st);
+
+}  // namespace ca

@@ -1,0 +1,131 @@
+"""Host-only checks of the C ABI: exports, argument validation, selector.
+
+No call here reaches the GPU: every rejected call returns its error code
+before any device call, so fake (never dereferenced) pointers are safe.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle.selection import select_chunks
+
+b = pytest.importorskip("sequence_chunked_exact_amd.binding")
+lib = b.lib
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "chunk_attn.h")
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x10008
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "chunk_attn_fwd" in names and "sparse_chunk_bwd" in names
+    so = ctypes.CDLL(b.LIB_PATH)
+    for name in names:
+        assert hasattr(so, name), name
+
+
+def desc(**kw):
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, kv_capacity=1024, q_capacity=256,
+                q_row_offset=0, chunk_start=512, chunk_len=256, softmax_scale=1.0, dtype=b.CA_BF16)
+    base.update(kw)
+    return b.Desc(**base)
+
+
+def fwd(d, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
+    return lib.chunk_attn_fwd(ctypes.byref(d) if d is not None else None, q, k, v, o, lse, None, 0, None)
+
+
+def bwd(d, ws=FAKE, ws_bytes=1 << 20, gs=1.0, dq=FAKE):
+    return lib.chunk_attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gs, dq, FAKE, FAKE,
+                              ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -3),
+    (dict(head_dim=96), -6),
+    (dict(head_dim=256), -6),
+    (dict(n_q_heads=6, n_kv_heads=4), -2),
+    (dict(n_kv_heads=0), -2),
+    (dict(batch=0), -2),
+    (dict(chunk_len=0), -2),
+    (dict(chunk_start=900), -2),            # start + len > kv_capacity
+    (dict(q_row_offset=1), -2),             # offset + len > q_capacity
+    (dict(chunk_start=-1), -2),
+    (dict(softmax_scale=float("nan")), -2),
+    (dict(softmax_scale=float("inf")), -2),
+])
+def test_descriptor_errors(kw, code):
+    assert fwd(desc(**kw)) == code
+    assert bwd(desc(**kw)) == code
+    assert b.lib.chunk_attn_last_error().decode() != ""
+
+
+def test_pointer_errors():
+    assert fwd(None) == -1
+    assert fwd(desc(), q=None) == -1
+    assert fwd(desc(), lse=None) == -1
+    assert fwd(desc(), v=MISALIGNED) == -4
+    assert bwd(desc(), dq=MISALIGNED) == -4
+    assert bwd(desc(), gs=float("nan")) == -2
+
+
+def test_workspace_errors():
+    d = desc()
+    need = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD)
+    assert need >= 4 * 4 * 256 and need % 256 == 0
+    assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_FWD) == 0
+    assert bwd(d, ws=None) == -5
+    assert bwd(d, ws_bytes=need - 1) == -5
+    assert bwd(d, ws=MISALIGNED, ws_bytes=need) == -4
+    assert lib.chunk_attn_workspace_size(ctypes.byref(desc(head_dim=80)), b.CA_OP_BWD) == 0
+
+
+def test_accumulate_errors():
+    f = lib.prefix_grad_accumulate
+    assert f(None, FAKE, 1, 1, 8, 8, 64, 4, 1.0, None) == -1
+    assert f(MISALIGNED, FAKE, 1, 1, 8, 8, 64, 4, 1.0, None) == -4
+    assert f(FAKE, FAKE, 1, 1, 8, 8, 64, 9, 1.0, None) == -2      # prefix > capacity
+    assert f(FAKE, FAKE, 1, 1, 8, 8, 6, 4, 1.0, None) == -2       # head_dim % 4
+    assert f(FAKE, FAKE, 0, 1, 8, 8, 64, 4, 1.0, None) == -2
+
+
+def test_sparse_errors():
+    d = desc(chunk_start=0, chunk_len=128, q_capacity=1024)
+    sel = (ctypes.c_int32 * 16)()
+    f = lib.sparse_chunk_bwd
+
+    def call(seq_len, t, selp=sel, ws_bytes=1 << 20):
+        return f(ctypes.byref(d), seq_len, t, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 selp, FAKE, ws_bytes, None)
+
+    assert call(1024, 9) == -2             # t > k = 8
+    assert call(1024, 0) == -2
+    assert call(2048, 2) == -2             # seq_len > capacity
+    assert call(1024, 2, selp=None) == -1
+    assert call(1024, 2, ws_bytes=16) == -5
+
+
+def test_selector_matches_oracle():
+    for k in (1, 3, 17, 64, 129):
+        for t in sorted({1, 2, k // 3 or 1, k // 8 or 1, k}):
+            if t > k:
+                continue
+            for seed in (0, 1, 2, 12345, 2**63 + 7, 2**64 - 1):
+                assert b.chunk_select(k, t, seed) == select_chunks(k, t, seed), (k, t, seed)
+    assert lib.chunk_select(4, 5, 0, (ctypes.c_int32 * 5)()) == -2
+    assert lib.chunk_select(4, 1, 0, None) == -1
+
+
+def test_strerror_names():
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert lib.chunk_attn_strerror(code).decode()
+    assert lib.chunk_attn_strerror(-99).decode() == "unknown error"

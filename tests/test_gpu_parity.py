@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (per tensor): ||X_gpu - X_ref||_inf / ||X_ref||_inf <= 1e-5 on the
+float32 path and <= 2e-2 on the bf16 path (float32 accumulation) for O, dQ,
+dK, dV; LSE by max absolute error with the same bounds. Both sides consume the
+same seeded inputs (bf16 values widened exactly to float64).
+
+Small cases compare every element. Full-size workloads, run exactly as the
+benchmark runs them (every chunk forward ascending, backward descending),
+compare sampled query rows of O/LSE/dQ, the keys of the last chunk (whose
+gradients only that chunk's queries reach), and two identities that hold for
+every key: sum_j dK_j = 0 and sum_j dV_j = sum of the group's dO rows.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle.selection import select_chunks
+from sequence_chunked_exact_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def binding():
+    from sequence_chunked_exact_amd import binding as B
+    return B
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_inf(a, b):
+    den = np.abs(b).max()
+    return float(np.abs(a - b).max() / (den if den > 0 else 1.0))
+
+
+def tol(wl):
+    return 1e-5 if wl.dtype == "f32" else 2e-2
+
+
+def to_dev(inp):
+    return {n: W.to_torch(inp.raw[n], DEV) for n in ("q", "k", "v", "do")}
+
+
+def run_chunked(wl, inp, T, scale, sparse=None):
+    """Forward over all chunks, then the backward (dense chunked or sparse)."""
+    B = binding()
+    t = to_dev(inp)
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    B.chunked_forward(q, k, v, o, lse, chunk=wl.chunk, seq_len=T, softmax_scale=scale)
+    dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
+    sel = None
+    if sparse is None:
+        B.chunked_backward(q, k, v, o, lse, do, dq, dk, dv, chunk=wl.chunk, seq_len=T, softmax_scale=scale)
+    else:
+        t_, seed = sparse
+        sel = B.sparse_chunk_bwd(q, k, v, o, lse, do, dq, dk, dv, seq_len=T, chunk=wl.chunk, t=t_,
+                                 seed=seed, softmax_scale=scale)
+    torch.cuda.synchronize()
+    out = {"o": o.float().cpu().double().numpy(), "lse": lse.cpu().double().numpy(),
+           "dq": dq.cpu().double().numpy(), "dk": dk.cpu().double().numpy(),
+           "dv": dv.cpu().double().numpy()}
+    return out, sel
+
+
+def custom(name, T, C, Hq, Hkv, d, dtype, seed, scale=1.0, spike=0):
+    return W.Workload(name, 1, T, C, Hq, Hkv, d, dtype, seed, softmax_scale=scale,
+                      spike_rank=4 if spike else 0, spike_amp=3.0 if spike else 0.0)
+
+
+def check_dense(wl, heads=None, T=None, scale=None):
+    T = wl.seq_len if T is None else T
+    scale = wl.softmax_scale if scale is None else scale
+    inp = W.make_inputs(wl, seq_len=T)
+    note(f"[case] {wl.name} T={T} C={wl.chunk} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} d={wl.head_dim} "
+         f"{wl.dtype} scale={scale:.4g} heads={heads}")
+    got, _ = run_chunked(wl, inp, T, scale)
+    f = inp.f64
+    ro, rlse = A.forward(f["q"], f["k"], f["v"], scale, heads=heads)
+    rdq, rdk, rdv = A.backward(f["q"], f["k"], f["v"], f["do"], scale, heads=heads)
+    hs = list(range(wl.n_q_heads)) if heads is None else list(heads)
+    G = wl.n_q_heads // wl.n_kv_heads
+    gs = sorted({h // G for h in hs})
+    errs = {
+        "o": rel_inf(got["o"][:, hs], ro[:, hs]),
+        "lse": float(np.abs(got["lse"][:, hs] - rlse[:, hs]).max()),
+        "dq": rel_inf(got["dq"][:, hs], rdq[:, hs]),
+        "dk": rel_inf(got["dk"][:, gs], rdk[:, gs]),
+        "dv": rel_inf(got["dv"][:, gs], rdv[:, gs]),
+    }
+    note(f"       errors {errs}")
+    for name, e in errs.items():
+        assert e <= tol(wl), (name, e)
+    return errs
+
+
+# ------------------------------------------------------------------ float32 path
+def test_tiny_workload_every_element():
+    check_dense(W.WORKLOADS["tiny"])
+
+
+@pytest.mark.parametrize("T,C,Hq,Hkv,d,scale", [
+    (512, 128, 4, 2, 64, 1 / 8),        # GQA, 1/sqrt(d) scale
+    (300, 300, 2, 1, 64, 0.7),          # one chunk = standard backprop (D = 1)
+    (200, 33, 4, 4, 128, 1.0),          # ragged chunks and tiles, d = 128
+    (70, 1, 2, 2, 64, 1.0),             # one-row chunks
+    (129, 64, 8, 1, 64, 0.3),           # G = 8, tail of one row
+])
+def test_f32_variants(T, C, Hq, Hkv, d, scale):
+    check_dense(custom("f32_var", T, C, Hq, Hkv, d, "f32", seed=T + C, scale=scale))
+
+
+# ------------------------------------------------------------------ bf16 path, reduced sizes
+@pytest.mark.parametrize("name,T", [("4b_layer", 1192), ("8b_layer", 2048), ("32b_layer", 4096)])
+def test_bf16_workload_shapes_reduced(name, T):
+    wl = W.WORKLOADS[name]
+    G = wl.n_q_heads // wl.n_kv_heads
+    heads = list(range(G)) + list(range(wl.n_q_heads - G, wl.n_q_heads))   # first and last group
+    check_dense(wl, heads=heads, T=T)
+
+
+@pytest.mark.parametrize("T,C,Hq,Hkv,d,spike,scale", [
+    (777, 100, 4, 2, 64, 0, 1.0),
+    (640, 640, 4, 1, 128, 1, 1.0),
+    (1000, 96, 2, 2, 128, 0, 1 / math.sqrt(128)),
+    (65, 7, 2, 1, 128, 1, 1.0),
+])
+def test_bf16_tile_and_tail_cases(T, C, Hq, Hkv, d, spike, scale):
+    check_dense(custom("bf16_var", T, C, Hq, Hkv, d, "bf16", seed=T * 3 + C, scale=scale, spike=spike))
+
+
+# ------------------------------------------------------------------ sparse driver
+def test_sparse_reduced_matches_oracle():
+    wl = W.WORKLOADS["sparse_64k"]
+    T, t, seed = 8192, 2, 5
+    k_chunks = T // wl.chunk
+    inp = W.make_inputs(wl, seq_len=T)
+    note(f"[case] sparse reduced T={T} k={k_chunks} t={t} seed={seed}")
+    got, sel = run_chunked(wl, inp, T, 1.0, sparse=(t, seed))
+    assert sel == select_chunks(k_chunks, t, seed)
+    f = inp.f64
+    heads = [0, 1, 2, 3]
+    rdq, rdk, rdv = A.sparse_backward(f["q"], f["k"], f["v"], f["do"], 1.0, wl.chunk, sel, k_chunks,
+                                      heads=heads)
+    errs = {"dq": rel_inf(got["dq"][:, heads], rdq[:, heads]),
+            "dk": rel_inf(got["dk"][:, :1], rdk[:, :1]), "dv": rel_inf(got["dv"][:, :1], rdv[:, :1])}
+    note(f"       errors {errs}")
+    for n_, e in errs.items():
+        assert e <= 2e-2, (n_, e)
+    unselected = [i for i in range(k_chunks) if i not in sel]
+    for i in unselected:
+        assert np.all(got["dq"][:, :, i * wl.chunk:(i + 1) * wl.chunk] == 0.0)
+
+
+def test_sparse_all_chunks_equals_chunked_backward_bitwise():
+    wl = custom("sp_all", 1000, 128, 4, 2, 128, "bf16", seed=21)
+    inp = W.make_inputs(wl)
+    dense, _ = run_chunked(wl, inp, 1000, 1.0)
+    k_chunks = wl.n_chunks
+    sparse, sel = run_chunked(wl, inp, 1000, 1.0, sparse=(k_chunks, 99))
+    assert sel == list(range(k_chunks))
+    for n_ in ("dq", "dk", "dv"):
+        assert np.array_equal(dense[n_], sparse[n_]), n_
+
+
+def test_deterministic():
+    wl = custom("det", 700, 256, 4, 2, 128, "bf16", seed=3)
+    inp = W.make_inputs(wl)
+    a, _ = run_chunked(wl, inp, 700, 1.0)
+    b, _ = run_chunked(wl, inp, 700, 1.0)
+    for n_ in a:
+        assert np.array_equal(a[n_], b[n_]), n_
+
+
+# ------------------------------------------------------------------ prefix accumulate
+def test_prefix_grad_accumulate():
+    B = binding()
+    g = torch.Generator().manual_seed(0)
+    acc = torch.randn(2, 3, 40, 128, generator=g)
+    src = torch.randn(2, 3, 33, 128, generator=g)
+    want = acc.double().numpy().copy()
+    want[:, :, :29] += 0.375 * src.double().numpy()[:, :, :29]
+    a = acc.to(DEV)
+    B.prefix_grad_accumulate(a, src.to(DEV), 29, 0.375)
+    torch.cuda.synchronize()
+    assert np.abs(a.cpu().double().numpy() - want).max() < 1e-5
+
+
+# ------------------------------------------------------------------ full sizes, bench launch config
+def full_size_check(name, sparse=False):
+    wl = W.WORKLOADS[name]
+    T, C, G = wl.seq_len, wl.chunk, wl.n_q_heads // wl.n_kv_heads
+    note(f"[case] full size {name}: generating inputs")
+    inp = W.make_inputs(wl)
+    k_chunks = wl.n_chunks
+    sp = (wl.sparse_t, wl.select_seed) if sparse else None
+    note(f"[case] full size {name}: GPU run")
+    got, sel = run_chunked(wl, inp, T, wl.softmax_scale, sparse=sp)
+    f = inp.f64
+    heads = list(range(G))      # kv group 0
+    rng = np.random.default_rng(7)
+    if sparse:
+        assert sel == select_chunks(k_chunks, wl.sparse_t, wl.select_seed)
+        gamma = k_chunks / wl.sparse_t
+        last = max(sel)
+    else:
+        gamma, last = 1.0, k_chunks - 1
+    # sampled query rows: a block at the end of three chunks plus random rows
+    rows = set(rng.choice(T, 48, replace=False).tolist())
+    for i in (0, k_chunks // 2, last):
+        s, c = wl.chunk_bounds(i)
+        rows.update(range(s + c - 16, s + c))
+        rows.update(range(s, s + 8))
+    rows = np.array(sorted(rows))
+    note(f"[case] full size {name}: oracle on {rows.size} rows")
+    ro, rlse = A.forward(f["q"], f["k"], f["v"], wl.softmax_scale, rows=rows, heads=heads)
+    assert rel_inf(got["o"][:, heads][:, :, rows], ro[:, heads][:, :, rows]) <= 2e-2
+    assert np.abs(got["lse"][:, heads][:, :, rows] - rlse[:, heads][:, :, rows]).max() <= 2e-2
+    if sparse:
+        sel_rows = np.array([r for r in rows if (r // C) in sel])
+        do_s = f["do"]
+        rdq, _, _ = A.backward(f["q"], f["k"], f["v"], gamma * do_s, 1.0, rows=sel_rows, heads=heads)
+        assert rel_inf(got["dq"][:, heads][:, :, sel_rows], rdq[:, heads][:, :, sel_rows]) <= 2e-2
+        for i in range(k_chunks):
+            if i not in sel:
+                assert np.all(got["dq"][:, :, i * C:(i + 1) * C] == 0.0)
+    else:
+        rdq, _, _ = A.backward(f["q"], f["k"], f["v"], f["do"], wl.softmax_scale, rows=rows, heads=heads)
+        assert rel_inf(got["dq"][:, heads][:, :, rows], rdq[:, heads][:, :, rows]) <= 2e-2
+    # keys of the last (selected) chunk: only that chunk's queries reach them
+    s, c = wl.chunk_bounds(last)
+    note(f"[case] full size {name}: oracle dK/dV for keys [{s}, {s + c})")
+    _, rdk, rdv = A.backward(f["q"], f["k"], f["v"], gamma * f["do"], wl.softmax_scale,
+                             rows=np.arange(s, s + c), heads=heads)
+    assert rel_inf(got["dk"][:, :1, s:s + c], rdk[:, :1, s:s + c]) <= 2e-2
+    assert rel_inf(got["dv"][:, :1, s:s + c], rdv[:, :1, s:s + c]) <= 2e-2
+    # identities over every key of every group
+    do_used = f["do"]
+    if sparse:
+        mask = np.zeros(T, dtype=bool)
+        for i in sel:
+            mask[i * C:(i + 1) * C] = True
+        do_used = do_used * mask[None, None, :, None]
+    want_dv = gamma * do_used.reshape(wl.batch, wl.n_kv_heads, G, T, wl.head_dim).sum(axis=(2, 3))
+    dv_sum = got["dv"].sum(axis=2)
+    assert rel_inf(dv_sum, want_dv) <= 2e-2
+    dk_sum = np.abs(got["dk"].sum(axis=2)).max()
+    assert dk_sum <= 2e-2 * np.abs(got["dk"]).max() * math.sqrt(T)
+    note(f"[case] full size {name}: ok")
+
+
+def test_full_size_8b_layer():
+    full_size_check("8b_layer")
+
+
+def test_full_size_4b_layer():
+    full_size_check("4b_layer")
+
+
+def test_full_size_32b_layer():
+    full_size_check("32b_layer")
+
+
+def test_full_size_sparse_64k():
+    full_size_check("sparse_64k", sparse=True)
