@@ -21,14 +21,24 @@
 // operands of a product always use the same order, which is all a k-reduction
 // needs.
 //
+// LDS holds every streamed tile once, row-major, with its 16-byte chunks
+// XOR-swizzled by row so that both access patterns are free of bank
+// conflicts: 16 lanes reading one chunk column of 16 rows (operands contracted
+// over head_dim), and ds_read_b64_tr_b16 transposing reads (operands
+// contracted over rows: V in P V, K in dS K, Q and dO in dS^T Q and P^T dO).
+// Tiles are double-buffered: the next tile's global loads are in flight while
+// the current one is consumed, with one barrier per tile.
+//
 // Layout choices:
 //  * forward / dQ: S^T = K Q^T per key tile, so each lane owns one query column
-//    and softmax statistics need no shuffles except the 4-lane max.
+//    and softmax statistics need only a 4-lane reduction.
 //  * dK/dV: S = Q K^T per query tile, so P and dS are already key-major for
-//    dV = P^T dO and dK = dS^T Q; Q and dO are staged in LDS both row-major and
-//    transposed.
+//    dV = P^T dO and dK = dS^T Q.
 //  * every dK/dV element is owned by one lane of one workgroup, which adds its
 //    total into the float32 accumulator once: no atomics.
+//  * softmax runs in the exp2 domain with the scale folded into one FMA, and the
+//    running maximum is only moved (rescaling O and the row sum) when a new
+//    score exceeds it by more than 2^8, which keeps every exponent <= 2^8.
 #include "launch.h"
 
 #include "chunk_attn.h"
@@ -43,12 +53,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kInf = __builtin_huge_valf();
+constexpr float kRescale = 8.f;  // lazy-rescale threshold, log2 units
 
 template <typename T>
 struct Elt;
@@ -78,19 +89,75 @@ struct Elt<float> {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 8 consecutive elements -> fragment (contiguous slot order).
-__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *(const bf16x8*)p; }
-__device__ __forceinline__ f32x8 ld8(const float* p) {
-  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+// Row-major [rows][D] LDS tile; the 16-byte chunk c of row r sits at chunk
+// position c ^ swz(r). The map (r mod 16, with bit 3 ^= bit 0 and bit 2 ^=
+// bit 3) was picked by measuring gfx950's LDS bank-conflict counter over a
+// family of candidate maps: with 256-byte rows it is the simplest one under
+// which both access patterns used here run conflict-free, namely a 64-lane
+// read of one 16-byte chunk column from 16 consecutive rows per 16 lanes, and
+// the transposing read of 4-row x 16-column blocks.
+template <typename T, int D>
+struct Lay {
+  static constexpr int EPC = 16 / sizeof(T);  // elements per chunk
+  static constexpr int CH = D / EPC;          // chunks per row
+  static __device__ __forceinline__ int swz(int r) {
+    const int x = (r ^ ((r & 1) << 3) ^ (((r >> 3) & 1) << 2)) & 15;
+    return x & (CH - 1);
+  }
+  static __device__ __forceinline__ int off(int r, int c) {
+    return r * D + (((c / EPC) ^ swz(r)) * EPC) + (c % EPC);
+  }
+};
+
+// 8 consecutive elements of row r from column c (c % 8 == 0), contiguous order.
+template <int D>
+__device__ __forceinline__ bf16x8 ld8s(const bf16* t, int r, int c) {
+  return *(const bf16x8*)(t + Lay<bf16, D>::off(r, c));
+}
+template <int D>
+__device__ __forceinline__ f32x8 ld8s(const float* t, int r, int c) {
+  const f32x4 a = *(const f32x4*)(t + Lay<float, D>::off(r, c));
+  const f32x4 b = *(const f32x4*)(t + Lay<float, D>::off(r, c + 4));
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-// elements p[0..3] and p[16..19] -> fragment (tile slot order).
-__device__ __forceinline__ bf16x8 ld44(const bf16* p) {
-  const bf16x4 a = *(const bf16x4*)p, b = *(const bf16x4*)(p + 16);
+
+// This lane's {t[rb + k][c0 + n] : k = 0..3} (n = lane % 16; rb a multiple of 4,
+// the same for the 16 lanes of a group). bf16 uses the transposing LDS read:
+// lane j of a group points at row rb + j/4, columns c0 + 4(j%4) .. +3, and the
+// hardware hands lane i element k of lane 4k + i/4's four.
+template <int D>
+__device__ __forceinline__ bf16x4 ldT4(const bf16* t, int rb, int c0, int lane) {
+  const int j = lane & 15;
+  const bf16* p = t + Lay<bf16, D>::off(rb + (j >> 2), c0 + 4 * (j & 3));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+template <int D>
+__device__ __forceinline__ f32x4 ldT4(const float* t, int rb, int c0, int lane) {
+  const int n = lane & 15;
+  f32x4 v;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = t[Lay<float, D>::off(rb + k, c0 + n)];
+  return v;
+}
+// Fragment of t[kbase + tile-order slots][c0 + n] (operand contracted over rows).
+template <int D>
+__device__ __forceinline__ bf16x8 ldT8(const bf16* t, int kbase, int c0, int lane) {
+  const int g = lane >> 4;
+  const bf16x4 a = ldT4<D>(t, kbase + 4 * g, c0, lane), b = ldT4<D>(t, kbase + 16 + 4 * g, c0, lane);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-__device__ __forceinline__ f32x8 ld44(const float* p) {
-  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 16);
+template <int D>
+__device__ __forceinline__ f32x8 ldT8(const float* t, int kbase, int c0, int lane) {
+  const int g = lane >> 4;
+  const f32x4 a = ldT4<D>(t, kbase + 4 * g, c0, lane), b = ldT4<D>(t, kbase + 16 + 4 * g, c0, lane);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// 8 consecutive elements from global memory.
+__device__ __forceinline__ bf16x8 ldg8(const bf16* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ f32x8 ldg8(const float* p) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
@@ -107,6 +174,14 @@ __device__ __forceinline__ typename Elt<T>::frag pack44(const f32x4& lo, const f
 }
 
 template <typename T>
+__device__ __forceinline__ typename Elt<T>::frag negate(const typename Elt<T>::frag& f) {
+  typename Elt<T>::frag r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = -f[i];
+  return r;
+}
+
+template <typename T>
 __device__ __forceinline__ void store4(T* dst, const f32x4& x, float mul) {
   typename Elt<T>::quad v;
 #pragma unroll
@@ -114,44 +189,21 @@ __device__ __forceinline__ void store4(T* dst, const f32x4& x, float mul) {
   *(typename Elt<T>::quad*)dst = v;
 }
 
-__device__ __forceinline__ uint32_t bits16(bf16 x) { return __builtin_bit_cast(uint16_t, x); }
-
-// Store R consecutive elements (R * sizeof(T) bytes, naturally aligned up to 16).
-template <typename T, int R>
-__device__ __forceinline__ void store_run(T* dst, const T (&x)[R]) {
-  if constexpr (sizeof(T) == 2) {
-    static_assert(R % 2 == 0, "bf16 runs hold an even count");
-    uint32_t w[R / 2];
-#pragma unroll
-    for (int i = 0; i < R / 2; ++i) w[i] = bits16(x[2 * i]) | (bits16(x[2 * i + 1]) << 16);
-    if constexpr (R == 2) {
-      *(uint32_t*)dst = w[0];
-    } else if constexpr (R == 4) {
-      *(u32x2*)dst = u32x2{w[0], w[1]};
-    } else {
-#pragma unroll
-      for (int i = 0; i < R / 8; ++i)
-        *((u32x4*)dst + i) = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-    }
-  } else {
-    static_assert(R % 4 == 0, "float runs hold a multiple of four");
-#pragma unroll
-    for (int i = 0; i < R / 4; ++i)
-      *((f32x4*)dst + i) = f32x4{x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
-  }
+__device__ __forceinline__ float wave_max16x4(float m) {
+  m = fmaxf(m, __shfl_xor(m, 16));
+  return fmaxf(m, __shfl_xor(m, 32));
 }
 
-// A [ROWS][D] tile of a row-major head, staged through registers. Thread tid
-// reads ROWS/GROUPS consecutive rows of one 16-byte column vector; rows at or
-// beyond `limit` read as zero. The same registers are written to LDS
-// row-major ([ROWS][ld]) and/or transposed ([D][ld]).
+// A [ROWS][D] tile of a row-major head staged through registers: thread tid
+// holds ROWS/GROUPS consecutive rows of one 16-byte column vector (rows at or
+// beyond `limit` read as zero) and writes them into a swizzled LDS tile.
 template <typename T, int ROWS, int D, int NT>
 struct Tile {
   using V = typename Elt<T>::vec;
   static constexpr int VEC = Elt<T>::VEC;
-  static constexpr int NDV = D / VEC;        // column vectors per row
-  static constexpr int GROUPS = NT / NDV;    // row groups
-  static constexpr int R = ROWS / GROUPS;    // rows per thread
+  static constexpr int NDV = D / VEC;      // column vectors per row
+  static constexpr int GROUPS = NT / NDV;  // row groups
+  static constexpr int R = ROWS / GROUPS;  // rows per thread
   static_assert(NT % NDV == 0 && ROWS % GROUPS == 0 && R >= 1, "tile/thread shape");
   V r[R];
 
@@ -166,29 +218,18 @@ struct Tile {
         r[i] = V{};
     }
   }
-  __device__ __forceinline__ void store_rows(T* lds, int ld, int tid) const {
+  __device__ __forceinline__ void store(T* lds, int tid) const {
     const int dv = tid % NDV, grp = tid / NDV;
 #pragma unroll
-    for (int i = 0; i < R; ++i) *(V*)(lds + (grp * R + i) * ld + dv * VEC) = r[i];
-  }
-  __device__ __forceinline__ void store_cols(T* lds, int ld, int tid) const {
-    const int dv = tid % NDV, grp = tid / NDV;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      T run[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) run[i] = r[i][e];
-      store_run<T, R>(lds + (dv * VEC + e) * ld + grp * R, run);
-    }
+    for (int i = 0; i < R; ++i) *(V*)(lds + Lay<T, D>::off(grp * R + i, dv * VEC)) = r[i];
   }
 };
 
 // ----------------------------------------------------------------------------
 // Forward. Grid (query tiles, Hq, batch); NW waves, each owning NQT*16 query
-// rows. Key tiles of BK rows are streamed through LDS (K row-major for
-// S^T = K Q^T, V transposed for O^T = V^T P^T) with the next tile's global
-// loads in flight during the current tile's math. Tiles past a wave's last
-// visible key are skipped; only tiles that cross its diagonal are masked.
+// rows held as B fragments of S^T = K Q^T. Key tiles of BK rows stream through
+// double-buffered LDS. Tiles past a wave's last visible key are skipped; only
+// tiles that cross its diagonal are masked.
 // ----------------------------------------------------------------------------
 struct FwdParams {
   const void* q;
@@ -197,7 +238,8 @@ struct FwdParams {
   void* o;
   float* lse;
   int hq, hkv, q_cap, kv_cap, q_off, start, len;
-  float c2;  // softmax scale * log2(e)
+  float c2;  // |softmax scale| * log2(e), > 0
+  int neg;   // softmax scale < 0: queries enter S negated
 };
 
 template <typename T, int D, int NQT, int BK, int NW>
@@ -206,9 +248,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using frag = typename E::frag;
   constexpr int NT = NW * 64, BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
-  constexpr int PAD = 16 / sizeof(T), KS = D + PAD, VS = BK + PAD;
-  __shared__ __attribute__((aligned(16))) T Ks[BK * KS];
-  __shared__ __attribute__((aligned(16))) T Vt[D * VS];
+  __shared__ __attribute__((aligned(16))) T Ks[2][BK * D];
+  __shared__ __attribute__((aligned(16))) T Vs[2][BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -225,20 +266,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const bool active = wr0 < p.len;
   const int wq_lo = p.start + wr0;
   const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
+  const float c2 = p.c2;
 
   frag qf[NQT][DK];
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
     const int row = wr0 + nt * 16 + n;
 #pragma unroll
-    for (int kb = 0; kb < DK; ++kb)
-      qf[nt][kb] = row < p.len ? ld8(Q + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+    for (int kb = 0; kb < DK; ++kb) {
+      qf[nt][kb] = row < p.len ? ldg8(Q + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+      if (p.neg) qf[nt][kb] = negate<T>(qf[nt][kb]);
+    }
   }
   f32x4 oacc[MD][NQT];
-  float mrun[NQT], lrun[NQT];
+  float m2[NQT], lrun[NQT];
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
-    mrun[nt] = -kInf;
+    m2[nt] = -kInf;
     lrun[nt] = 0.f;
 #pragma unroll
     for (int md = 0; md < MD; ++md) oacc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -247,77 +291,93 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   Tile<T, BK, D, NT> kt, vt;
   kt.load(K, 0, L, tid);
   vt.load(V, 0, L, tid);
+  kt.store(Ks[0], tid);
+  vt.store(Vs[0], tid);
+  __syncthreads();
   for (int j = 0; j < n_tiles; ++j) {
-    const int kb0 = j * BK;
-    __syncthreads();
-    kt.store_rows(Ks, KS, tid);
-    vt.store_cols(Vt, VS, tid);
-    __syncthreads();
-    if (j + 1 < n_tiles) {
+    const int kb0 = j * BK, cur = j & 1;
+    const bool more = j + 1 < n_tiles;
+    if (more) {
       kt.load(K, kb0 + BK, L, tid);
       vt.load(V, kb0 + BK, L, tid);
     }
-    if (!active || kb0 > wq_hi) continue;
-
-    f32x4 s[MK][NQT];
-#pragma unroll
-    for (int mk = 0; mk < MK; ++mk)
-#pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) s[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-      for (int mk = 0; mk < MK; ++mk) {
-        const frag a = ld8(&Ks[(mk * 16 + n) * KS + kb * 32 + 8 * g]);
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) E::mma(s[mk][nt], a, qf[nt][kb]);
-      }
-
-    const bool need_mask = kb0 + BK - 1 > wq_lo;
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-      const int qp = wq_lo + nt * 16 + n;
-      float mx = -kInf;
+    if (active && kb0 <= wq_hi) {
+      const T* Kc = Ks[cur];
+      const T* Vc = Vs[cur];
+      f32x4 s[MK][NQT];
 #pragma unroll
       for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[mk][nt][i] * p.c2;
-          if (need_mask && kb0 + mk * 16 + 4 * g + i > qp) x = -kInf;
-          s[mk][nt][i] = x;
-          mx = fmaxf(mx, x);
+        for (int nt = 0; nt < NQT; ++nt) s[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk) {
+          const frag a = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) E::mma(s[mk][nt], a, qf[nt][kb]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[nt], mx);
-      const float alpha = fexp2(mrun[nt] - mnew);
-      mrun[nt] = mnew;
-      float lsum = 0.f;
+
+      const bool diag = kb0 + BK - 1 > wq_lo;
+      bool grow = false;
+      float mx2[NQT];
 #pragma unroll
-      for (int mk = 0; mk < MK; ++mk)
+      for (int nt = 0; nt < NQT; ++nt) {
+        const int qp = wq_lo + nt * 16 + n;
+        float mx = -kInf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fexp2(s[mk][nt][i] - mnew);
-          s[mk][nt][i] = e;
-          lsum += e;
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (diag && kb0 + mk * 16 + 4 * g + i > qp) s[mk][nt][i] = -kInf;
+            mx = fmaxf(mx, s[mk][nt][i]);
+          }
+        mx2[nt] = wave_max16x4(mx) * c2;
+        grow |= mx2[nt] > m2[nt] + kRescale;
+      }
+      if (__any(grow)) {
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+          const float mnew = fmaxf(m2[nt], mx2[nt]);
+          const float alpha = fexp2(m2[nt] - mnew);
+          m2[nt] = mnew;
+          lrun[nt] *= alpha;
+#pragma unroll
+          for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;
         }
-      lrun[nt] = lrun[nt] * alpha + lsum;
+      }
 #pragma unroll
-      for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;
-    }
+      for (int nt = 0; nt < NQT; ++nt) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e = fexp2(__builtin_fmaf(s[mk][nt][i], c2, -m2[nt]));
+            s[mk][nt][i] = e;
+            lsum += e;
+          }
+        lrun[nt] += lsum;
+      }
 
 #pragma unroll
-    for (int kb2 = 0; kb2 < KB2; ++kb2) {
-      frag pf[NQT];
+      for (int kb2 = 0; kb2 < KB2; ++kb2) {
+        frag pf[NQT];
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) pf[nt] = pack44<T>(s[2 * kb2][nt], s[2 * kb2 + 1][nt]);
+        for (int nt = 0; nt < NQT; ++nt) pf[nt] = pack44<T>(s[2 * kb2][nt], s[2 * kb2 + 1][nt]);
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const frag a = ld44(&Vt[(md * 16 + n) * VS + kb2 * 32 + 4 * g]);
+        for (int md = 0; md < MD; ++md) {
+          const frag a = ldT8<D>(Vc, kb2 * 32, md * 16, lane);
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) E::mma(oacc[md][nt], a, pf[nt]);
+          for (int nt = 0; nt < NQT; ++nt) E::mma(oacc[md][nt], a, pf[nt]);
+        }
       }
     }
+    if (more) {
+      kt.store(Ks[cur ^ 1], tid);
+      vt.store(Vs[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
 
   if (!active) return;
@@ -333,7 +393,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
       const float inv = 1.f / l;
 #pragma unroll
       for (int md = 0; md < MD; ++md) store4<T>(O + (size_t)row * D + md * 16 + 4 * g, oacc[md][nt], inv);
-      if (g == 0) LSE[row] = (mrun[nt] + __builtin_amdgcn_logf(l)) * kLn2;
+      if (g == 0) LSE[row] = (m2[nt] + __builtin_amdgcn_logf(l)) * kLn2;
     }
   }
 }
@@ -375,25 +435,24 @@ struct BwdParams {
   float* dk;
   float* dv;
   int hq, hkv, q_cap, kv_cap, q_off, start, len;
-  float c2;        // softmax scale * log2(e)
+  float c2;        // |softmax scale| * log2(e), > 0
+  int neg;         // softmax scale < 0
   float dq_scale;  // grad_scale * softmax scale
   float dk_scale;  // grad_scale * softmax scale
   float dv_scale;  // grad_scale
 };
 
-// dQ pass. Same walk as the forward (grid over query tiles, key tiles through
-// LDS): S^T = K Q^T and dP^T = V dO^T from row-major K, V; P from the stored
-// LSE; dQ^T += K^T dS^T from a transposed copy of K made from the same loads.
+// dQ pass. Same walk as the forward: S^T = K Q^T and dP^T = V dO^T with K, V
+// row-major from LDS, P from the stored LSE, and dQ^T += K^T dS^T with K read
+// through the transposing LDS path.
 template <typename T, int D, int NQT, int BK, int NW>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
   constexpr int NT = NW * 64, BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
-  constexpr int PAD = 16 / sizeof(T), KS = D + PAD, VS = BK + PAD;
-  __shared__ __attribute__((aligned(16))) T Ks[BK * KS];
-  __shared__ __attribute__((aligned(16))) T Vs[BK * KS];
-  __shared__ __attribute__((aligned(16))) T Kt[D * VS];
+  __shared__ __attribute__((aligned(16))) T Ks[2][BK * D];
+  __shared__ __attribute__((aligned(16))) T Vs[2][BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -414,6 +473,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   const bool active = wr0 < p.len;
   const int wq_lo = p.start + wr0;
   const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
+  const float c2 = p.c2;
 
   frag qf[NQT][DK], df[NQT][DK];
   float lse2[NQT], dl[NQT];
@@ -423,8 +483,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
     const bool ok = row < p.len;
 #pragma unroll
     for (int kb = 0; kb < DK; ++kb) {
-      qf[nt][kb] = ok ? ld8(Q + (size_t)row * D + kb * 32 + 8 * g) : frag{};
-      df[nt][kb] = ok ? ld8(dO + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+      qf[nt][kb] = ok ? ldg8(Q + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+      if (p.neg) qf[nt][kb] = negate<T>(qf[nt][kb]);
+      df[nt][kb] = ok ? ldg8(dO + (size_t)row * D + kb * 32 + 8 * g) : frag{};
     }
     lse2[nt] = ok ? LSE[row] * kLog2e : kInf;
     dl[nt] = ok ? DL[row] : 0.f;
@@ -438,66 +499,72 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   Tile<T, BK, D, NT> kt, vt;
   kt.load(K, 0, L, tid);
   vt.load(V, 0, L, tid);
+  kt.store(Ks[0], tid);
+  vt.store(Vs[0], tid);
+  __syncthreads();
   for (int j = 0; j < n_tiles; ++j) {
-    const int kb0 = j * BK;
-    __syncthreads();
-    kt.store_rows(Ks, KS, tid);
-    kt.store_cols(Kt, VS, tid);
-    vt.store_rows(Vs, KS, tid);
-    __syncthreads();
-    if (j + 1 < n_tiles) {
+    const int kb0 = j * BK, cur = j & 1;
+    const bool more = j + 1 < n_tiles;
+    if (more) {
       kt.load(K, kb0 + BK, L, tid);
       vt.load(V, kb0 + BK, L, tid);
     }
-    if (!active || kb0 > wq_hi) continue;
-
-    f32x4 s[MK][NQT], dp[MK][NQT];
-#pragma unroll
-    for (int mk = 0; mk < MK; ++mk)
-#pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) {
-        s[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-      for (int mk = 0; mk < MK; ++mk) {
-        const frag ak = ld8(&Ks[(mk * 16 + n) * KS + kb * 32 + 8 * g]);
-        const frag av = ld8(&Vs[(mk * 16 + n) * KS + kb * 32 + 8 * g]);
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-          E::mma(s[mk][nt], ak, qf[nt][kb]);
-          E::mma(dp[mk][nt], av, df[nt][kb]);
-        }
-      }
-
-    const bool need_mask = kb0 + BK - 1 > wq_lo;
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-      const int qp = wq_lo + nt * 16 + n;
+    if (active && kb0 <= wq_hi) {
+      const T* Kc = Ks[cur];
+      const T* Vc = Vs[cur];
+      f32x4 s[MK][NQT], dp[MK][NQT];
 #pragma unroll
       for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float pr = fexp2(s[mk][nt][i] * p.c2 - lse2[nt]);
-          if (need_mask && kb0 + mk * 16 + 4 * g + i > qp) pr = 0.f;
-          dp[mk][nt][i] = pr * (dp[mk][nt][i] - dl[nt]);
+        for (int nt = 0; nt < NQT; ++nt) {
+          s[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    }
+#pragma unroll
+      for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk) {
+          const frag ak = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
+          const frag av = ld8s<D>(Vc, mk * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) {
+            E::mma(s[mk][nt], ak, qf[nt][kb]);
+            E::mma(dp[mk][nt], av, df[nt][kb]);
+          }
+        }
+
+      const bool diag = kb0 + BK - 1 > wq_lo;
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) {
+        const int qp = wq_lo + nt * 16 + n;
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float pr = fexp2(__builtin_fmaf(s[mk][nt][i], c2, -lse2[nt]));
+            if (diag && kb0 + mk * 16 + 4 * g + i > qp) pr = 0.f;
+            dp[mk][nt][i] = pr * (dp[mk][nt][i] - dl[nt]);
+          }
+      }
 
 #pragma unroll
-    for (int kb2 = 0; kb2 < KB2; ++kb2) {
-      frag dsf[NQT];
+      for (int kb2 = 0; kb2 < KB2; ++kb2) {
+        frag dsf[NQT];
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) dsf[nt] = pack44<T>(dp[2 * kb2][nt], dp[2 * kb2 + 1][nt]);
+        for (int nt = 0; nt < NQT; ++nt) dsf[nt] = pack44<T>(dp[2 * kb2][nt], dp[2 * kb2 + 1][nt]);
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const frag a = ld44(&Kt[(md * 16 + n) * VS + kb2 * 32 + 4 * g]);
+        for (int md = 0; md < MD; ++md) {
+          const frag a = ldT8<D>(Kc, kb2 * 32, md * 16, lane);
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], a, dsf[nt]);
+          for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], a, dsf[nt]);
+        }
       }
     }
+    if (more) {
+      kt.store(Ks[cur ^ 1], tid);
+      vt.store(Vs[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
 
   if (!active) return;
@@ -516,20 +583,19 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
 // dK/dV pass. Grid (key tiles of NW*NKT*16 rows, Hkv, batch); each wave keeps
 // its NKT*16 keys' K and V fragments and dK, dV sums in registers and walks
 // every (q head of the group, query tile) that can see them. Query tiles are
-// staged in LDS row-major (A operand of S = Q K^T and dP = dO V^T) and
-// transposed (B operand of dK = dS^T Q and dV = P^T dO).
+// staged once in LDS: read row-major as the A operand of S = Q K^T and
+// dP = dO V^T, and through the transposing path as the B operand of
+// dK = dS^T Q and dV = P^T dO.
 template <typename T, int D, int NKT, int BQ, int NW>
 __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
   constexpr int NT = NW * 64, BKV = NW * NKT * 16;
   constexpr int DK = D / 32, MD = D / 16, MQ = BQ / 16, KQ = BQ / 32;
-  constexpr int PAD = 16 / sizeof(T), KS = D + PAD, QS = BQ + PAD;
-  __shared__ __attribute__((aligned(16))) T Qs[BQ * KS];
-  __shared__ __attribute__((aligned(16))) T Ds[BQ * KS];
-  __shared__ __attribute__((aligned(16))) T Qt[D * QS];
-  __shared__ __attribute__((aligned(16))) T Dt[D * QS];
-  __shared__ float lse_s[BQ], dl_s[BQ];
+  __shared__ __attribute__((aligned(16))) T Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) T Ds[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dl_s[2][BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -541,6 +607,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
   const int wk0 = kb0 + wave * NKT * 16;
   const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
   const T* V = (const T*)p.v + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const float c2 = p.c2;
 
   frag kf[NKT][DK], vf[NKT][DK];
 #pragma unroll
@@ -549,8 +616,9 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
     const bool ok = key < L;
 #pragma unroll
     for (int kb = 0; kb < DK; ++kb) {
-      kf[nk][kb] = ok ? ld8(K + (size_t)key * D + kb * 32 + 8 * g) : frag{};
-      vf[nk][kb] = ok ? ld8(V + (size_t)key * D + kb * 32 + 8 * g) : frag{};
+      kf[nk][kb] = ok ? ldg8(K + (size_t)key * D + kb * 32 + 8 * g) : frag{};
+      if (p.neg) kf[nk][kb] = negate<T>(kf[nk][kb]);
+      vf[nk][kb] = ok ? ldg8(V + (size_t)key * D + kb * 32 + 8 * g) : frag{};
     }
   }
   f32x4 dka[NKT][MD], dva[NKT][MD];
@@ -580,81 +648,91 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
       dl_r = r < p.len ? p.delta[(size_t)(b * p.hq + h) * p.len + r] : 0.f;
     }
   };
-  if (iters > 0) load(0);
-  for (int it = 0; it < iters; ++it) {
-    const int q0 = (qt0 + it % nq) * BQ;
-    __syncthreads();
-    qtile.store_rows(Qs, KS, tid);
-    qtile.store_cols(Qt, QS, tid);
-    dtile.store_rows(Ds, KS, tid);
-    dtile.store_cols(Dt, QS, tid);
+  auto stage = [&](int buf) {
+    qtile.store(Qs[buf], tid);
+    dtile.store(Ds[buf], tid);
     if (tid < BQ) {
-      lse_s[tid] = lse_r;
-      dl_s[tid] = dl_r;
+      lse_s[buf][tid] = lse_r;
+      dl_s[buf][tid] = dl_r;
     }
-    __syncthreads();
-    if (it + 1 < iters) load(it + 1);
+  };
+  if (iters > 0) {
+    load(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < iters; ++it) {
+    const int cur = it & 1;
+    const bool more = it + 1 < iters;
+    const int q0 = (qt0 + it % nq) * BQ;
+    if (more) load(it + 1);
 
     const int q_lo = p.start + q0;
     const int q_hi = p.start + min(q0 + BQ, p.len) - 1;
-    if (wk0 >= L || wk0 > q_hi) continue;
-    const bool need_mask = q_lo < wk0 + NKT * 16 - 1;
+    if (wk0 < L && wk0 <= q_hi) {
+      const T* Qc = Qs[cur];
+      const T* Dc = Ds[cur];
+      const bool diag = q_lo < wk0 + NKT * 16 - 1;
+      f32x4 s[MQ][NKT], dp[MQ][NKT];
+#pragma unroll
+      for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+        for (int nk = 0; nk < NKT; ++nk) {
+          s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
+          dp[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq) {
+          const frag aq = ld8s<D>(Qc, mq * 16 + n, kb * 32 + 8 * g);
+          const frag ad = ld8s<D>(Dc, mq * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+          for (int nk = 0; nk < NKT; ++nk) {
+            E::mma(s[mq][nk], aq, kf[nk][kb]);
+            E::mma(dp[mq][nk], ad, vf[nk][kb]);
+          }
+        }
 
-    f32x4 s[MQ][NKT], dp[MQ][NKT];
-#pragma unroll
-    for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-      for (int nk = 0; nk < NKT; ++nk) {
-        s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
       for (int mq = 0; mq < MQ; ++mq) {
-        const frag aq = ld8(&Qs[(mq * 16 + n) * KS + kb * 32 + 8 * g]);
-        const frag ad = ld8(&Ds[(mq * 16 + n) * KS + kb * 32 + 8 * g]);
+        const f32x4 l4 = *(const f32x4*)&lse_s[cur][mq * 16 + 4 * g];
+        const f32x4 d4 = *(const f32x4*)&dl_s[cur][mq * 16 + 4 * g];
 #pragma unroll
-        for (int nk = 0; nk < NKT; ++nk) {
-          E::mma(s[mq][nk], aq, kf[nk][kb]);
-          E::mma(dp[mq][nk], ad, vf[nk][kb]);
+        for (int i = 0; i < 4; ++i) {
+          const int qp = q_lo + mq * 16 + 4 * g + i;
+#pragma unroll
+          for (int nk = 0; nk < NKT; ++nk) {
+            float pr = fexp2(__builtin_fmaf(s[mq][nk][i], c2, -l4[i]));
+            if (diag && wk0 + nk * 16 + n > qp) pr = 0.f;
+            s[mq][nk][i] = pr;
+            dp[mq][nk][i] = pr * (dp[mq][nk][i] - d4[i]);
+          }
         }
       }
 
 #pragma unroll
-    for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = mq * 16 + 4 * g + i;
-        const float l2 = lse_s[rr], dlt = dl_s[rr];
+      for (int kq = 0; kq < KQ; ++kq) {
+        frag pf[NKT], dsf[NKT];
 #pragma unroll
         for (int nk = 0; nk < NKT; ++nk) {
-          float pr = fexp2(s[mq][nk][i] * p.c2 - l2);
-          if (need_mask && wk0 + nk * 16 + n > q_lo + rr) pr = 0.f;
-          s[mq][nk][i] = pr;
-          dp[mq][nk][i] = pr * (dp[mq][nk][i] - dlt);
+          pf[nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
+          dsf[nk] = pack44<T>(dp[2 * kq][nk], dp[2 * kq + 1][nk]);
         }
-      }
-
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) {
-      frag pf[NKT], dsf[NKT];
+        for (int md = 0; md < MD; ++md) {
+          const frag bd = ldT8<D>(Dc, kq * 32, md * 16, lane);
+          const frag bq = ldT8<D>(Qc, kq * 32, md * 16, lane);
 #pragma unroll
-      for (int nk = 0; nk < NKT; ++nk) {
-        pf[nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
-        dsf[nk] = pack44<T>(dp[2 * kq][nk], dp[2 * kq + 1][nk]);
-      }
-#pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const frag bd = ld44(&Dt[(md * 16 + n) * QS + kq * 32 + 4 * g]);
-        const frag bq = ld44(&Qt[(md * 16 + n) * QS + kq * 32 + 4 * g]);
-#pragma unroll
-        for (int nk = 0; nk < NKT; ++nk) {
-          E::mma(dva[nk][md], pf[nk], bd);
-          E::mma(dka[nk][md], dsf[nk], bq);
+          for (int nk = 0; nk < NKT; ++nk) {
+            E::mma(dva[nk][md], pf[nk], bd);
+            E::mma(dka[nk][md], dsf[nk], bq);
+          }
         }
       }
     }
+    if (more) stage(cur ^ 1);
+    __syncthreads();
   }
 
   float* DKp = p.dk + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
@@ -708,13 +786,30 @@ struct Cfg {
   static constexpr int DQ_NQT = 2, DQ_BK = 64, DQ_NW = 4;
   static constexpr int KV_NKT = 2, KV_BQ = 64, KV_NW = 4;
 };
+// float32 storage (the exactness path) takes smaller tiles: its fragments are
+// twice as wide in registers.
+template <int D>
+struct Cfg<float, D> {
+  static constexpr int FWD_NQT = 1, FWD_BK = 32, FWD_NW = 4;
+  static constexpr int DQ_NQT = 1, DQ_BK = 32, DQ_NW = 4;
+  static constexpr int KV_NKT = 1, KV_BQ = 32, KV_NW = 4;
+};
+
+// |scale| * log2(e), kept strictly positive so that a masked score of -inf
+// times it stays -inf (a zero scale becomes 1e-30: every score then weighs
+// exp(~0) = 1, as it should).
+float exp2_coef(float scale) {
+  const float c = fabsf(scale) * kLog2e;
+  return c > 1e-30f ? c : 1e-30f;
+}
 
 template <typename T, int D>
 hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse,
                     hipStream_t st) {
   using C = Cfg<T, D>;
   constexpr int BQ = C::FWD_NW * C::FWD_NQT * 16;
-  FwdParams p{q, k, v, o, lse, s.hq, s.hkv, s.q_cap, s.kv_cap, s.q_off, s.start, s.len, s.scale * kLog2e};
+  FwdParams p{q,     k,     v,       o,        lse,     s.hq,    s.hkv, s.q_cap, s.kv_cap, s.q_off,
+              s.start, s.len, exp2_coef(s.scale), s.scale < 0.f ? 1 : 0};
   dim3 grid((s.len + BQ - 1) / BQ, s.hq, s.batch);
   prof_begin(CA_KERNEL_FWD, st);
   hipLaunchKernelGGL((fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), grid, dim3(C::FWD_NW * 64), 0,
@@ -737,8 +832,9 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   prof_end(CA_KERNEL_DELTA, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  BwdParams p{q, k, v, dout, lse, delta, dq, dk, dv, s.hq, s.hkv, s.q_cap, s.kv_cap, s.q_off, s.start,
-              s.len, s.scale * kLog2e, gs * s.scale, gs * s.scale, gs};
+  BwdParams p{q,        k,       v,     dout,  lse,     delta,   dq,       dk,
+              dv,       s.hq,    s.hkv, s.q_cap, s.kv_cap, s.q_off, s.start, s.len,
+              exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs};
   constexpr int BKV = C::KV_NW * C::KV_NKT * 16;
   const int L = s.start + s.len;
   prof_begin(CA_KERNEL_DKDV, st);
@@ -759,7 +855,7 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
 
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse,
                       hipStream_t st) {
-  if (s.dtype == 1) {
+  if (s.dtype == CA_BF16) {
     return s.head_dim == 128 ? fwd_impl<bf16, 128>(s, q, k, v, o, lse, st)
                              : fwd_impl<bf16, 64>(s, q, k, v, o, lse, st);
   }
@@ -770,7 +866,7 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
                       float* delta, hipStream_t st) {
-  if (s.dtype == 1) {
+  if (s.dtype == CA_BF16) {
     return s.head_dim == 128 ? bwd_impl<bf16, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st)
                              : bwd_impl<bf16, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st);
   }
