@@ -87,7 +87,7 @@ ca::Shape shape_of(const chunk_attn_desc* d) {
 }
 
 size_t delta_bytes(const chunk_attn_desc* d) {
-  return round_up((size_t)d->batch * d->n_q_heads * d->chunk_len * sizeof(float));
+  return round_up(ca::bwd_ws_bytes((size_t)d->batch * d->n_q_heads * d->chunk_len));
 }
 
 int check_ptrs(std::initializer_list<const void*> ps) {

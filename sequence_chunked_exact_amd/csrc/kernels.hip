@@ -189,41 +189,58 @@ __device__ __forceinline__ void store4(T* dst, const f32x4& x, float mul) {
   *(typename Elt<T>::quad*)dst = v;
 }
 
-__device__ __forceinline__ float wave_max16x4(float m) {
+// Maximum / sum over the 4 lanes l, l^16, l^32, l^48 (the 4 row groups of one
+// output column).
+__device__ __forceinline__ float max4(float m) {
   m = fmaxf(m, __shfl_xor(m, 16));
   return fmaxf(m, __shfl_xor(m, 32));
 }
+__device__ __forceinline__ float sum4(float s) {
+  s += __shfl_xor(s, 16);
+  return s + __shfl_xor(s, 32);
+}
 
-// A [ROWS][D] tile of a row-major head staged through registers: thread tid
-// holds ROWS/GROUPS consecutive rows of one 16-byte column vector (rows at or
-// beyond `limit` read as zero) and writes them into a swizzled LDS tile.
-template <typename T, int ROWS, int D, int NT>
-struct Tile {
-  using V = typename Elt<T>::vec;
-  static constexpr int VEC = Elt<T>::VEC;
-  static constexpr int NDV = D / VEC;      // column vectors per row
-  static constexpr int GROUPS = NT / NDV;  // row groups
-  static constexpr int R = ROWS / GROUPS;  // rows per thread
-  static_assert(NT % NDV == 0 && ROWS % GROUPS == 0 && R >= 1, "tile/thread shape");
-  V r[R];
+typedef __attribute__((address_space(3))) void lds_void;
 
-  __device__ __forceinline__ void load(const T* head, int row0, int limit, int tid) {
-    const int dv = tid % NDV, grp = tid / NDV;
+// Stream rows [row0, row0 + ROWS) of a row-major [*, D] head into a swizzled
+// LDS tile with direct global->LDS loads: each wave instruction fills 64
+// consecutive 16-byte LDS slots, so lane l fetches the global chunk that
+// belongs in its slot (the swizzle is applied on the global side, and each
+// instruction still reads whole rows). Rows at or beyond `limit` (>= 1)
+// re-read row limit-1; every consumer gives such rows zero weight (keys past
+// the prefix are causally masked, query rows past the chunk get LSE = +inf).
+template <typename T, int ROWS, int D, int NW>
+__device__ __forceinline__ void stage_tile(T* lds, const T* head, int row0, int limit, int wave, int lane) {
+  using Lt = Lay<T, D>;
+  constexpr int CH = Lt::CH, RPI = 64 / CH, PER_WAVE = ROWS / NW;
+  static_assert(CH <= 64 && PER_WAVE % RPI == 0, "tile rows per wave must fill whole instructions");
+#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-loading builtin exists only in the device pass
+  const int rl = lane / CH, slot = lane % CH;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int row = row0 + grp * R + i;
-      if (row < limit)
-        r[i] = *(const V*)(head + (size_t)row * D + dv * VEC);
-      else
-        r[i] = V{};
-    }
+  for (int i = 0; i < PER_WAVE / RPI; ++i) {
+    const int rb = wave * PER_WAVE + i * RPI;  // wave-uniform first row of this instruction
+    const int r = rb + rl;
+    const int c = slot ^ Lt::swz(r);
+    const T* src = head + (size_t)min(row0 + r, limit - 1) * D + c * Lt::EPC;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + rb * D), 16, 0, 0);
   }
-  __device__ __forceinline__ void store(T* lds, int tid) const {
-    const int dv = tid % NDV, grp = tid / NDV;
-#pragma unroll
-    for (int i = 0; i < R; ++i) *(V*)(lds + Lay<T, D>::off(grp * R + i, dv * VEC)) = r[i];
-  }
-};
+#endif
+}
+
+// 64 consecutive floats starting at row0 (rows clamped to limit-1) into LDS,
+// 4 bytes per lane of one wave.
+__device__ __forceinline__ void stage_vec64(float* lds, const float* src, int row0, int limit, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src + min(row0 + lane, limit - 1), (lds_void*)lds, 4, 0, 0);
+#endif
+}
+
+// Wait for every outstanding memory operation of this wave (including direct
+// global->LDS loads), then synchronize the workgroup.
+__device__ __forceinline__ void drain_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
 
 // ----------------------------------------------------------------------------
 // Forward. Grid (query tiles, Hq, batch); NW waves, each owning NQT*16 query
@@ -246,12 +263,13 @@ template <typename T, int D, int NQT, int BK, int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int NT = NW * 64, BQ = NW * NQT * 16;
+  constexpr int BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
   __shared__ __attribute__((aligned(16))) T Ks[2][BK * D];
   __shared__ __attribute__((aligned(16))) T Vs[2][BK * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int h = blockIdx.y, b = blockIdx.z;
@@ -268,13 +286,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
   const float c2 = p.c2;
 
+  stage_tile<T, BK, D, NW>(Ks[0], K, 0, L, wave, lane);
+  stage_tile<T, BK, D, NW>(Vs[0], V, 0, L, wave, lane);
+
   frag qf[NQT][DK];
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
-    const int row = wr0 + nt * 16 + n;
+    const int row = min(wr0 + nt * 16 + n, p.len - 1);
 #pragma unroll
     for (int kb = 0; kb < DK; ++kb) {
-      qf[nt][kb] = row < p.len ? ldg8(Q + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+      qf[nt][kb] = ldg8(Q + (size_t)row * D + kb * 32 + 8 * g);
       if (p.neg) qf[nt][kb] = negate<T>(qf[nt][kb]);
     }
   }
@@ -287,23 +308,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) oacc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  drain_and_sync();
 
-  Tile<T, BK, D, NT> kt, vt;
-  kt.load(K, 0, L, tid);
-  vt.load(V, 0, L, tid);
-  kt.store(Ks[0], tid);
-  vt.store(Vs[0], tid);
-  __syncthreads();
+  // Per tile: read every fragment this wave needs from LDS, then start the
+  // next tile's direct-to-LDS loads (so they overlap the math, and no LDS read
+  // of this tile has to wait for them), then compute.
   for (int j = 0; j < n_tiles; ++j) {
     const int kb0 = j * BK, cur = j & 1;
-    const bool more = j + 1 < n_tiles;
-    if (more) {
-      kt.load(K, kb0 + BK, L, tid);
-      vt.load(V, kb0 + BK, L, tid);
-    }
-    if (active && kb0 <= wq_hi) {
+    const bool work = active && kb0 <= wq_hi;
+    frag kfr[DK][MK], vfr[KB2][MD];
+    if (work) {
       const T* Kc = Ks[cur];
       const T* Vc = Vs[cur];
+#pragma unroll
+      for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk) kfr[kb][mk] = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+      for (int kb2 = 0; kb2 < KB2; ++kb2)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) vfr[kb2][md] = ldT8<D>(Vc, kb2 * 32, md * 16, lane);
+    }
+    if (j + 1 < n_tiles) {
+      stage_tile<T, BK, D, NW>(Ks[cur ^ 1], K, kb0 + BK, L, wave, lane);
+      stage_tile<T, BK, D, NW>(Vs[cur ^ 1], V, kb0 + BK, L, wave, lane);
+    }
+    if (work) {
       f32x4 s[MK][NQT];
 #pragma unroll
       for (int mk = 0; mk < MK; ++mk)
@@ -312,27 +342,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
-        for (int mk = 0; mk < MK; ++mk) {
-          const frag a = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
+        for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-          for (int nt = 0; nt < NQT; ++nt) E::mma(s[mk][nt], a, qf[nt][kb]);
-        }
+          for (int nt = 0; nt < NQT; ++nt) E::mma(s[mk][nt], kfr[kb][mk], qf[nt][kb]);
 
-      const bool diag = kb0 + BK - 1 > wq_lo;
+      if (kb0 + BK - 1 > wq_lo) {  // tile crosses this wave's diagonal
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+          const int qp = wq_lo + nt * 16 + n;
+#pragma unroll
+          for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (kb0 + mk * 16 + 4 * g + i > qp) s[mk][nt][i] = -kInf;
+        }
+      }
       bool grow = false;
       float mx2[NQT];
 #pragma unroll
       for (int nt = 0; nt < NQT; ++nt) {
-        const int qp = wq_lo + nt * 16 + n;
         float mx = -kInf;
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (diag && kb0 + mk * 16 + 4 * g + i > qp) s[mk][nt][i] = -kInf;
-            mx = fmaxf(mx, s[mk][nt][i]);
-          }
-        mx2[nt] = wave_max16x4(mx) * c2;
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mk][nt][i]);
+        mx2[nt] = max4(mx) * c2;
         grow |= mx2[nt] > m2[nt] + kRescale;
       }
       if (__any(grow)) {
@@ -359,25 +393,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
           }
         lrun[nt] += lsum;
       }
-
 #pragma unroll
       for (int kb2 = 0; kb2 < KB2; ++kb2) {
         frag pf[NQT];
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt) pf[nt] = pack44<T>(s[2 * kb2][nt], s[2 * kb2 + 1][nt]);
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const frag a = ldT8<D>(Vc, kb2 * 32, md * 16, lane);
+        for (int md = 0; md < MD; ++md)
 #pragma unroll
-          for (int nt = 0; nt < NQT; ++nt) E::mma(oacc[md][nt], a, pf[nt]);
-        }
+          for (int nt = 0; nt < NQT; ++nt) E::mma(oacc[md][nt], vfr[kb2][md], pf[nt]);
       }
     }
-    if (more) {
-      kt.store(Ks[cur ^ 1], tid);
-      vt.store(Vs[cur ^ 1], tid);
-    }
-    __syncthreads();
+    drain_and_sync();
   }
 
   if (!active) return;
@@ -385,9 +412,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   float* LSE = p.lse + (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
-    float l = lrun[nt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = sum4(lrun[nt]);
     const int row = wr0 + nt * 16 + n;
     if (row < p.len) {
       const float inv = 1.f / l;
@@ -399,26 +424,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// delta_r = sum_c dO_rc O_rc in float32; LPR lanes share one row.
+// delta_r = sum_c dO_rc O_rc (float32) and lse2_r = LSE_r * log2(e) for the
+// chunk's rows, both [batch*hq][len]; LPR lanes share one row.
 // ----------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const T* o, const T* dout, float* delta, int q_cap,
-                                                    int q_off, int len, int rows) {
+__global__ __launch_bounds__(256) void delta_kernel(const T* o, const T* dout, const float* lse, float* delta,
+                                                    float* lse2, int q_cap, int q_off, int len, int rows) {
   using V = typename Elt<T>::vec;
   constexpr int VEC = Elt<T>::VEC, LPR = D / VEC;
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = gid / LPR, sub = gid % LPR;
   float acc = 0.f;
+  size_t qrow = 0;
   if (row < rows) {
     const int bh = row / len, r = row % len;
-    const size_t off = ((size_t)bh * q_cap + q_off + r) * D + sub * VEC;
-    const V a = *(const V*)(o + off), c = *(const V*)(dout + off);
+    qrow = (size_t)bh * q_cap + q_off + r;
+    const V a = *(const V*)(o + qrow * D + sub * VEC), c = *(const V*)(dout + qrow * D + sub * VEC);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc += (float)a[e] * (float)c[e];
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && sub == 0) delta[row] = acc;
+  if (row < rows && sub == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[qrow] * kLog2e;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -429,8 +459,9 @@ struct BwdParams {
   const void* k;
   const void* v;
   const void* dout;
-  const float* lse;
+  const float* lse;    // natural-log LSE, q-side layout
   const float* delta;  // [batch*hq][len]
+  const float* lse2;   // [batch*hq][len], LSE * log2(e)
   float* dq;
   float* dk;
   float* dv;
@@ -449,12 +480,13 @@ template <typename T, int D, int NQT, int BK, int NW>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int NT = NW * 64, BQ = NW * NQT * 16;
+  constexpr int BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
   __shared__ __attribute__((aligned(16))) T Ks[2][BK * D];
   __shared__ __attribute__((aligned(16))) T Vs[2][BK * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int qt = gridDim.x - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
@@ -462,7 +494,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   const size_t qhead = ((size_t)(b * p.hq + h) * p.q_cap + p.q_off);
   const T* Q = (const T*)p.q + qhead * D;
   const T* dO = (const T*)p.dout + qhead * D;
-  const float* LSE = p.lse + qhead;
+  const float* LSE2 = p.lse2 + (size_t)(b * p.hq + h) * p.len;
   const float* DL = p.delta + (size_t)(b * p.hq + h) * p.len;
   const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
   const T* V = (const T*)p.v + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
@@ -475,43 +507,55 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
   const float c2 = p.c2;
 
+  stage_tile<T, BK, D, NW>(Ks[0], K, 0, L, wave, lane);
+  stage_tile<T, BK, D, NW>(Vs[0], V, 0, L, wave, lane);
+
   frag qf[NQT][DK], df[NQT][DK];
   float lse2[NQT], dl[NQT];
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
     const int row = wr0 + nt * 16 + n;
-    const bool ok = row < p.len;
+    const int rc = min(row, p.len - 1);
 #pragma unroll
     for (int kb = 0; kb < DK; ++kb) {
-      qf[nt][kb] = ok ? ldg8(Q + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+      qf[nt][kb] = ldg8(Q + (size_t)rc * D + kb * 32 + 8 * g);
       if (p.neg) qf[nt][kb] = negate<T>(qf[nt][kb]);
-      df[nt][kb] = ok ? ldg8(dO + (size_t)row * D + kb * 32 + 8 * g) : frag{};
+      df[nt][kb] = ldg8(dO + (size_t)rc * D + kb * 32 + 8 * g);
     }
-    lse2[nt] = ok ? LSE[row] * kLog2e : kInf;
-    dl[nt] = ok ? DL[row] : 0.f;
+    lse2[nt] = row < p.len ? LSE2[rc] : kInf;
+    dl[nt] = DL[rc];
   }
   f32x4 acc[MD][NQT];
 #pragma unroll
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  drain_and_sync();
 
-  Tile<T, BK, D, NT> kt, vt;
-  kt.load(K, 0, L, tid);
-  vt.load(V, 0, L, tid);
-  kt.store(Ks[0], tid);
-  vt.store(Vs[0], tid);
-  __syncthreads();
   for (int j = 0; j < n_tiles; ++j) {
     const int kb0 = j * BK, cur = j & 1;
-    const bool more = j + 1 < n_tiles;
-    if (more) {
-      kt.load(K, kb0 + BK, L, tid);
-      vt.load(V, kb0 + BK, L, tid);
-    }
-    if (active && kb0 <= wq_hi) {
+    const bool work = active && kb0 <= wq_hi;
+    frag kfr[DK][MK], vfr[DK][MK], ktr[KB2][MD];
+    if (work) {  // all LDS reads of this tile before the next tile's loads start
       const T* Kc = Ks[cur];
       const T* Vc = Vs[cur];
+#pragma unroll
+      for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk) {
+          kfr[kb][mk] = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
+          vfr[kb][mk] = ld8s<D>(Vc, mk * 16 + n, kb * 32 + 8 * g);
+        }
+#pragma unroll
+      for (int kb2 = 0; kb2 < KB2; ++kb2)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) ktr[kb2][md] = ldT8<D>(Kc, kb2 * 32, md * 16, lane);
+    }
+    if (j + 1 < n_tiles) {
+      stage_tile<T, BK, D, NW>(Ks[cur ^ 1], K, kb0 + BK, L, wave, lane);
+      stage_tile<T, BK, D, NW>(Vs[cur ^ 1], V, kb0 + BK, L, wave, lane);
+    }
+    if (work) {
       f32x4 s[MK][NQT], dp[MK][NQT];
 #pragma unroll
       for (int mk = 0; mk < MK; ++mk)
@@ -523,29 +567,36 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
-        for (int mk = 0; mk < MK; ++mk) {
-          const frag ak = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
-          const frag av = ld8s<D>(Vc, mk * 16 + n, kb * 32 + 8 * g);
+        for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
           for (int nt = 0; nt < NQT; ++nt) {
-            E::mma(s[mk][nt], ak, qf[nt][kb]);
-            E::mma(dp[mk][nt], av, df[nt][kb]);
+            E::mma(s[mk][nt], kfr[kb][mk], qf[nt][kb]);
+            E::mma(dp[mk][nt], vfr[kb][mk], df[nt][kb]);
           }
-        }
 
-      const bool diag = kb0 + BK - 1 > wq_lo;
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) {
-        const int qp = wq_lo + nt * 16 + n;
+      for (int nt = 0; nt < NQT; ++nt)
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float pr = fexp2(__builtin_fmaf(s[mk][nt][i], c2, -lse2[nt]));
-            if (diag && kb0 + mk * 16 + 4 * g + i > qp) pr = 0.f;
-            dp[mk][nt][i] = pr * (dp[mk][nt][i] - dl[nt]);
-          }
+          for (int i = 0; i < 4; ++i) s[mk][nt][i] = fexp2(__builtin_fmaf(s[mk][nt][i], c2, -lse2[nt]));
+      if (kb0 + BK - 1 > wq_lo) {  // tile crosses this wave's diagonal
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+          const int qp = wq_lo + nt * 16 + n;
+#pragma unroll
+          for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (kb0 + mk * 16 + 4 * g + i > qp) s[mk][nt][i] = 0.f;
+        }
       }
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt)
+#pragma unroll
+        for (int mk = 0; mk < MK; ++mk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dp[mk][nt][i] = s[mk][nt][i] * (dp[mk][nt][i] - dl[nt]);
 
 #pragma unroll
       for (int kb2 = 0; kb2 < KB2; ++kb2) {
@@ -553,18 +604,12 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt) dsf[nt] = pack44<T>(dp[2 * kb2][nt], dp[2 * kb2 + 1][nt]);
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const frag a = ldT8<D>(Kc, kb2 * 32, md * 16, lane);
+        for (int md = 0; md < MD; ++md)
 #pragma unroll
-          for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], a, dsf[nt]);
-        }
+          for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], ktr[kb2][md], dsf[nt]);
       }
     }
-    if (more) {
-      kt.store(Ks[cur ^ 1], tid);
-      vt.store(Vs[cur ^ 1], tid);
-    }
-    __syncthreads();
+    drain_and_sync();
   }
 
   if (!active) return;
@@ -590,14 +635,16 @@ template <typename T, int D, int NKT, int BQ, int NW>
 __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int NT = NW * 64, BKV = NW * NKT * 16;
+  constexpr int BKV = NW * NKT * 16;
   constexpr int DK = D / 32, MD = D / 16, MQ = BQ / 16, KQ = BQ / 32;
+  static_assert(BQ <= 64, "row statistics are staged 64 rows per wave instruction");
   __shared__ __attribute__((aligned(16))) T Qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) T Ds[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float dl_s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][64];
+  __shared__ __attribute__((aligned(16))) float dl_s[2][64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int kt = gridDim.x - 1 - blockIdx.x;  // keys with the most queries first
   const int hk = blockIdx.y, b = blockIdx.z;
@@ -609,16 +656,31 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
   const T* V = (const T*)p.v + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
   const float c2 = p.c2;
 
+  // Query rows that can see key kb0: chunk rows r with start + r >= kb0.
+  const int qt0 = max(0, kb0 - p.start) / BQ;
+  const int nq = (p.len + BQ - 1) / BQ - qt0;
+  const int iters = G * nq;
+
+  auto stage = [&](int it, int buf) {
+    const int h = hk * G + it / nq, q0 = (qt0 + it % nq) * BQ;
+    const size_t qhead = (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
+    const size_t rhead = (size_t)(b * p.hq + h) * p.len;
+    stage_tile<T, BQ, D, NW>(Qs[buf], (const T*)p.q + qhead * D, q0, p.len, wave, lane);
+    stage_tile<T, BQ, D, NW>(Ds[buf], (const T*)p.dout + qhead * D, q0, p.len, wave, lane);
+    if (wave == 0) stage_vec64(lse_s[buf], p.lse2 + rhead, q0, p.len, lane);
+    if (wave == 1 % NW) stage_vec64(dl_s[buf], p.delta + rhead, q0, p.len, lane);
+  };
+  if (iters > 0) stage(0, 0);
+
   frag kf[NKT][DK], vf[NKT][DK];
 #pragma unroll
   for (int nk = 0; nk < NKT; ++nk) {
-    const int key = wk0 + nk * 16 + n;
-    const bool ok = key < L;
+    const int key = min(wk0 + nk * 16 + n, L - 1);
 #pragma unroll
     for (int kb = 0; kb < DK; ++kb) {
-      kf[nk][kb] = ok ? ldg8(K + (size_t)key * D + kb * 32 + 8 * g) : frag{};
+      kf[nk][kb] = ldg8(K + (size_t)key * D + kb * 32 + 8 * g);
       if (p.neg) kf[nk][kb] = negate<T>(kf[nk][kb]);
-      vf[nk][kb] = ok ? ldg8(V + (size_t)key * D + kb * 32 + 8 * g) : frag{};
+      vf[nk][kb] = ldg8(V + (size_t)key * D + kb * 32 + 8 * g);
     }
   }
   f32x4 dka[NKT][MD], dva[NKT][MD];
@@ -629,51 +691,31 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
       dka[nk][md] = f32x4{0.f, 0.f, 0.f, 0.f};
       dva[nk][md] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  drain_and_sync();
 
-  // Query rows that can see key kb0: chunk rows r with start + r >= kb0.
-  const int qt0 = max(0, kb0 - p.start) / BQ;
-  const int nq = (p.len + BQ - 1) / BQ - qt0;
-  const int iters = G * nq;
-
-  Tile<T, BQ, D, NT> qtile, dtile;
-  float lse_r = 0.f, dl_r = 0.f;
-  auto load = [&](int it) {
-    const int h = hk * G + it / nq, q0 = (qt0 + it % nq) * BQ;
-    const size_t qhead = (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
-    qtile.load((const T*)p.q + qhead * D, q0, p.len, tid);
-    dtile.load((const T*)p.dout + qhead * D, q0, p.len, tid);
-    if (tid < BQ) {
-      const int r = q0 + tid;
-      lse_r = r < p.len ? p.lse[qhead + r] * kLog2e : kInf;
-      dl_r = r < p.len ? p.delta[(size_t)(b * p.hq + h) * p.len + r] : 0.f;
-    }
-  };
-  auto stage = [&](int buf) {
-    qtile.store(Qs[buf], tid);
-    dtile.store(Ds[buf], tid);
-    if (tid < BQ) {
-      lse_s[buf][tid] = lse_r;
-      dl_s[buf][tid] = dl_r;
-    }
-  };
-  if (iters > 0) {
-    load(0);
-    stage(0);
-  }
-  __syncthreads();
   for (int it = 0; it < iters; ++it) {
     const int cur = it & 1;
-    const bool more = it + 1 < iters;
     const int q0 = (qt0 + it % nq) * BQ;
-    if (more) load(it + 1);
-
     const int q_lo = p.start + q0;
     const int q_hi = p.start + min(q0 + BQ, p.len) - 1;
-    if (wk0 < L && wk0 <= q_hi) {
+    const bool work = wk0 < L && wk0 <= q_hi;
+    // Row-major fragments -> S and dP; then the transposing reads and the row
+    // statistics; only then the next tile's direct-to-LDS loads, which overlap
+    // the exponentials and the dV / dK products.
+    f32x4 s[MQ][NKT], dp[MQ][NKT];
+    frag qtr[KQ][MD], dtr[KQ][MD];
+    f32x4 l4[MQ], d4[MQ];
+    if (work) {
       const T* Qc = Qs[cur];
       const T* Dc = Ds[cur];
-      const bool diag = q_lo < wk0 + NKT * 16 - 1;
-      f32x4 s[MQ][NKT], dp[MQ][NKT];
+      frag qfr[DK][MQ], dfr[DK][MQ];
+#pragma unroll
+      for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq) {
+          qfr[kb][mq] = ld8s<D>(Qc, mq * 16 + n, kb * 32 + 8 * g);
+          dfr[kb][mq] = ld8s<D>(Dc, mq * 16 + n, kb * 32 + 8 * g);
+        }
 #pragma unroll
       for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
@@ -684,31 +726,52 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq) {
-          const frag aq = ld8s<D>(Qc, mq * 16 + n, kb * 32 + 8 * g);
-          const frag ad = ld8s<D>(Dc, mq * 16 + n, kb * 32 + 8 * g);
+        for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk) {
-            E::mma(s[mq][nk], aq, kf[nk][kb]);
-            E::mma(dp[mq][nk], ad, vf[nk][kb]);
+            E::mma(s[mq][nk], qfr[kb][mq], kf[nk][kb]);
+            E::mma(dp[mq][nk], dfr[kb][mq], vf[nk][kb]);
           }
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          dtr[kq][md] = ldT8<D>(Dc, kq * 32, md * 16, lane);
+          qtr[kq][md] = ldT8<D>(Qc, kq * 32, md * 16, lane);
         }
-
 #pragma unroll
       for (int mq = 0; mq < MQ; ++mq) {
-        const f32x4 l4 = *(const f32x4*)&lse_s[cur][mq * 16 + 4 * g];
-        const f32x4 d4 = *(const f32x4*)&dl_s[cur][mq * 16 + 4 * g];
+        l4[mq] = *(const f32x4*)&lse_s[cur][mq * 16 + 4 * g];
+        d4[mq] = *(const f32x4*)&dl_s[cur][mq * 16 + 4 * g];
+      }
+    }
+    if (it + 1 < iters) stage(it + 1, cur ^ 1);
+
+    if (work) {
+      const bool tail = q0 + BQ > p.len;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qp = q_lo + mq * 16 + 4 * g + i;
+      for (int mq = 0; mq < MQ; ++mq) {
+        if (tail) {
 #pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) {
-            float pr = fexp2(__builtin_fmaf(s[mq][nk][i], c2, -l4[i]));
-            if (diag && wk0 + nk * 16 + n > qp) pr = 0.f;
-            s[mq][nk][i] = pr;
-            dp[mq][nk][i] = pr * (dp[mq][nk][i] - d4[i]);
-          }
+          for (int i = 0; i < 4; ++i)
+            if (q0 + mq * 16 + 4 * g + i >= p.len) l4[mq][i] = kInf;
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int nk = 0; nk < NKT; ++nk)
+            s[mq][nk][i] = fexp2(__builtin_fmaf(s[mq][nk][i], c2, -l4[mq][i]));
+        if (q_lo < wk0 + NKT * 16 - 1) {  // block crosses this wave's diagonal
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int nk = 0; nk < NKT; ++nk)
+              if (wk0 + nk * 16 + n > q_lo + mq * 16 + 4 * g + i) s[mq][nk][i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int nk = 0; nk < NKT; ++nk) dp[mq][nk][i] = s[mq][nk][i] * (dp[mq][nk][i] - d4[mq][i]);
       }
 
 #pragma unroll
@@ -720,19 +783,15 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
           dsf[nk] = pack44<T>(dp[2 * kq][nk], dp[2 * kq + 1][nk]);
         }
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const frag bd = ldT8<D>(Dc, kq * 32, md * 16, lane);
-          const frag bq = ldT8<D>(Qc, kq * 32, md * 16, lane);
+        for (int md = 0; md < MD; ++md)
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk) {
-            E::mma(dva[nk][md], pf[nk], bd);
-            E::mma(dka[nk][md], dsf[nk], bq);
+            E::mma(dva[nk][md], pf[nk], dtr[kq][md]);
+            E::mma(dka[nk][md], dsf[nk], qtr[kq][md]);
           }
-        }
       }
     }
-    if (more) stage(cur ^ 1);
-    __syncthreads();
+    drain_and_sync();
   }
 
   float* DKp = p.dk + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
@@ -784,7 +843,7 @@ template <typename T, int D>
 struct Cfg {
   static constexpr int FWD_NQT = 2, FWD_BK = 64, FWD_NW = 4;
   static constexpr int DQ_NQT = 2, DQ_BK = 64, DQ_NW = 4;
-  static constexpr int KV_NKT = 2, KV_BQ = 64, KV_NW = 4;
+  static constexpr int KV_NKT = 2, KV_BQ = 32, KV_NW = 4;
 };
 // float32 storage (the exactness path) takes smaller tiles: its fragments are
 // twice as wide in registers.
@@ -821,19 +880,21 @@ hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v,
 template <typename T, int D>
 hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
-                    float* delta, hipStream_t st) {
+                    float* ws, hipStream_t st) {
   using C = Cfg<T, D>;
   constexpr int LPR = D / Elt<T>::VEC;
   const int rows = s.batch * s.hq * s.len;
   const int threads = rows * LPR;
+  float* delta = ws;
+  float* lse2 = ws + bwd_ws_stride(rows);
   prof_begin(CA_KERNEL_DELTA, st);
   hipLaunchKernelGGL((delta_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0, st, (const T*)o,
-                     (const T*)dout, delta, s.q_cap, s.q_off, s.len, rows);
+                     (const T*)dout, lse, delta, lse2, s.q_cap, s.q_off, s.len, rows);
   prof_end(CA_KERNEL_DELTA, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  BwdParams p{q,        k,       v,     dout,  lse,     delta,   dq,       dk,
-              dv,       s.hq,    s.hkv, s.q_cap, s.kv_cap, s.q_off, s.start, s.len,
+  BwdParams p{q,     k,     v,       dout,     lse,     delta,   lse2,  dq,   dk,
+              dv,    s.hq,  s.hkv,   s.q_cap,  s.kv_cap, s.q_off, s.start, s.len,
               exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs};
   constexpr int BKV = C::KV_NW * C::KV_NKT * 16;
   const int L = s.start + s.len;
@@ -865,13 +926,13 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
 
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
-                      float* delta, hipStream_t st) {
+                      float* ws, hipStream_t st) {
   if (s.dtype == CA_BF16) {
-    return s.head_dim == 128 ? bwd_impl<bf16, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st)
-                             : bwd_impl<bf16, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st);
+    return s.head_dim == 128 ? bwd_impl<bf16, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, st)
+                             : bwd_impl<bf16, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, st);
   }
-  return s.head_dim == 128 ? bwd_impl<float, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st)
-                           : bwd_impl<float, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, delta, st);
+  return s.head_dim == 128 ? bwd_impl<float, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, st)
+                           : bwd_impl<float, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, st);
 }
 
 hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap, int src_cap,

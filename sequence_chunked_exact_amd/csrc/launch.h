@@ -20,11 +20,16 @@ struct Shape {
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* v, void* o,
                       float* lse, hipStream_t st);
 
-// Backward: delta (workspace, batch*hq*len floats) = rowsum(dout * o), then dq
-// (overwritten, times grad_scale) and dk/dv accumulators (incremented).
+// Backward workspace: two float arrays of batch*hq*len rows (row delta and
+// LSE*log2(e)), each starting on a 256-byte boundary.
+inline size_t bwd_ws_stride(size_t rows) { return (rows + 63) / 64 * 64; }
+inline size_t bwd_ws_bytes(size_t rows) { return 2 * bwd_ws_stride(rows) * sizeof(float); }
+
+// Backward: row statistics into the workspace, then dq (overwritten, times
+// grad_scale) and the dk/dv accumulators (incremented).
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, float grad_scale,
-                      float* dq, float* dk, float* dv, float* delta, hipStream_t st);
+                      float* dq, float* dk, float* dv, float* ws, hipStream_t st);
 
 // acc[b][h][r][:] += scale * src[b][h][r][:], r < rows.
 hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap,
