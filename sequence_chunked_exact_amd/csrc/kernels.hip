@@ -202,6 +202,18 @@ __device__ __forceinline__ float sum4(float s) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
+// own L2. This maps the linear id to a logical work index so that every XCD
+// receives one contiguous range of the logical order (heads outermost): the
+// workgroups streaming the same K/V (forward, dQ) or the same Q/dO (dK/dV)
+// then share one L2. Within a range the order is ascending, i.e. each XCD
+// starts with the first (longest) tiles of its heads.
+__device__ __forceinline__ int xcd_order(int id, int n) {
+  constexpr int X = 8;
+  const int per = n / X;
+  return id < per * X ? (id % X) * per + id / X : id;
+}
+
 // Stream rows [row0, row0 + ROWS) of a row-major [*, D] head into a swizzled
 // LDS tile with direct global->LDS loads: each wave instruction fills 64
 // consecutive 16-byte LDS slots, so lane l fetches the global chunk that
@@ -271,8 +283,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int qt = gridDim.x - 1 - blockIdx.x;  // longest rows first
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int nqt = (p.len + BQ - 1) / BQ;
+  const int work_id = xcd_order(blockIdx.x, gridDim.x);
+  const int qt = nqt - 1 - work_id % nqt;  // longest rows first
+  const int h = (work_id / nqt) % p.hq, b = work_id / (nqt * p.hq);
   const int hk = h / (p.hq / p.hkv);
   const T* Q = (const T*)p.q + ((size_t)(b * p.hq + h) * p.q_cap + p.q_off) * D;
   const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
@@ -488,8 +502,10 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int qt = gridDim.x - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int nqt = (p.len + BQ - 1) / BQ;
+  const int work_id = xcd_order(blockIdx.x, gridDim.x);
+  const int qt = nqt - 1 - work_id % nqt;  // longest rows first
+  const int h = (work_id / nqt) % p.hq, b = work_id / (nqt * p.hq);
   const int hk = h / (p.hq / p.hkv);
   const size_t qhead = ((size_t)(b * p.hq + h) * p.q_cap + p.q_off);
   const T* Q = (const T*)p.q + qhead * D;
@@ -646,10 +662,12 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int kt = gridDim.x - 1 - blockIdx.x;  // keys with the most queries first
-  const int hk = blockIdx.y, b = blockIdx.z;
   const int G = p.hq / p.hkv;
   const int L = p.start + p.len;
+  const int nkt = (L + BKV - 1) / BKV;
+  const int work_id = xcd_order(blockIdx.x, gridDim.x);
+  const int kt = nkt - 1 - work_id % nkt;  // keys with the most queries first
+  const int hk = (work_id / nkt) % p.hkv, b = work_id / (nkt * p.hkv);
   const int kb0 = kt * BKV;
   const int wk0 = kb0 + wave * NKT * 16;
   const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
@@ -869,7 +887,7 @@ hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   constexpr int BQ = C::FWD_NW * C::FWD_NQT * 16;
   FwdParams p{q,     k,     v,       o,        lse,     s.hq,    s.hkv, s.q_cap, s.kv_cap, s.q_off,
               s.start, s.len, exp2_coef(s.scale), s.scale < 0.f ? 1 : 0};
-  dim3 grid((s.len + BQ - 1) / BQ, s.hq, s.batch);
+  dim3 grid(((s.len + BQ - 1) / BQ) * s.hq * s.batch);
   prof_begin(CA_KERNEL_FWD, st);
   hipLaunchKernelGGL((fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), grid, dim3(C::FWD_NW * 64), 0,
                      st, p);
@@ -899,14 +917,14 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   constexpr int BKV = C::KV_NW * C::KV_NKT * 16;
   const int L = s.start + s.len;
   prof_begin(CA_KERNEL_DKDV, st);
-  hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NW>), dim3((L + BKV - 1) / BKV, s.hkv, s.batch),
+  hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NW>), dim3(((L + BKV - 1) / BKV) * s.hkv * s.batch),
                      dim3(C::KV_NW * 64), 0, st, p);
   prof_end(CA_KERNEL_DKDV, st);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int BQ = C::DQ_NW * C::DQ_NQT * 16;
   prof_begin(CA_KERNEL_DQ, st);
-  hipLaunchKernelGGL((dq_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW>), dim3((s.len + BQ - 1) / BQ, s.hq, s.batch),
+  hipLaunchKernelGGL((dq_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW>), dim3(((s.len + BQ - 1) / BQ) * s.hq * s.batch),
                      dim3(C::DQ_NW * 64), 0, st, p);
   prof_end(CA_KERNEL_DQ, st);
   return hipGetLastError();
