@@ -49,8 +49,12 @@ def flop_plan(wl, selected):
     }
 
 
-def cpu_baseline(wl, inp_raw):
-    """The float64 oracle on a bounded sample, extrapolated by causal FLOPs."""
+def cpu_baseline(wl, inp_raw, n_heads=8):
+    """The float64 oracle on a bounded sample, extrapolated by causal FLOPs.
+
+    Sample: the full causal forward + backward of the first `n_heads` query
+    heads (each against its kv head) over the whole sequence.
+    """
     import numpy as np
     from oracle import attention as A
     from sequence_chunked_exact_amd import workloads as W
@@ -59,28 +63,29 @@ def cpu_baseline(wl, inp_raw):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    G = wl.n_q_heads // wl.n_kv_heads
 
     def head(name, h):
         a = inp_raw[name][:, h:h + 1]
         return W.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
-    q, k, v, do = head("q", 0), head("k", 0), head("v", 0), head("do", 0)
-    s, c = wl.chunk_bounds(wl.n_chunks - 1)
-    rows = np.arange(s + c - min(c, 512), s + c)
     t0 = time.perf_counter()
-    A.forward(q, k, v, wl.softmax_scale, rows=rows)
-    A.backward(q, k, v, do, wl.softmax_scale, rows=rows)
+    for h in range(n_heads):
+        q, do = head("q", h), head("do", h)
+        k, v = head("k", h // G), head("v", h // G)
+        A.forward(q, k, v, wl.softmax_scale)
+        A.backward(q, k, v, do, wl.softmax_scale)
     dt = time.perf_counter() - t0
-    pairs = int(sum(int(r) + 1 for r in rows))
-    sample_flops = 14 * wl.head_dim * pairs
+    pairs = wl.seq_len * (wl.seq_len + 1) // 2
+    sample_flops = 14 * wl.head_dim * pairs * n_heads
     rate = sample_flops / dt
     plan = flop_plan(wl, None)
     total = plan["fwd"] + plan["bwd"]
     tokens_per_s = wl.seq_len * rate / total
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 oracle forward+backward of query rows [{rows[0]}, {rows[-1] + 1}) of one "
-                      f"query head against its full causal prefix ({pairs} visible pairs, {dt:.1f} s, "
-                      f"{rate / 1e9:.2f} GFLOP/s), extrapolated to the whole workload by causal FLOPs",
+            "sample": f"float64 oracle forward+backward of query heads 0..{n_heads - 1} of "
+                      f"{wl.n_q_heads} over all {wl.seq_len} positions ({dt:.1f} s, "
+                      f"{rate / 1e9:.1f} GFLOP/s), extrapolated to all heads by causal FLOPs",
             "seconds": dt, "gflops": rate / 1e9}
 
 
@@ -157,20 +162,24 @@ def main():
             kernels[name] = {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps,
                              "avg_us": tot / n * 1e3}
     log("[bench] kernels " + json.dumps(kernels))
-    # roofline for the kernel with the most GPU time
+    # roofline for the kernel with the most GPU time; its algorithmic FLOPs are
+    # the products it carries (forward: S, PV = 4d per pair; dK/dV: S, dP, dV,
+    # dK = 8d per pair; dQ: the dQ product, 2d, the rest being recompute)
     dom = max(kernels, key=lambda n_: kernels[n_]["ms_per_step"])
-    dom_flops = {"fwd": plan["fwd"], "dkdv": plan["dkdv"]}.get(dom)
+    dom_flops = {"fwd": plan["fwd"], "dkdv": plan["dkdv"], "dq": plan["bwd"] // 5}.get(dom)
     n_launch, tot_ms = prof[dom]
+    roof = {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": None, "traffic": None}
     if dom_flops is not None:
         per_launch_flops = dom_flops / (n_launch / args.steps)
         avg_s = tot_ms / n_launch * 1e-3
         achieved = per_launch_flops / avg_s / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                "avg_launch_us": avg_s * 1e6, "flops_per_launch": per_launch_flops}
-    else:
-        roof = {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": None, "traffic": None}
+        roof.update({"achieved": achieved, "frac": achieved / PEAK_BF16_TFLOPS,
+                     "avg_launch_us": avg_s * 1e6, "flops_per_launch": per_launch_flops})
+    from sequence_chunked_exact_amd.profile_summary import read_traffic
+    roof["traffic"] = read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{wl.name}.md"))
+    fwd_ms = kernels.get("fwd", {}).get("ms_per_step", 0.0)
+    bwd_ms = sum(kernels.get(k_, {}).get("ms_per_step", 0.0) for k_ in ("delta", "dkdv", "dq", "zero"))
 
     out = {
         "metric": METRIC,
@@ -187,6 +196,8 @@ def main():
         "data": "synthetic",
         "tflops": tflops,
         "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "tflops_fwd": plan["fwd"] / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,
+        "tflops_bwd": plan["bwd"] / (bwd_ms * 1e-3) / 1e12 if bwd_ms else None,
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": T, "chunk": C,
                    "n_chunks": wl.n_chunks, "n_q_heads": wl.n_q_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "softmax_scale": wl.softmax_scale,

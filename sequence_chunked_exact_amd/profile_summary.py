@@ -1,0 +1,132 @@
+"""Turn rocprofv3 CSV output into the short summaries kept under profiles/.
+
+    python -m sequence_chunked_exact_amd.profile_summary copy
+        Calibration workload: a plain 1 GiB device-to-device copy, three times
+        (run it under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE).
+
+    python -m sequence_chunked_exact_amd.profile_summary summarize \\
+        --stats S.csv --fetch F.csv --write W.csv --cal-fetch CF.csv \\
+        --cal-write CW.csv --kernel dkdv --workload 8b_layer --out profiles/X.md \\
+        --commands "..."
+        Writes a markdown summary: per-kernel average durations from the
+        kernel-trace statistics, and for one kernel the FETCH_SIZE/WRITE_SIZE
+        per dispatch scaled by what the same counters read for the copy of
+        known size, plus the SHA-256 of the kernel source it was measured on.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(HERE, "csrc", "kernels.hip")
+COPY_BYTES = 1 << 30
+
+SHORT = {"fwd_kernel": "fwd", "dkdv_kernel": "dkdv", "dq_kernel": "dq", "delta_kernel": "delta",
+         "zero_kernel": "zero", "accumulate_kernel": "accumulate"}
+
+
+def kernel_source_sha256() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def short_name(full: str) -> str:
+    for key, val in SHORT.items():
+        if key in full:
+            return val
+    return full[:40]
+
+
+def per_dispatch(path: str, counter: str, name_filter=None):
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        if name_filter and name_filter not in short_name(r["Kernel_Name"]) and \
+                name_filter not in r["Kernel_Name"]:
+            continue
+        vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def copy_main():
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x3")
+
+
+def summarize_main(args):
+    rows = list(csv.DictReader(open(args.stats)))
+    lines = [f"# rocprofv3 summary: `{args.kernel}` kernel, `{args.workload}` workload", ""]
+    lines += ["Commands (run from the repository root):", "", "```"]
+    lines += [c.strip() for c in args.commands.split(";;") if c.strip()]
+    lines += ["```", "", "## Kernel trace statistics", "",
+              "| kernel | calls | average (us) | total (ms) | share |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
+    out = {}
+    if args.fetch and args.write and args.cal_fetch and args.cal_write:
+        f = per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
+        w = per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+        cf = max(per_dispatch(args.cal_fetch, "FETCH_SIZE"))
+        cw = max(per_dispatch(args.cal_write, "WRITE_SIZE"))
+        kf, kw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+        fetch_b = statistics.mean(f) * 1024 * kf
+        write_b = statistics.mean(w) * 1024 * kw
+        out = {"fetch": fetch_b, "write": write_b}
+        lines += ["", f"## HBM traffic of `{args.kernel}` (per dispatch, mean over {len(f)} dispatches)", "",
+                  f"- copy calibration: a {COPY_BYTES} B copy reads FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE "
+                  f"{cw:.0f} KiB per dispatch; scale factors {kf:.4f} (fetch) and {kw:.4f} (write)",
+                  f"- FETCH_SIZE {statistics.mean(f):.0f} KiB -> {fetch_b / 1e6:.1f} MB",
+                  f"- WRITE_SIZE {statistics.mean(w):.0f} KiB -> {write_b / 1e6:.1f} MB",
+                  "", f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}"]
+    lines += [f"kernel_source_sha256: {kernel_source_sha256()}", ""]
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+    return out
+
+
+def read_traffic(path: str):
+    """traffic_bytes_per_launch from a summary, or None if missing or stale."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for ln in open(path):
+        if ":" in ln and ln.split(":")[0].strip() in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            k, v = ln.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_sha256() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    sub.add_parser("copy")
+    s = sub.add_parser("summarize")
+    for opt in ("--stats", "--fetch", "--write", "--cal-fetch", "--cal-write", "--kernel", "--workload",
+                "--out", "--commands"):
+        s.add_argument(opt, default=None)
+    args = ap.parse_args(argv)
+    if args.cmd == "copy":
+        copy_main()
+    else:
+        summarize_main(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
