@@ -247,6 +247,34 @@ __device__ __forceinline__ void stage_vec64(float* lds, const float* src, int ro
 #endif
 }
 
+// A [ROWS][D] tile staged through registers: thread tid fetches R rows of
+// one 16-byte column vector (rows at or beyond `limit` re-read row limit-1,
+// given zero weight by every consumer, as for stage_tile) and later writes
+// them into a swizzled LDS tile. Plain loads into registers let the next
+// tile's fetch overlap the current tile's math without any LDS ordering.
+template <typename T, int ROWS, int D, int NT>
+struct RegTile {
+  using V = typename Elt<T>::vec;
+  static constexpr int VEC = Elt<T>::VEC;
+  static constexpr int NDV = D / VEC;      // column vectors per row
+  static constexpr int GROUPS = NT / NDV;  // row groups
+  static constexpr int R = ROWS / GROUPS;  // rows per thread
+  static_assert(NT % NDV == 0 && ROWS % GROUPS == 0 && R >= 1, "tile/thread shape");
+  V r[R];
+
+  __device__ __forceinline__ void load(const T* head, int row0, int limit, int tid) {
+    const int dv = tid % NDV, grp = tid / NDV;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      r[i] = *(const V*)(head + (size_t)min(row0 + grp * R + i, limit - 1) * D + dv * VEC);
+  }
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+    const int dv = tid % NDV, grp = tid / NDV;
+#pragma unroll
+    for (int i = 0; i < R; ++i) *(V*)(lds + Lay<T, D>::off(grp * R + i, dv * VEC)) = r[i];
+  }
+};
+
 // Wait for every outstanding memory operation of this wave (including direct
 // global->LDS loads), then synchronize the workgroup.
 __device__ __forceinline__ void drain_and_sync() {
@@ -255,10 +283,15 @@ __device__ __forceinline__ void drain_and_sync() {
 }
 
 // ----------------------------------------------------------------------------
-// Forward. Grid (query tiles, Hq, batch); NW waves, each owning NQT*16 query
-// rows held as B fragments of S^T = K Q^T. Key tiles of BK rows stream through
-// double-buffered LDS. Tiles past a wave's last visible key are skipped; only
-// tiles that cross its diagonal are masked.
+// Forward. 1-D grid over (batch, q head, query tile). A workgroup has two
+// groups of NW waves; wave w of each group owns the same NQT*16 query rows
+// (held as B fragments of S^T = K Q^T), and group 0 takes the even key tiles
+// while group 1 takes the odd ones, so each SIMD runs two waves (one's LDS
+// reads and softmax overlap the other's MFMAs) without more LDS traffic per
+// product. Pairs of key tiles stream through double-buffered LDS, fetched
+// into registers one pair ahead. At the end group 1 hands its running
+// maximum, row sums and O^T to group 0 through LDS, which merges and stores.
+// Tiles past a wave's rows are skipped; only diagonal tiles are masked.
 // ----------------------------------------------------------------------------
 struct FwdParams {
   const void* q;
@@ -272,16 +305,18 @@ struct FwdParams {
 };
 
 template <typename T, int D, int NQT, int BK, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int BQ = NW * NQT * 16;
+  constexpr int NT = 2 * NW * 64, BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
-  __shared__ __attribute__((aligned(16))) T Ks[2][BK * D];
-  __shared__ __attribute__((aligned(16))) T Vs[2][BK * D];
+  // smem[b][0] holds the K tiles 2i (slot 0) and 2i+1 (slot 1) of pair i,
+  // smem[b][1] the V tiles, with b = i & 1.
+  __shared__ __attribute__((aligned(16))) T smem[2][2][2][BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / NW, wq = wave % NW;
   const int n = lane & 15, g = lane >> 4;
   const int nqt = (p.len + BQ - 1) / BQ;
   const int work_id = xcd_order(blockIdx.x, gridDim.x);
@@ -294,14 +329,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int L = p.start + p.len;
   const int r0 = qt * BQ;
   const int n_tiles = (p.start + min(r0 + BQ, p.len) - 1) / BK + 1;
-  const int wr0 = r0 + wave * NQT * 16;
+  const int n_pairs = (n_tiles + 1) / 2;
+  const int wr0 = r0 + wq * NQT * 16;
   const bool active = wr0 < p.len;
   const int wq_lo = p.start + wr0;
   const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
   const float c2 = p.c2;
 
-  stage_tile<T, BK, D, NW>(Ks[0], K, 0, L, wave, lane);
-  stage_tile<T, BK, D, NW>(Vs[0], V, 0, L, wave, lane);
+  // The pair's two K tiles and two V tiles are one [2*BK][D] block each.
+  RegTile<T, 2 * BK, D, NT> kt, vt;
+  kt.load(K, 0, L, tid);
+  vt.load(V, 0, L, tid);
 
   frag qf[NQT][DK];
 #pragma unroll
@@ -322,32 +360,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) oacc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  drain_and_sync();
+  kt.store(&smem[0][0][0][0], tid);
+  vt.store(&smem[0][1][0][0], tid);
+  __syncthreads();
 
-  // Per tile: read every fragment this wave needs from LDS, then start the
-  // next tile's direct-to-LDS loads (so they overlap the math, and no LDS read
-  // of this tile has to wait for them), then compute.
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kb0 = j * BK, cur = j & 1;
-    const bool work = active && kb0 <= wq_hi;
-    frag kfr[DK][MK], vfr[KB2][MD];
-    if (work) {
-      const T* Kc = Ks[cur];
-      const T* Vc = Vs[cur];
-#pragma unroll
-      for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-        for (int mk = 0; mk < MK; ++mk) kfr[kb][mk] = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
-#pragma unroll
-      for (int kb2 = 0; kb2 < KB2; ++kb2)
-#pragma unroll
-        for (int md = 0; md < MD; ++md) vfr[kb2][md] = ldT8<D>(Vc, kb2 * 32, md * 16, lane);
+  for (int i = 0; i < n_pairs; ++i) {
+    const int cur = i & 1;
+    const bool more = i + 1 < n_pairs;
+    if (more) {
+      kt.load(K, (2 * i + 2) * BK, L, tid);
+      vt.load(V, (2 * i + 2) * BK, L, tid);
     }
-    if (j + 1 < n_tiles) {
-      stage_tile<T, BK, D, NW>(Ks[cur ^ 1], K, kb0 + BK, L, wave, lane);
-      stage_tile<T, BK, D, NW>(Vs[cur ^ 1], V, kb0 + BK, L, wave, lane);
-    }
-    if (work) {
+    const int j = 2 * i + grp;  // this group's key tile
+    const int kb0 = j * BK;
+    if (active && j < n_tiles && kb0 <= wq_hi) {
+      const T* Kc = smem[cur][0][grp];
+      const T* Vc = smem[cur][1][grp];
       f32x4 s[MK][NQT];
 #pragma unroll
       for (int mk = 0; mk < MK; ++mk)
@@ -356,9 +384,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
+        for (int mk = 0; mk < MK; ++mk) {
+          const frag a = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
 #pragma unroll
-          for (int nt = 0; nt < NQT; ++nt) E::mma(s[mk][nt], kfr[kb][mk], qf[nt][kb]);
+          for (int nt = 0; nt < NQT; ++nt) E::mma(s[mk][nt], a, qf[nt][kb]);
+        }
 
       if (kb0 + BK - 1 > wq_lo) {  // tile crosses this wave's diagonal
 #pragma unroll
@@ -367,10 +397,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (kb0 + mk * 16 + 4 * g + i > qp) s[mk][nt][i] = -kInf;
+            for (int ii = 0; ii < 4; ++ii)
+              if (kb0 + mk * 16 + 4 * g + ii > qp) s[mk][nt][ii] = -kInf;
         }
       }
+      // Each lane tests its own scores against the running maximum; the exact
+      // 4-lane maximum (a cross-lane move) is only taken when some lane's score
+      // exceeds it by more than 2^8, so the common path has no cross-lane op.
       bool grow = false;
       float mx2[NQT];
 #pragma unroll
@@ -379,49 +412,91 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mk][nt][i]);
-        mx2[nt] = max4(mx) * c2;
+          for (int ii = 0; ii < 4; ++ii) mx = fmaxf(mx, s[mk][nt][ii]);
+        mx2[nt] = mx * c2;
         grow |= mx2[nt] > m2[nt] + kRescale;
       }
       if (__any(grow)) {
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt) {
-          const float mnew = fmaxf(m2[nt], mx2[nt]);
-          const float alpha = fexp2(m2[nt] - mnew);
+          const float mnew = fmaxf(m2[nt], max4(mx2[nt]));
+          const float alpha = mnew == -kInf ? 1.f : fexp2(m2[nt] - mnew);
           m2[nt] = mnew;
           lrun[nt] *= alpha;
 #pragma unroll
           for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;
         }
       }
+      // A row with no visible key yet (possible for group 1) keeps m2 = -inf;
+      // its scores are all -inf, and a finite stand-in keeps exp2 at 0.
+      float mref[NQT];
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e = fexp2(__builtin_fmaf(s[mk][nt][i], c2, -m2[nt]));
-            s[mk][nt][i] = e;
-            lsum += e;
-          }
-        lrun[nt] += lsum;
-      }
+      for (int nt = 0; nt < NQT; ++nt) mref[nt] = fmaxf(m2[nt], -1e30f);
 #pragma unroll
       for (int kb2 = 0; kb2 < KB2; ++kb2) {
         frag pf[NQT];
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) pf[nt] = pack44<T>(s[2 * kb2][nt], s[2 * kb2 + 1][nt]);
+        for (int nt = 0; nt < NQT; ++nt) {
+          float lsum = 0.f;
 #pragma unroll
-        for (int md = 0; md < MD; ++md)
+          for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int nt = 0; nt < NQT; ++nt) E::mma(oacc[md][nt], vfr[kb2][md], pf[nt]);
+            for (int ii = 0; ii < 4; ++ii) {
+              const float e = fexp2(__builtin_fmaf(s[2 * kb2 + hh][nt][ii], c2, -mref[nt]));
+              s[2 * kb2 + hh][nt][ii] = e;
+              lsum += e;
+            }
+          lrun[nt] += lsum;
+          pf[nt] = pack44<T>(s[2 * kb2][nt], s[2 * kb2 + 1][nt]);
+        }
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const frag a = ldT8<D>(Vc, kb2 * 32, md * 16, lane);
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) E::mma(oacc[md][nt], a, pf[nt]);
+        }
       }
     }
-    drain_and_sync();
+    if (more) {
+      kt.store(&smem[cur ^ 1][0][0][0], tid);
+      vt.store(&smem[cur ^ 1][1][0][0], tid);
+    }
+    __syncthreads();
   }
 
-  if (!active) return;
+  // Merge: group 1 publishes (m2, lane-partial row sum, O^T) per lane; the
+  // matching lane of group 0 rescales both to the larger maximum and adds.
+  float* xfer = (float*)&smem[0][0][0][0];
+  constexpr int PER = 2 + MD * 4;  // floats per lane and query tile
+  static_assert(sizeof(smem) >= (size_t)NW * 64 * NQT * PER * sizeof(float), "merge area");
+  if (grp == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      float* x = xfer + ((size_t)(nt * NW + wq) * PER) * 64 + lane;
+      x[0] = m2[nt];
+      x[64] = lrun[nt];
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[(2 + md * 4 + e) * 64] = oacc[md][nt][e];
+    }
+  }
+  __syncthreads();
+  if (grp == 1 || !active) return;
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    const float* x = xfer + ((size_t)(nt * NW + wq) * PER) * 64 + lane;
+    const float mb = x[0];
+    const float mnew = fmaxf(m2[nt], mb);
+    // both maxima are finite for every visible row: tile 0 (group 0) holds key 0
+    const float fa = fexp2(m2[nt] - mnew), fb = mb == -kInf ? 0.f : fexp2(mb - mnew);
+    lrun[nt] = lrun[nt] * fa + x[64] * fb;
+    m2[nt] = mnew;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) oacc[md][nt][e] = oacc[md][nt][e] * fa + x[(2 + md * 4 + e) * 64] * fb;
+  }
   T* O = (T*)p.o + ((size_t)(b * p.hq + h) * p.q_cap + p.q_off) * D;
   float* LSE = p.lse + (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
 #pragma unroll
@@ -889,7 +964,7 @@ hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v,
               s.start, s.len, exp2_coef(s.scale), s.scale < 0.f ? 1 : 0};
   dim3 grid(((s.len + BQ - 1) / BQ) * s.hq * s.batch);
   prof_begin(CA_KERNEL_FWD, st);
-  hipLaunchKernelGGL((fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), grid, dim3(C::FWD_NW * 64), 0,
+  hipLaunchKernelGGL((fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), grid, dim3(2 * C::FWD_NW * 64), 0,
                      st, p);
   prof_end(CA_KERNEL_FWD, st);
   return hipGetLastError();
