@@ -29,9 +29,6 @@ def command(out: str = LIB, extra=()) -> list:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA accumulators in the VGPR form: keeps the accumulator tiles from
-        # bouncing between AGPRs and VGPRs around every product
-        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"),
         *extra,

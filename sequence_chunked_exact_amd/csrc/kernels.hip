@@ -89,24 +89,21 @@ struct Elt<float> {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Row-major [rows][D] LDS tile; the 16-byte chunk c of row r sits at chunk
-// position c ^ swz(r). The map (r mod 16, with bit 3 ^= bit 0 and bit 2 ^=
-// bit 3) was picked by measuring gfx950's LDS bank-conflict counter over a
-// family of candidate maps: with 256-byte rows it is the simplest one under
-// which both access patterns used here run conflict-free, namely a 64-lane
-// read of one 16-byte chunk column from 16 consecutive rows per 16 lanes, and
-// the transposing read of 4-row x 16-column blocks.
+// Row-major [rows][D] LDS tile whose rows are padded by one 16-byte chunk:
+// row r starts at element r * RS, RS = D + 16 / sizeof(T). Every head size
+// here makes the row stride an odd multiple of 4 banks (mod 64), so the
+// 16 consecutive rows of one access start 4 banks apart in 16 different
+// positions. Both read patterns used here are then conflict-free: 16 lanes
+// reading one 16-byte chunk column from 16 consecutive rows (row-major
+// fragments), and the transposing read of 16 rows x 32 bytes, which lands
+// on every bank exactly twice (its minimum, 512 bytes in two passes). A
+// lane's address is a loop-invariant base plus a constant offset.
 template <typename T, int D>
 struct Lay {
-  static constexpr int EPC = 16 / sizeof(T);  // elements per chunk
-  static constexpr int CH = D / EPC;          // chunks per row
-  static __device__ __forceinline__ int swz(int r) {
-    const int x = (r ^ ((r & 1) << 3) ^ (((r >> 3) & 1) << 2)) & 15;
-    return x & (CH - 1);
-  }
-  static __device__ __forceinline__ int off(int r, int c) {
-    return r * D + (((c / EPC) ^ swz(r)) * EPC) + (c % EPC);
-  }
+  static constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  static constexpr int RS = D + 2 * EPC;      // row stride in elements
+  static_assert(((RS * sizeof(T) / 4 / 8) & 1) == 1, "row stride must be an odd multiple of 8 banks");
+  static __device__ __forceinline__ int off(int r, int c) { return r * RS + c; }
 };
 
 // 8 consecutive elements of row r from column c (c % 8 == 0), contiguous order.
@@ -200,8 +197,6 @@ __device__ __forceinline__ float sum4(float s) {
   return s + __shfl_xor(s, 32);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 // Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
 // own L2. This maps the linear id to a logical work index so that every XCD
 // receives one contiguous range of the logical order (heads outermost): the
@@ -214,73 +209,45 @@ __device__ __forceinline__ int xcd_order(int id, int n) {
   return id < per * X ? (id % X) * per + id / X : id;
 }
 
-// Stream rows [row0, row0 + ROWS) of a row-major [*, D] head into a swizzled
-// LDS tile with direct global->LDS loads: each wave instruction fills 64
-// consecutive 16-byte LDS slots, so lane l fetches the global chunk that
-// belongs in its slot (the swizzle is applied on the global side, and each
-// instruction still reads whole rows). Rows at or beyond `limit` (>= 1)
-// re-read row limit-1; every consumer gives such rows zero weight (keys past
-// the prefix are causally masked, query rows past the chunk get LSE = +inf).
-template <typename T, int ROWS, int D, int NW>
-__device__ __forceinline__ void stage_tile(T* lds, const T* head, int row0, int limit, int wave, int lane) {
-  using Lt = Lay<T, D>;
-  constexpr int CH = Lt::CH, RPI = 64 / CH, PER_WAVE = ROWS / NW;
-  static_assert(CH <= 64 && PER_WAVE % RPI == 0, "tile rows per wave must fill whole instructions");
-#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-loading builtin exists only in the device pass
-  const int rl = lane / CH, slot = lane % CH;
-#pragma unroll
-  for (int i = 0; i < PER_WAVE / RPI; ++i) {
-    const int rb = wave * PER_WAVE + i * RPI;  // wave-uniform first row of this instruction
-    const int r = rb + rl;
-    const int c = slot ^ Lt::swz(r);
-    const T* src = head + (size_t)min(row0 + r, limit - 1) * D + c * Lt::EPC;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + rb * D), 16, 0, 0);
-  }
-#endif
-}
-
-// 64 consecutive floats starting at row0 (rows clamped to limit-1) into LDS,
-// 4 bytes per lane of one wave.
-__device__ __forceinline__ void stage_vec64(float* lds, const float* src, int row0, int limit, int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src + min(row0 + lane, limit - 1), (lds_void*)lds, 4, 0, 0);
-#endif
-}
-
 // A [ROWS][D] tile staged through registers: thread tid fetches R rows of
-// one 16-byte column vector (rows at or beyond `limit` re-read row limit-1,
-// given zero weight by every consumer, as for stage_tile) and later writes
-// them into a swizzled LDS tile. Plain loads into registers let the next
-// tile's fetch overlap the current tile's math without any LDS ordering.
+// one 16-byte column vector and later writes them into a swizzled LDS tile
+// (threads beyond the tile's ROWS * D / VEC vectors fetch a duplicate and
+// store nothing). Rows at or beyond `limit` (>= 1) re-read row limit-1;
+// every consumer gives such rows zero weight (keys past the prefix are
+// causally masked, query rows past the chunk get LSE = +inf). Plain loads
+// into registers let the next tile's fetch overlap the current tile's math
+// without any LDS ordering.
 template <typename T, int ROWS, int D, int NT>
 struct RegTile {
   using V = typename Elt<T>::vec;
   static constexpr int VEC = Elt<T>::VEC;
   static constexpr int NDV = D / VEC;      // column vectors per row
   static constexpr int GROUPS = NT / NDV;  // row groups
-  static constexpr int R = ROWS / GROUPS;  // rows per thread
-  static_assert(NT % NDV == 0 && ROWS % GROUPS == 0 && R >= 1, "tile/thread shape");
+  static constexpr bool SPARE = GROUPS > ROWS;
+  static constexpr int R = SPARE ? 1 : ROWS / GROUPS;  // rows per thread
+  static_assert(NT % NDV == 0 && (SPARE || ROWS % GROUPS == 0), "tile/thread shape");
   V r[R];
 
   __device__ __forceinline__ void load(const T* head, int row0, int limit, int tid) {
-    const int dv = tid % NDV, grp = tid / NDV;
+    const int dv = tid % NDV, grp = SPARE ? min(tid / NDV, ROWS - 1) : tid / NDV;
 #pragma unroll
     for (int i = 0; i < R; ++i)
       r[i] = *(const V*)(head + (size_t)min(row0 + grp * R + i, limit - 1) * D + dv * VEC);
   }
   __device__ __forceinline__ void store(T* lds, int tid) const {
     const int dv = tid % NDV, grp = tid / NDV;
+    if (SPARE && grp >= ROWS) return;
 #pragma unroll
     for (int i = 0; i < R; ++i) *(V*)(lds + Lay<T, D>::off(grp * R + i, dv * VEC)) = r[i];
   }
 };
 
-// Wait for every outstanding memory operation of this wave (including direct
-// global->LDS loads), then synchronize the workgroup.
-__device__ __forceinline__ void drain_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-}
+// Wait for every load this wave has in flight. Called once before a main
+// loop: wait counting in the compiler cannot tell the first iteration from
+// the others, so a register loaded before the loop and first read inside it
+// would otherwise wait, in every iteration, on the in-order load counter for
+// the next tile's prefetch as well.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ----------------------------------------------------------------------------
 // Forward. 1-D grid over (batch, q head, query tile). A workgroup has two
@@ -312,7 +279,7 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
   // smem[b][0] holds the K tiles 2i (slot 0) and 2i+1 (slot 1) of pair i,
   // smem[b][1] the V tiles, with b = i & 1.
-  __shared__ __attribute__((aligned(16))) T smem[2][2][2][BK * D];
+  __shared__ __attribute__((aligned(16))) T smem[2][2][2][BK * Lay<T, D>::RS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -362,6 +329,7 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   }
   kt.store(&smem[0][0][0][0], tid);
   vt.store(&smem[0][1][0][0], tid);
+  wait_loads();
   __syncthreads();
 
   for (int i = 0; i < n_pairs; ++i) {
@@ -562,20 +530,22 @@ struct BwdParams {
   float dv_scale;  // grad_scale
 };
 
-// dQ pass. Same walk as the forward: S^T = K Q^T and dP^T = V dO^T with K, V
-// row-major from LDS, P from the stored LSE, and dQ^T += K^T dS^T with K read
-// through the transposing LDS path.
+// dQ pass. Same walk and split as the forward: two groups of NW waves own the
+// same query rows and take the even / odd key tiles; per tile S^T = K Q^T and
+// dP^T = V dO^T with K, V read row-major from LDS, P from the stored LSE, and
+// dQ^T += K^T dS^T with K read through the transposing path. Group 1 hands
+// its partial dQ to group 0 through LDS at the end.
 template <typename T, int D, int NQT, int BK, int NW>
-__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int BQ = NW * NQT * 16;
-  constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
-  __shared__ __attribute__((aligned(16))) T Ks[2][BK * D];
-  __shared__ __attribute__((aligned(16))) T Vs[2][BK * D];
+  constexpr int NT = 2 * NW * 64, BQ = NW * NQT * 16;
+  constexpr int DK = D / 32, MD = D / 16, KB2 = BK / 32;
+  __shared__ __attribute__((aligned(16))) T smem[2][2][2][BK * Lay<T, D>::RS];  // [buffer][K|V][tile of pair]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / NW, wq = wave % NW;
   const int n = lane & 15, g = lane >> 4;
   const int nqt = (p.len + BQ - 1) / BQ;
   const int work_id = xcd_order(blockIdx.x, gridDim.x);
@@ -592,14 +562,16 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   const int L = p.start + p.len;
   const int r0 = qt * BQ;
   const int n_tiles = (p.start + min(r0 + BQ, p.len) - 1) / BK + 1;
-  const int wr0 = r0 + wave * NQT * 16;
+  const int n_pairs = (n_tiles + 1) / 2;
+  const int wr0 = r0 + wq * NQT * 16;
   const bool active = wr0 < p.len;
   const int wq_lo = p.start + wr0;
   const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
   const float c2 = p.c2;
 
-  stage_tile<T, BK, D, NW>(Ks[0], K, 0, L, wave, lane);
-  stage_tile<T, BK, D, NW>(Vs[0], V, 0, L, wave, lane);
+  RegTile<T, 2 * BK, D, NT> kt, vt;
+  kt.load(K, 0, L, tid);
+  vt.load(V, 0, L, tid);
 
   frag qf[NQT][DK], df[NQT][DK];
   float lse2[NQT], dl[NQT];
@@ -621,288 +593,341 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdParams p) {
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  drain_and_sync();
+  kt.store(&smem[0][0][0][0], tid);
+  vt.store(&smem[0][1][0][0], tid);
+  wait_loads();
+  __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kb0 = j * BK, cur = j & 1;
-    const bool work = active && kb0 <= wq_hi;
-    frag kfr[DK][MK], vfr[DK][MK], ktr[KB2][MD];
-    if (work) {  // all LDS reads of this tile before the next tile's loads start
-      const T* Kc = Ks[cur];
-      const T* Vc = Vs[cur];
-#pragma unroll
-      for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-        for (int mk = 0; mk < MK; ++mk) {
-          kfr[kb][mk] = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
-          vfr[kb][mk] = ld8s<D>(Vc, mk * 16 + n, kb * 32 + 8 * g);
-        }
-#pragma unroll
-      for (int kb2 = 0; kb2 < KB2; ++kb2)
-#pragma unroll
-        for (int md = 0; md < MD; ++md) ktr[kb2][md] = ldT8<D>(Kc, kb2 * 32, md * 16, lane);
+  for (int i = 0; i < n_pairs; ++i) {
+    const int cur = i & 1;
+    const bool more = i + 1 < n_pairs;
+    if (more) {
+      kt.load(K, (2 * i + 2) * BK, L, tid);
+      vt.load(V, (2 * i + 2) * BK, L, tid);
     }
-    if (j + 1 < n_tiles) {
-      stage_tile<T, BK, D, NW>(Ks[cur ^ 1], K, kb0 + BK, L, wave, lane);
-      stage_tile<T, BK, D, NW>(Vs[cur ^ 1], V, kb0 + BK, L, wave, lane);
-    }
-    if (work) {
-      f32x4 s[MK][NQT], dp[MK][NQT];
+    const int j = 2 * i + grp;  // this group's key tile
+    const int kb0 = j * BK;
+    if (active && j < n_tiles && kb0 <= wq_hi) {
+      const T* Kc = smem[cur][0][grp];
+      const T* Vc = smem[cur][1][grp];
+      const bool diag = kb0 + BK - 1 > wq_lo;  // tile crosses this wave's diagonal
+      // One 32-key half at a time keeps only half the tile's S and dP live.
 #pragma unroll
-      for (int mk = 0; mk < MK; ++mk)
+      for (int kb2 = 0; kb2 < KB2; ++kb2) {
+        f32x4 s[2][NQT], dp[2][NQT];
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-          s[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[mk][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-      for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int nt = 0; nt < NQT; ++nt) {
-            E::mma(s[mk][nt], kfr[kb][mk], qf[nt][kb]);
-            E::mma(dp[mk][nt], vfr[kb][mk], df[nt][kb]);
+            s[hh][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[hh][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-
 #pragma unroll
-      for (int nt = 0; nt < NQT; ++nt)
+        for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
+          for (int hh = 0; hh < 2; ++hh) {
+            const int mk = 2 * kb2 + hh;
+            const frag ak = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
+            const frag av = ld8s<D>(Vc, mk * 16 + n, kb * 32 + 8 * g);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[mk][nt][i] = fexp2(__builtin_fmaf(s[mk][nt][i], c2, -lse2[nt]));
-      if (kb0 + BK - 1 > wq_lo) {  // tile crosses this wave's diagonal
+            for (int nt = 0; nt < NQT; ++nt) {
+              E::mma(s[hh][nt], ak, qf[nt][kb]);
+              E::mma(dp[hh][nt], av, df[nt][kb]);
+            }
+          }
+        frag dsf[NQT];
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt) {
           const int qp = wq_lo + nt * 16 + n;
 #pragma unroll
-          for (int mk = 0; mk < MK; ++mk)
+          for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (kb0 + mk * 16 + 4 * g + i > qp) s[mk][nt][i] = 0.f;
+            for (int ii = 0; ii < 4; ++ii) {
+              float pv = fexp2(__builtin_fmaf(s[hh][nt][ii], c2, -lse2[nt]));
+              if (diag && kb0 + (2 * kb2 + hh) * 16 + 4 * g + ii > qp) pv = 0.f;
+              dp[hh][nt][ii] = pv * (dp[hh][nt][ii] - dl[nt]);
+            }
+          dsf[nt] = pack44<T>(dp[0][nt], dp[1][nt]);
+        }
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const frag a = ldT8<D>(Kc, kb2 * 32, md * 16, lane);
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], a, dsf[nt]);
         }
       }
-#pragma unroll
-      for (int nt = 0; nt < NQT; ++nt)
-#pragma unroll
-        for (int mk = 0; mk < MK; ++mk)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dp[mk][nt][i] = s[mk][nt][i] * (dp[mk][nt][i] - dl[nt]);
-
-#pragma unroll
-      for (int kb2 = 0; kb2 < KB2; ++kb2) {
-        frag dsf[NQT];
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) dsf[nt] = pack44<T>(dp[2 * kb2][nt], dp[2 * kb2 + 1][nt]);
-#pragma unroll
-        for (int md = 0; md < MD; ++md)
-#pragma unroll
-          for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], ktr[kb2][md], dsf[nt]);
-      }
     }
-    drain_and_sync();
+    if (more) {
+      kt.store(&smem[cur ^ 1][0][0][0], tid);
+      vt.store(&smem[cur ^ 1][1][0][0], tid);
+    }
+    __syncthreads();
   }
 
-  if (!active) return;
+  // Merge: group 1 publishes its partial dQ^T per lane, group 0 adds it.
+  float* xfer = (float*)&smem[0][0][0][0];
+  constexpr int PER = MD * 4;
+  static_assert(sizeof(smem) >= (size_t)NW * 64 * NQT * PER * sizeof(float), "merge area");
+  if (grp == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      float* x = xfer + ((size_t)(nt * NW + wq) * PER) * 64 + lane;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[(md * 4 + e) * 64] = acc[md][nt][e];
+    }
+  }
+  __syncthreads();
+  if (grp == 1 || !active) return;
   float* DQ = p.dq + qhead * D;
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
+    const float* x = xfer + ((size_t)(nt * NW + wq) * PER) * 64 + lane;
     const int row = wr0 + nt * 16 + n;
-    if (row < p.len) {
 #pragma unroll
-      for (int md = 0; md < MD; ++md)
-        *(f32x4*)(DQ + (size_t)row * D + md * 16 + 4 * g) = acc[md][nt] * p.dq_scale;
+    for (int md = 0; md < MD; ++md) {
+      f32x4 v = acc[md][nt];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += x[(md * 4 + e) * 64];
+      if (row < p.len) *(f32x4*)(DQ + (size_t)row * D + md * 16 + 4 * g) = v * p.dq_scale;
     }
   }
 }
 
-// dK/dV pass. Grid (key tiles of NW*NKT*16 rows, Hkv, batch); each wave keeps
-// its NKT*16 keys' K and V fragments and dK, dV sums in registers and walks
-// every (q head of the group, query tile) that can see them. Query tiles are
-// staged once in LDS: read row-major as the A operand of S = Q K^T and
-// dP = dO V^T, and through the transposing path as the B operand of
-// dK = dS^T Q and dV = P^T dO.
-template <typename T, int D, int NKT, int BQ, int NW>
-__global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdParams p) {
+// dK/dV pass. Grid (key tiles of NP*NKT*16 rows, Hkv, batch); NP pairs of
+// waves, each pair owning NKT*16 keys, walk every (q head of the group,
+// query tile) block that can see them. Wave w < NP of a pair holds the keys'
+// K fragments and dV sums: S = Q K^T, P = exp(S - LSE) (causally masked),
+// dV += P^T dO, and P goes to LDS. Its partner, wave NP + w, holds the V
+// fragments and dK sums and runs one block behind: dP = dO V^T,
+// dS = P (dP - delta) with that P, dK += dS^T Q. Each wave then does two of
+// the four products per block and fits in half the register file, so the two
+// waves of a pair share a SIMD and overlap each other's LDS reads and
+// exponentials with their products. Q and dO blocks go through three LDS
+// buffers (the P/dV waves read block it, the dS/dK waves block it-1, the
+// loads fill block it+1), read row-major as the A operand of S and dP and
+// through the transposing path as the B operand of dV and dK.
+template <typename T, int D, int NKT, int BQ, int NP>
+__global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int BKV = NW * NKT * 16;
+  constexpr int NT = 2 * NP * 64, BKV = NP * NKT * 16, NB = 3;
   constexpr int DK = D / 32, MD = D / 16, MQ = BQ / 16, KQ = BQ / 32;
-  static_assert(BQ <= 64, "row statistics are staged 64 rows per wave instruction");
-  __shared__ __attribute__((aligned(16))) T Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) T Ds[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][64];
-  __shared__ __attribute__((aligned(16))) float dl_s[2][64];
+  static_assert(2 * BQ <= NT, "row statistics: one value per thread");
+  __shared__ __attribute__((aligned(16))) T Qs[NB][BQ * Lay<T, D>::RS];
+  __shared__ __attribute__((aligned(16))) T Ds[NB][BQ * Lay<T, D>::RS];
+  // per buffer: LSE*log2(e) of the block's rows in [0, BQ), delta in [BQ, 2BQ)
+  __shared__ __attribute__((aligned(16))) float stat_s[NB][2 * BQ];
+  // P of a pair's block, as the lanes hold it: [block parity][pair][mq][nk][lane]
+  __shared__ f32x4 Ps[2][NP][MQ][NKT][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pv_wave = wave < NP;  // P/dV role; otherwise dS/dK
+  const int pair = pv_wave ? wave : wave - NP;
   const int n = lane & 15, g = lane >> 4;
   const int G = p.hq / p.hkv;
   const int L = p.start + p.len;
   const int nkt = (L + BKV - 1) / BKV;
   const int work_id = xcd_order(blockIdx.x, gridDim.x);
-  const int kt = nkt - 1 - work_id % nkt;  // keys with the most queries first
+  const int kt = work_id % nkt;  // ascending: the first key tiles see the most queries
   const int hk = (work_id / nkt) % p.hkv, b = work_id / (nkt * p.hkv);
   const int kb0 = kt * BKV;
-  const int wk0 = kb0 + wave * NKT * 16;
-  const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
-  const T* V = (const T*)p.v + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const int wk0 = kb0 + pair * NKT * 16;
   const float c2 = p.c2;
 
   // Query rows that can see key kb0: chunk rows r with start + r >= kb0.
   const int qt0 = max(0, kb0 - p.start) / BQ;
-  const int nq = (p.len + BQ - 1) / BQ - qt0;
-  const int iters = G * nq;
+  const int qt_end = (p.len + BQ - 1) / BQ;
+  const int iters = G * (qt_end - qt0);
 
-  auto stage = [&](int it, int buf) {
-    const int h = hk * G + it / nq, q0 = (qt0 + it % nq) * BQ;
-    const size_t qhead = (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
-    const size_t rhead = (size_t)(b * p.hq + h) * p.len;
-    stage_tile<T, BQ, D, NW>(Qs[buf], (const T*)p.q + qhead * D, q0, p.len, wave, lane);
-    stage_tile<T, BQ, D, NW>(Ds[buf], (const T*)p.dout + qhead * D, q0, p.len, wave, lane);
-    if (wave == 0) stage_vec64(lse_s[buf], p.lse2 + rhead, q0, p.len, lane);
-    if (wave == 1 % NW) stage_vec64(dl_s[buf], p.delta + rhead, q0, p.len, lane);
+  // Next block to fetch, walked q tile fastest then q head.
+  int f_qt = qt0, f_h = hk * G;
+  RegTile<T, BQ, D, NT> qreg, dreg;
+  float stat;
+  bool past;  // this thread's LSE row lies past the chunk: zero weight
+  auto fetch = [&]() {
+    const int q0 = f_qt * BQ;
+    const size_t qhead = (size_t)(b * p.hq + f_h) * p.q_cap + p.q_off;
+    const size_t rhead = (size_t)(b * p.hq + f_h) * p.len;
+    qreg.load((const T*)p.q + qhead * D, q0, p.len, tid);
+    dreg.load((const T*)p.dout + qhead * D, q0, p.len, tid);
+    const int r = q0 + tid % BQ;
+    stat = (tid < BQ ? p.lse2 : p.delta)[rhead + min(r, p.len - 1)];
+    past = tid < BQ && r >= p.len;
+    if (++f_qt == qt_end) {
+      f_qt = qt0;
+      ++f_h;
+    }
   };
-  if (iters > 0) stage(0, 0);
+  // (The +inf substitution waits until here so that the fetch never waits
+  // on its own loads.)
+  auto publish = [&](int buf) {
+    qreg.store(Qs[buf], tid);
+    dreg.store(Ds[buf], tid);
+    if (tid < 2 * BQ) stat_s[buf][tid] = past ? kInf : stat;
+  };
 
-  frag kf[NKT][DK], vf[NKT][DK];
+  // K (P/dV waves, negated for a negative scale) or V (dS/dK waves) rows of
+  // this pair's keys as B fragments; keys past the prefix re-read key L-1.
+  frag kv[NKT][DK];
+  {
+    const T* src = (const T*)(pv_wave ? p.k : p.v) + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
 #pragma unroll
-  for (int nk = 0; nk < NKT; ++nk) {
-    const int key = min(wk0 + nk * 16 + n, L - 1);
+    for (int nk = 0; nk < NKT; ++nk) {
+      const int key = min(wk0 + nk * 16 + n, L - 1);
 #pragma unroll
-    for (int kb = 0; kb < DK; ++kb) {
-      kf[nk][kb] = ldg8(K + (size_t)key * D + kb * 32 + 8 * g);
-      if (p.neg) kf[nk][kb] = negate<T>(kf[nk][kb]);
-      vf[nk][kb] = ldg8(V + (size_t)key * D + kb * 32 + 8 * g);
+      for (int kb = 0; kb < DK; ++kb) {
+        kv[nk][kb] = ldg8(src + (size_t)key * D + kb * 32 + 8 * g);
+        if (pv_wave && p.neg) kv[nk][kb] = negate<T>(kv[nk][kb]);
+      }
     }
   }
-  f32x4 dka[NKT][MD], dva[NKT][MD];
+  f32x4 acc[NKT][MD];  // dV (P/dV waves) or dK (dS/dK waves)
 #pragma unroll
   for (int nk = 0; nk < NKT; ++nk)
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      dka[nk][md] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dva[nk][md] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  drain_and_sync();
+    for (int md = 0; md < MD; ++md) acc[nk][md] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = 0; it < iters; ++it) {
-    const int cur = it & 1;
-    const int q0 = (qt0 + it % nq) * BQ;
-    const int q_lo = p.start + q0;
-    const int q_hi = p.start + min(q0 + BQ, p.len) - 1;
-    const bool work = wk0 < L && wk0 <= q_hi;
-    // Row-major fragments -> S and dP; then the transposing reads and the row
-    // statistics; only then the next tile's direct-to-LDS loads, which overlap
-    // the exponentials and the dV / dK products.
-    f32x4 s[MQ][NKT], dp[MQ][NKT];
-    frag qtr[KQ][MD], dtr[KQ][MD];
-    f32x4 l4[MQ], d4[MQ];
-    if (work) {
-      const T* Qc = Qs[cur];
-      const T* Dc = Ds[cur];
-      frag qfr[DK][MQ], dfr[DK][MQ];
-#pragma unroll
-      for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-        for (int mq = 0; mq < MQ; ++mq) {
-          qfr[kb][mq] = ld8s<D>(Qc, mq * 16 + n, kb * 32 + 8 * g);
-          dfr[kb][mq] = ld8s<D>(Dc, mq * 16 + n, kb * 32 + 8 * g);
-        }
-#pragma unroll
-      for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-        for (int nk = 0; nk < NKT; ++nk) {
-          s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
-          dp[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-      for (int kb = 0; kb < DK; ++kb)
+  fetch();
+  publish(0);
+  wait_loads();
+  __syncthreads();
+
+  // q_lo: position of the first row of block `it` (rows advance q tile first).
+  int a_qt = qt0;  // q tile of the block the P/dV waves take next
+  for (int it = 0; it <= iters; ++it) {
+    const bool more = it + 1 < iters;
+    if (more) fetch();
+    if (pv_wave) {
+      const int q0 = a_qt * BQ;
+      const int q_lo = p.start + q0, q_hi = p.start + min(q0 + BQ, p.len) - 1;
+      if (++a_qt == qt_end) a_qt = qt0;
+      if (it < iters && wk0 <= q_hi) {
+        const int cur = it % NB;
+        const T* Qc = Qs[cur];
+        f32x4 s[MQ][NKT];
 #pragma unroll
         for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) {
-            E::mma(s[mq][nk], qfr[kb][mq], kf[nk][kb]);
-            E::mma(dp[mq][nk], dfr[kb][mq], vf[nk][kb]);
+          for (int nk = 0; nk < NKT; ++nk) s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+          for (int mq = 0; mq < MQ; ++mq) {
+            const frag qa = ld8s<D>(Qc, mq * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+            for (int nk = 0; nk < NKT; ++nk) E::mma(s[mq][nk], qa, kv[nk][kb]);
           }
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq)
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          dtr[kq][md] = ldT8<D>(Dc, kq * 32, md * 16, lane);
-          qtr[kq][md] = ldT8<D>(Qc, kq * 32, md * 16, lane);
-        }
-#pragma unroll
-      for (int mq = 0; mq < MQ; ++mq) {
-        l4[mq] = *(const f32x4*)&lse_s[cur][mq * 16 + 4 * g];
-        d4[mq] = *(const f32x4*)&dl_s[cur][mq * 16 + 4 * g];
-      }
-    }
-    if (it + 1 < iters) stage(it + 1, cur ^ 1);
-
-    if (work) {
-      const bool tail = q0 + BQ > p.len;
-#pragma unroll
-      for (int mq = 0; mq < MQ; ++mq) {
-        if (tail) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (q0 + mq * 16 + 4 * g + i >= p.len) l4[mq][i] = kInf;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int mq = 0; mq < MQ; ++mq) {
+          const f32x4 l4 = *(const f32x4*)&stat_s[cur][mq * 16 + 4 * g];
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk)
-            s[mq][nk][i] = fexp2(__builtin_fmaf(s[mq][nk][i], c2, -l4[mq][i]));
-        if (q_lo < wk0 + NKT * 16 - 1) {  // block crosses this wave's diagonal
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) s[mq][nk][i] = fexp2(__builtin_fmaf(s[mq][nk][i], c2, -l4[i]));
+        }
+        if (q_lo < wk0 + NKT * 16 - 1) {  // block crosses this pair's diagonal
+#pragma unroll
+          for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
             for (int nk = 0; nk < NKT; ++nk)
-              if (wk0 + nk * 16 + n > q_lo + mq * 16 + 4 * g + i) s[mq][nk][i] = 0.f;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (wk0 + nk * 16 + n > q_lo + mq * 16 + 4 * g + i) s[mq][nk][i] = 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) dp[mq][nk][i] = s[mq][nk][i] * (dp[mq][nk][i] - d4[mq][i]);
+          for (int nk = 0; nk < NKT; ++nk) Ps[it & 1][pair][mq][nk][lane] = s[mq][nk];
+        const T* Dc = Ds[cur];
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) {
+          frag pf[NKT];
+#pragma unroll
+          for (int nk = 0; nk < NKT; ++nk) pf[nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
+#pragma unroll
+          for (int md = 0; md < MD; ++md) {
+            const frag dtr = ldT8<D>(Dc, kq * 32, md * 16, lane);
+#pragma unroll
+            for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], pf[nk], dtr);
+          }
+        }
       }
-
+    } else if (it >= 1) {  // block it - 1
+      const int q0 = a_qt * BQ;
+      const int q_hi = p.start + min(q0 + BQ, p.len) - 1;
+      if (++a_qt == qt_end) a_qt = qt0;
+      if (wk0 <= q_hi) {
+        const int prv = (it + NB - 1) % NB;
+        const T* Dc = Ds[prv];
+        f32x4 dp[MQ][NKT];
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq) {
-        frag pf[NKT], dsf[NKT];
+        for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
-        for (int nk = 0; nk < NKT; ++nk) {
-          pf[nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
-          dsf[nk] = pack44<T>(dp[2 * kq][nk], dp[2 * kq + 1][nk]);
-        }
+          for (int nk = 0; nk < NKT; ++nk) dp[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int md = 0; md < MD; ++md)
+        for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+          for (int mq = 0; mq < MQ; ++mq) {
+            const frag da = ld8s<D>(Dc, mq * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+            for (int nk = 0; nk < NKT; ++nk) E::mma(dp[mq][nk], da, kv[nk][kb]);
+          }
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq) {
+          const f32x4 d4 = *(const f32x4*)&stat_s[prv][BQ + mq * 16 + 4 * g];
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk) {
-            E::mma(dva[nk][md], pf[nk], dtr[kq][md]);
-            E::mma(dka[nk][md], dsf[nk], qtr[kq][md]);
+            const f32x4 pv = Ps[(it - 1) & 1][pair][mq][nk][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dp[mq][nk][i] = pv[i] * (dp[mq][nk][i] - d4[i]);
           }
+        }
+        const T* Qc = Qs[prv];
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) {
+          frag dsf[NKT];
+#pragma unroll
+          for (int nk = 0; nk < NKT; ++nk) dsf[nk] = pack44<T>(dp[2 * kq][nk], dp[2 * kq + 1][nk]);
+#pragma unroll
+          for (int md = 0; md < MD; ++md) {
+            const frag qtr = ldT8<D>(Qc, kq * 32, md * 16, lane);
+#pragma unroll
+            for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], dsf[nk], qtr);
+          }
+        }
       }
     }
-    drain_and_sync();
+    // Buffer (it + 1) % NB last served block it - 2, whose dS/dK pass ended
+    // before the previous barrier.
+    if (more) publish((it + 1) % NB);
+    __syncthreads();
   }
 
-  float* DKp = p.dk + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
-  float* DVp = p.dv + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  // Read-modify-write of the fp32 accumulator, 16 keys at a time: all reads
+  // are issued before any write.
+  float* dst = (pv_wave ? p.dv : p.dk) + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const float scale = pv_wave ? p.dv_scale : p.dk_scale;
 #pragma unroll
-  for (int nk = 0; nk < NKT; ++nk)
+  for (int nk = 0; nk < NKT; ++nk) {
+    f32x4 old[MD];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = min(wk0 + nk * 16 + 4 * g + i, L - 1);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) old[md][i] = dst[(size_t)key * D + md * 16 + n];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = wk0 + nk * 16 + 4 * g + i;
       if (key < L) {
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const size_t idx = (size_t)key * D + md * 16 + n;
-          DKp[idx] += p.dk_scale * dka[nk][md][i];
-          DVp[idx] += p.dv_scale * dva[nk][md][i];
-        }
+        for (int md = 0; md < MD; ++md) dst[(size_t)key * D + md * 16 + n] = old[md][i] + scale * acc[nk][md][i];
       }
     }
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -936,7 +961,7 @@ template <typename T, int D>
 struct Cfg {
   static constexpr int FWD_NQT = 2, FWD_BK = 64, FWD_NW = 4;
   static constexpr int DQ_NQT = 2, DQ_BK = 64, DQ_NW = 4;
-  static constexpr int KV_NKT = 2, KV_BQ = 32, KV_NW = 4;
+  static constexpr int KV_NKT = 2, KV_BQ = 32, KV_NP = 4;
 };
 // float32 storage (the exactness path) takes smaller tiles: its fragments are
 // twice as wide in registers.
@@ -944,7 +969,7 @@ template <int D>
 struct Cfg<float, D> {
   static constexpr int FWD_NQT = 1, FWD_BK = 32, FWD_NW = 4;
   static constexpr int DQ_NQT = 1, DQ_BK = 32, DQ_NW = 4;
-  static constexpr int KV_NKT = 1, KV_BQ = 32, KV_NW = 4;
+  static constexpr int KV_NKT = 1, KV_BQ = 32, KV_NP = 4;
 };
 
 // |scale| * log2(e), kept strictly positive so that a masked score of -inf
@@ -989,18 +1014,18 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   BwdParams p{q,     k,     v,       dout,     lse,     delta,   lse2,  dq,   dk,
               dv,    s.hq,  s.hkv,   s.q_cap,  s.kv_cap, s.q_off, s.start, s.len,
               exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs};
-  constexpr int BKV = C::KV_NW * C::KV_NKT * 16;
+  constexpr int BKV = C::KV_NP * C::KV_NKT * 16;
   const int L = s.start + s.len;
   prof_begin(CA_KERNEL_DKDV, st);
-  hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NW>), dim3(((L + BKV - 1) / BKV) * s.hkv * s.batch),
-                     dim3(C::KV_NW * 64), 0, st, p);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(((L + BKV - 1) / BKV) * s.hkv * s.batch),
+                     dim3(2 * C::KV_NP * 64), 0, st, p);
   prof_end(CA_KERNEL_DKDV, st);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int BQ = C::DQ_NW * C::DQ_NQT * 16;
   prof_begin(CA_KERNEL_DQ, st);
   hipLaunchKernelGGL((dq_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW>), dim3(((s.len + BQ - 1) / BQ) * s.hq * s.batch),
-                     dim3(C::DQ_NW * 64), 0, st, p);
+                     dim3(2 * C::DQ_NW * 64), 0, st, p);
   prof_end(CA_KERNEL_DQ, st);
   return hipGetLastError();
 }
