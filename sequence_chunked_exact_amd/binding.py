@@ -11,6 +11,13 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
+# torch first: its HIP runtime (torch/lib/libamdhip64.so, soname
+# libamdhip64.so.7) must be the one the library's libamdhip64.so.7 dependency
+# binds to. Loading the library first would map the system runtime, and torch,
+# which asks for the file name rather than the soname, would then map a second
+# one; two HIP runtimes in one process do not share devices or memory.
+import torch  # noqa: F401  (imported for its side effect on library loading)
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libchunk_attn.so")
 

@@ -699,9 +699,10 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
 // waves, each pair owning NKT*16 keys, walk every (q head of the group,
 // query tile) block that can see them. Wave w < NP of a pair holds the keys'
 // K fragments and dV sums: S = Q K^T, P = exp(S - LSE) (causally masked),
-// dV += P^T dO, and P goes to LDS. Its partner, wave NP + w, holds the V
-// fragments and dK sums and runs one block behind: dP = dO V^T,
-// dS = P (dP - delta) with that P, dK += dS^T Q. Each wave then does two of
+// dV += P^T dO, and P goes to LDS as the packed fragments of that product.
+// Its partner, wave NP + w, holds the V fragments and dK sums and runs one
+// block behind: dP = dO V^T, dS = P (dP - delta) with that (rounded) P,
+// dK += dS^T Q. Each wave then does two of
 // the four products per block and fits in half the register file, so the two
 // waves of a pair share a SIMD and overlap each other's LDS reads and
 // exponentials with their products. Q and dO blocks go through three LDS
@@ -719,8 +720,8 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) T Ds[NB][BQ * Lay<T, D>::RS];
   // per buffer: LSE*log2(e) of the block's rows in [0, BQ), delta in [BQ, 2BQ)
   __shared__ __attribute__((aligned(16))) float stat_s[NB][2 * BQ];
-  // P of a pair's block, as the lanes hold it: [block parity][pair][mq][nk][lane]
-  __shared__ f32x4 Ps[2][NP][MQ][NKT][64];
+  // P of a pair's block as the A fragments of dV: [block parity][pair][kq][nk][lane]
+  __shared__ frag Ps[2][NP][KQ][NKT][64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -837,16 +838,15 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
               for (int i = 0; i < 4; ++i)
                 if (wk0 + nk * 16 + n > q_lo + mq * 16 + 4 * g + i) s[mq][nk][i] = 0.f;
         }
-#pragma unroll
-        for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) Ps[it & 1][pair][mq][nk][lane] = s[mq][nk];
         const T* Dc = Ds[cur];
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
           frag pf[NKT];
 #pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) pf[nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
+          for (int nk = 0; nk < NKT; ++nk) {
+            pf[nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
+            Ps[it & 1][pair][kq][nk][lane] = pf[nk];
+          }
 #pragma unroll
           for (int md = 0; md < MD; ++md) {
             const frag dtr = ldT8<D>(Dc, kq * 32, md * 16, lane);
@@ -876,13 +876,17 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
             for (int nk = 0; nk < NKT; ++nk) E::mma(dp[mq][nk], da, kv[nk][kb]);
           }
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq) {
-          const f32x4 d4 = *(const f32x4*)&stat_s[prv][BQ + mq * 16 + 4 * g];
+        for (int kq = 0; kq < KQ; ++kq) {
+          const f32x4 d4lo = *(const f32x4*)&stat_s[prv][BQ + kq * 32 + 4 * g];
+          const f32x4 d4hi = *(const f32x4*)&stat_s[prv][BQ + kq * 32 + 16 + 4 * g];
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk) {
-            const f32x4 pv = Ps[(it - 1) & 1][pair][mq][nk][lane];
+            const frag pf = Ps[(it - 1) & 1][pair][kq][nk][lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dp[mq][nk][i] = pv[i] * (dp[mq][nk][i] - d4[i]);
+            for (int i = 0; i < 4; ++i) {
+              dp[2 * kq][nk][i] = (float)pf[i] * (dp[2 * kq][nk][i] - d4lo[i]);
+              dp[2 * kq + 1][nk][i] = (float)pf[4 + i] * (dp[2 * kq + 1][nk][i] - d4hi[i]);
+            }
           }
         }
         const T* Qc = Qs[prv];
@@ -961,7 +965,7 @@ template <typename T, int D>
 struct Cfg {
   static constexpr int FWD_NQT = 2, FWD_BK = 64, FWD_NW = 4;
   static constexpr int DQ_NQT = 2, DQ_BK = 64, DQ_NW = 4;
-  static constexpr int KV_NKT = 2, KV_BQ = 32, KV_NP = 4;
+  static constexpr int KV_NKT = 2, KV_BQ = 64, KV_NP = 4;
 };
 // float32 storage (the exactness path) takes smaller tiles: its fragments are
 // twice as wide in registers.

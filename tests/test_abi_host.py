@@ -33,6 +33,19 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(so, name), name
 
 
+def test_one_hip_runtime_when_loaded_before_torch():
+    # A caller that imports the binding before torch must still end up with a
+    # single HIP runtime in the process (the library shares torch's).
+    import subprocess
+    import sys
+    code = ("import sequence_chunked_exact_amd.binding, torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths), sorted(paths))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, check=True)
+    assert out.stdout.split()[0] == "1", out.stdout
+
+
 def desc(**kw):
     base = dict(batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, kv_capacity=1024, q_capacity=256,
                 q_row_offset=0, chunk_start=512, chunk_len=256, softmax_scale=1.0, dtype=b.CA_BF16)
