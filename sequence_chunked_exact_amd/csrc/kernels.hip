@@ -742,6 +742,7 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   const int qt0 = max(0, kb0 - p.start) / BQ;
   const int qt_end = (p.len + BQ - 1) / BQ;
   const int iters = G * (qt_end - qt0);
+  auto next_qt = [&](int q) { return q + 1 == qt_end ? qt0 : q + 1; };
 
   // Next block to fetch, walked q tile fastest then q head.
   int f_qt = qt0, f_h = hk * G;
@@ -796,34 +797,39 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   wait_loads();
   __syncthreads();
 
-  // q_lo: position of the first row of block `it` (rows advance q tile first).
-  int a_qt = qt0;  // q tile of the block the P/dV waves take next
+  // One code path for both roles (only the VALU step between the two
+  // products differs), so that the accumulator chain has a single home in
+  // registers. The P/dV waves take block it, the dS/dK waves block it - 1.
+  int qv = qt0;  // q tile of this wave's block
   for (int it = 0; it <= iters; ++it) {
     const bool more = it + 1 < iters;
     if (more) fetch();
-    if (pv_wave) {
-      const int q0 = a_qt * BQ;
-      const int q_lo = p.start + q0, q_hi = p.start + min(q0 + BQ, p.len) - 1;
-      if (++a_qt == qt_end) a_qt = qt0;
-      if (it < iters && wk0 <= q_hi) {
-        const int cur = it % NB;
-        const T* Qc = Qs[cur];
-        f32x4 s[MQ][NKT];
+    const int blk = pv_wave ? it : it - 1;
+    const int q0 = qv * BQ;
+    const int q_lo = p.start + q0, q_hi = p.start + min(q0 + BQ, p.len) - 1;
+    if (blk >= 0 && blk < iters) qv = next_qt(qv);
+    if (blk >= 0 && blk < iters && wk0 <= q_hi) {
+      const int buf = blk % NB;
+      const T* A = pv_wave ? Qs[buf] : Ds[buf];  // row-major operand of S or dP
+      const T* X = pv_wave ? Ds[buf] : Qs[buf];  // transposed operand of dV or dK
+      f32x4 s[MQ][NKT];
 #pragma unroll
-        for (int mq = 0; mq < MQ; ++mq)
+      for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nk = 0; nk < NKT; ++nk) s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-          for (int mq = 0; mq < MQ; ++mq) {
-            const frag qa = ld8s<D>(Qc, mq * 16 + n, kb * 32 + 8 * g);
-#pragma unroll
-            for (int nk = 0; nk < NKT; ++nk) E::mma(s[mq][nk], qa, kv[nk][kb]);
-          }
+      for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
         for (int mq = 0; mq < MQ; ++mq) {
-          const f32x4 l4 = *(const f32x4*)&stat_s[cur][mq * 16 + 4 * g];
+          const frag a = ld8s<D>(A, mq * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+          for (int nk = 0; nk < NKT; ++nk) E::mma(s[mq][nk], a, kv[nk][kb]);
+        }
+      frag wf[KQ][NKT];  // P (P/dV) or dS (dS/dK) as A fragments
+      if (pv_wave) {
+#pragma unroll
+        for (int mq = 0; mq < MQ; ++mq) {
+          const f32x4 l4 = *(const f32x4*)&stat_s[buf][mq * 16 + 4 * g];
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk)
 #pragma unroll
@@ -838,71 +844,39 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
               for (int i = 0; i < 4; ++i)
                 if (wk0 + nk * 16 + n > q_lo + mq * 16 + 4 * g + i) s[mq][nk][i] = 0.f;
         }
-        const T* Dc = Ds[cur];
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) {
-          frag pf[NKT];
+        for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk) {
-            pf[nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
-            Ps[it & 1][pair][kq][nk][lane] = pf[nk];
+            wf[kq][nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
+            Ps[blk & 1][pair][kq][nk][lane] = wf[kq][nk];
           }
-#pragma unroll
-          for (int md = 0; md < MD; ++md) {
-            const frag dtr = ldT8<D>(Dc, kq * 32, md * 16, lane);
-#pragma unroll
-            for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], pf[nk], dtr);
-          }
-        }
-      }
-    } else if (it >= 1) {  // block it - 1
-      const int q0 = a_qt * BQ;
-      const int q_hi = p.start + min(q0 + BQ, p.len) - 1;
-      if (++a_qt == qt_end) a_qt = qt0;
-      if (wk0 <= q_hi) {
-        const int prv = (it + NB - 1) % NB;
-        const T* Dc = Ds[prv];
-        f32x4 dp[MQ][NKT];
-#pragma unroll
-        for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) dp[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-          for (int mq = 0; mq < MQ; ++mq) {
-            const frag da = ld8s<D>(Dc, mq * 16 + n, kb * 32 + 8 * g);
-#pragma unroll
-            for (int nk = 0; nk < NKT; ++nk) E::mma(dp[mq][nk], da, kv[nk][kb]);
-          }
+      } else {
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
-          const f32x4 d4lo = *(const f32x4*)&stat_s[prv][BQ + kq * 32 + 4 * g];
-          const f32x4 d4hi = *(const f32x4*)&stat_s[prv][BQ + kq * 32 + 16 + 4 * g];
+          const f32x4 d4lo = *(const f32x4*)&stat_s[buf][BQ + kq * 32 + 4 * g];
+          const f32x4 d4hi = *(const f32x4*)&stat_s[buf][BQ + kq * 32 + 16 + 4 * g];
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk) {
-            const frag pf = Ps[(it - 1) & 1][pair][kq][nk][lane];
+            const frag pf = Ps[blk & 1][pair][kq][nk][lane];
+            f32x4 lo, hi;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              dp[2 * kq][nk][i] = (float)pf[i] * (dp[2 * kq][nk][i] - d4lo[i]);
-              dp[2 * kq + 1][nk][i] = (float)pf[4 + i] * (dp[2 * kq + 1][nk][i] - d4hi[i]);
+              lo[i] = (float)pf[i] * (s[2 * kq][nk][i] - d4lo[i]);
+              hi[i] = (float)pf[4 + i] * (s[2 * kq + 1][nk][i] - d4hi[i]);
             }
-          }
-        }
-        const T* Qc = Qs[prv];
-#pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) {
-          frag dsf[NKT];
-#pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) dsf[nk] = pack44<T>(dp[2 * kq][nk], dp[2 * kq + 1][nk]);
-#pragma unroll
-          for (int md = 0; md < MD; ++md) {
-            const frag qtr = ldT8<D>(Qc, kq * 32, md * 16, lane);
-#pragma unroll
-            for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], dsf[nk], qtr);
+            wf[kq][nk] = pack44<T>(lo, hi);
           }
         }
       }
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const frag x = ldT8<D>(X, kq * 32, md * 16, lane);
+#pragma unroll
+          for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], wf[kq][nk], x);
+        }
     }
     // Buffer (it + 1) % NB last served block it - 2, whose dS/dK pass ended
     // before the previous barrier.
