@@ -89,32 +89,54 @@ struct Elt<float> {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Row-major [rows][D] LDS tile whose rows are padded by one 16-byte chunk:
-// row r starts at element r * RS, RS = D + 16 / sizeof(T). Every head size
-// here makes the row stride an odd multiple of 4 banks (mod 64), so the
-// 16 consecutive rows of one access start 4 banks apart in 16 different
-// positions. Both read patterns used here are then conflict-free: 16 lanes
-// reading one 16-byte chunk column from 16 consecutive rows (row-major
-// fragments), and the transposing read of 16 rows x 32 bytes, which lands
-// on every bank exactly twice (its minimum, 512 bytes in two passes). A
-// lane's address is a loop-invariant base plus a constant offset.
+// Two row-major [rows][D] LDS tile layouts; both keep the two read patterns
+// used here free of bank conflicts: 16 lanes reading one 16-byte chunk
+// column from 16 consecutive rows (row-major fragments), and the transposing
+// read of 16 rows x 32 bytes, which lands on every bank exactly twice (its
+// minimum: 512 bytes in two passes).
+//
+// PadLay: rows padded by 32 bytes (row stride RS = D + 32 / sizeof(T)
+// elements, an odd multiple of 8 banks for every head size here), so 16
+// consecutive rows start in 16 different bank groups. A lane's address is a
+// loop-invariant base plus a constant offset. Used for tiles written from
+// registers.
 template <typename T, int D>
-struct Lay {
+struct PadLay {
   static constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   static constexpr int RS = D + 2 * EPC;      // row stride in elements
   static_assert(((RS * sizeof(T) / 4 / 8) & 1) == 1, "row stride must be an odd multiple of 8 banks");
   static __device__ __forceinline__ int off(int r, int c) { return r * RS + c; }
 };
 
+// SwzLay: unpadded rows (stride D), the 16-byte chunk c of row r stored at
+// chunk position c ^ swz(r). The map (r mod 16, with bit 3 ^= bit 0 and bit
+// 2 ^= bit 3) was picked by measuring gfx950's LDS bank-conflict counter over
+// a family of candidate maps; it is the simplest one under which both read
+// patterns run conflict-free. Used for tiles filled by direct global->LDS
+// loads, which write each wave's 64 x 16 bytes contiguously.
+template <typename T, int D>
+struct SwzLay {
+  static constexpr int EPC = 16 / sizeof(T);
+  static constexpr int CH = D / EPC;  // chunks per row
+  static constexpr int RS = D;
+  static __device__ __forceinline__ int swz(int r) {
+    const int x = (r ^ ((r & 1) << 3) ^ (((r >> 3) & 1) << 2)) & 15;
+    return x & (CH - 1);
+  }
+  static __device__ __forceinline__ int off(int r, int c) {
+    return r * D + (((c / EPC) ^ swz(r)) * EPC) + (c % EPC);
+  }
+};
+
 // 8 consecutive elements of row r from column c (c % 8 == 0), contiguous order.
-template <int D>
+template <class Lt>
 __device__ __forceinline__ bf16x8 ld8s(const bf16* t, int r, int c) {
-  return *(const bf16x8*)(t + Lay<bf16, D>::off(r, c));
+  return *(const bf16x8*)(t + Lt::off(r, c));
 }
-template <int D>
+template <class Lt>
 __device__ __forceinline__ f32x8 ld8s(const float* t, int r, int c) {
-  const f32x4 a = *(const f32x4*)(t + Lay<float, D>::off(r, c));
-  const f32x4 b = *(const f32x4*)(t + Lay<float, D>::off(r, c + 4));
+  const f32x4 a = *(const f32x4*)(t + Lt::off(r, c));
+  const f32x4 b = *(const f32x4*)(t + Lt::off(r, c + 4));
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
@@ -122,32 +144,32 @@ __device__ __forceinline__ f32x8 ld8s(const float* t, int r, int c) {
 // the same for the 16 lanes of a group). bf16 uses the transposing LDS read:
 // lane j of a group points at row rb + j/4, columns c0 + 4(j%4) .. +3, and the
 // hardware hands lane i element k of lane 4k + i/4's four.
-template <int D>
+template <class Lt>
 __device__ __forceinline__ bf16x4 ldT4(const bf16* t, int rb, int c0, int lane) {
   const int j = lane & 15;
-  const bf16* p = t + Lay<bf16, D>::off(rb + (j >> 2), c0 + 4 * (j & 3));
+  const bf16* p = t + Lt::off(rb + (j >> 2), c0 + 4 * (j & 3));
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<bf16*>(p)));
   return __builtin_bit_cast(bf16x4, v);
 }
-template <int D>
+template <class Lt>
 __device__ __forceinline__ f32x4 ldT4(const float* t, int rb, int c0, int lane) {
   const int n = lane & 15;
   f32x4 v;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = t[Lay<float, D>::off(rb + k, c0 + n)];
+  for (int k = 0; k < 4; ++k) v[k] = t[Lt::off(rb + k, c0 + n)];
   return v;
 }
 // Fragment of t[kbase + tile-order slots][c0 + n] (operand contracted over rows).
-template <int D>
+template <class Lt>
 __device__ __forceinline__ bf16x8 ldT8(const bf16* t, int kbase, int c0, int lane) {
   const int g = lane >> 4;
-  const bf16x4 a = ldT4<D>(t, kbase + 4 * g, c0, lane), b = ldT4<D>(t, kbase + 16 + 4 * g, c0, lane);
+  const bf16x4 a = ldT4<Lt>(t, kbase + 4 * g, c0, lane), b = ldT4<Lt>(t, kbase + 16 + 4 * g, c0, lane);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-template <int D>
+template <class Lt>
 __device__ __forceinline__ f32x8 ldT8(const float* t, int kbase, int c0, int lane) {
   const int g = lane >> 4;
-  const f32x4 a = ldT4<D>(t, kbase + 4 * g, c0, lane), b = ldT4<D>(t, kbase + 16 + 4 * g, c0, lane);
+  const f32x4 a = ldT4<Lt>(t, kbase + 4 * g, c0, lane), b = ldT4<Lt>(t, kbase + 16 + 4 * g, c0, lane);
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
@@ -156,6 +178,16 @@ __device__ __forceinline__ bf16x8 ldg8(const bf16* p) { return *(const bf16x8*)p
 __device__ __forceinline__ f32x8 ldg8(const float* p) {
   const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// A fragment of ones: as the A operand of a product with P^T it gives every
+// output lane the sum of P over the 32 contracted rows.
+template <typename T>
+__device__ __forceinline__ typename Elt<T>::frag ones_frag() {
+  typename Elt<T>::frag f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (T)1.f;
+  return f;
 }
 
 // Two stacked output tiles' registers -> fragment in tile slot order.
@@ -192,10 +224,6 @@ __device__ __forceinline__ float max4(float m) {
   m = fmaxf(m, __shfl_xor(m, 16));
   return fmaxf(m, __shfl_xor(m, 32));
 }
-__device__ __forceinline__ float sum4(float s) {
-  s += __shfl_xor(s, 16);
-  return s + __shfl_xor(s, 32);
-}
 
 // Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
 // own L2. This maps the linear id to a logical work index so that every XCD
@@ -209,8 +237,35 @@ __device__ __forceinline__ int xcd_order(int id, int n) {
   return id < per * X ? (id % X) * per + id / X : id;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Stream rows [row0, row0 + ROWS) of a row-major [*, D] head into a SwzLay
+// LDS tile with direct global->LDS loads, shared by NW waves: each wave
+// instruction fills 64 consecutive 16-byte LDS slots, so lane l fetches the
+// global chunk that belongs in its slot (the swizzle is applied on the global
+// side, and each instruction still reads whole rows). Rows at or beyond
+// `limit` (>= 1) re-read row limit-1; every consumer gives such rows zero
+// weight (keys past the prefix are causally masked).
+template <typename T, int ROWS, int D, int NW>
+__device__ __forceinline__ void stage_tile(T* lds, const T* head, int row0, int limit, int wave, int lane) {
+  using Lt = SwzLay<T, D>;
+  constexpr int CH = Lt::CH, RPI = 64 / CH, PER_WAVE = ROWS / NW;
+  static_assert(CH <= 64 && PER_WAVE % RPI == 0, "tile rows per wave must fill whole instructions");
+#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-loading builtin exists only in the device pass
+  const int rl = lane / CH, slot = lane % CH;
+#pragma unroll
+  for (int i = 0; i < PER_WAVE / RPI; ++i) {
+    const int rb = wave * PER_WAVE + i * RPI;  // wave-uniform first row of this instruction
+    const int r = rb + rl;
+    const int c = slot ^ Lt::swz(r);
+    const T* src = head + (size_t)min(row0 + r, limit - 1) * D + c * Lt::EPC;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + rb * D), 16, 0, 0);
+  }
+#endif
+}
+
 // A [ROWS][D] tile staged through registers: thread tid fetches R rows of
-// one 16-byte column vector and later writes them into a swizzled LDS tile
+// one 16-byte column vector and later writes them into a PadLay LDS tile
 // (threads beyond the tile's ROWS * D / VEC vectors fetch a duplicate and
 // store nothing). Rows at or beyond `limit` (>= 1) re-read row limit-1;
 // every consumer gives such rows zero weight (keys past the prefix are
@@ -238,7 +293,7 @@ struct RegTile {
     const int dv = tid % NDV, grp = tid / NDV;
     if (SPARE && grp >= ROWS) return;
 #pragma unroll
-    for (int i = 0; i < R; ++i) *(V*)(lds + Lay<T, D>::off(grp * R + i, dv * VEC)) = r[i];
+    for (int i = 0; i < R; ++i) *(V*)(lds + PadLay<T, D>::off(grp * R + i, dv * VEC)) = r[i];
   }
 };
 
@@ -255,10 +310,13 @@ __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 // (held as B fragments of S^T = K Q^T), and group 0 takes the even key tiles
 // while group 1 takes the odd ones, so each SIMD runs two waves (one's LDS
 // reads and softmax overlap the other's MFMAs) without more LDS traffic per
-// product. Pairs of key tiles stream through double-buffered LDS, fetched
-// into registers one pair ahead. At the end group 1 hands its running
-// maximum, row sums and O^T to group 0 through LDS, which merges and stores.
-// Tiles past a wave's rows are skipped; only diagonal tiles are masked.
+// product. Pairs of key tiles stream into double-buffered LDS by direct
+// global->LDS loads issued one pair ahead; the two buffers are separate
+// arrays named statically (the loop is unrolled by two), which lets the
+// compiler see that reads of one buffer do not depend on the loads into the
+// other. At the end group 1 hands its running maximum, row sums and O^T to
+// group 0 through LDS, which merges and stores. Tiles past a wave's rows are
+// skipped; only diagonal tiles are masked.
 // ----------------------------------------------------------------------------
 struct FwdParams {
   const void* q;
@@ -275,11 +333,15 @@ template <typename T, int D, int NQT, int BK, int NW>
 __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int NT = 2 * NW * 64, BQ = NW * NQT * 16;
+  using Lt = SwzLay<T, D>;
+  constexpr int BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
-  // smem[b][0] holds the K tiles 2i (slot 0) and 2i+1 (slot 1) of pair i,
-  // smem[b][1] the V tiles, with b = i & 1.
-  __shared__ __attribute__((aligned(16))) T smem[2][2][2][BK * Lay<T, D>::RS];
+  // Pair i uses buffer i & 1: K tiles 2i, 2i+1 in Kb<i&1> (rows [0, BK) and
+  // [BK, 2BK)), V tiles likewise in Vb<i&1>.
+  __shared__ __attribute__((aligned(16))) T Kb0[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) T Vb0[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) T Kb1[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) T Vb1[2 * BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -303,10 +365,11 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
   const float c2 = p.c2;
 
-  // The pair's two K tiles and two V tiles are one [2*BK][D] block each.
-  RegTile<T, 2 * BK, D, NT> kt, vt;
-  kt.load(K, 0, L, tid);
-  vt.load(V, 0, L, tid);
+  auto stage = [&](T* kd, T* vd, int pair) {
+    stage_tile<T, 2 * BK, D, 2 * NW>(kd, K, 2 * pair * BK, L, wave, lane);
+    stage_tile<T, 2 * BK, D, 2 * NW>(vd, V, 2 * pair * BK, L, wave, lane);
+  };
+  stage(Kb0, Vb0, 0);
 
   frag qf[NQT][DK];
 #pragma unroll
@@ -319,31 +382,29 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
     }
   }
   f32x4 oacc[MD][NQT];
-  float m2[NQT], lrun[NQT];
+  // Row sums of P come out of the matrix cores (ones times P^T): every lane
+  // of a query column holds the column's full sum, in all four slots.
+  f32x4 lacc[NQT];
+  float m2[NQT];
+  const frag ones = ones_frag<T>();
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
     m2[nt] = -kInf;
-    lrun[nt] = 0.f;
+    lacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int md = 0; md < MD; ++md) oacc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  kt.store(&smem[0][0][0][0], tid);
-  vt.store(&smem[0][1][0][0], tid);
   wait_loads();
   __syncthreads();
 
-  for (int i = 0; i < n_pairs; ++i) {
-    const int cur = i & 1;
-    const bool more = i + 1 < n_pairs;
-    if (more) {
-      kt.load(K, (2 * i + 2) * BK, L, tid);
-      vt.load(V, (2 * i + 2) * BK, L, tid);
-    }
+  // Pair i from the buffer (Kc, Vc); the next pair streams into (Kn, Vn).
+  auto pair_step = [&](int i, const T* Kc, const T* Vc, T* Kn, T* Vn) {
+    if (i + 1 < n_pairs) stage(Kn, Vn, i + 1);
     const int j = 2 * i + grp;  // this group's key tile
     const int kb0 = j * BK;
     if (active && j < n_tiles && kb0 <= wq_hi) {
-      const T* Kc = smem[cur][0][grp];
-      const T* Vc = smem[cur][1][grp];
+      const T* Kt = Kc + grp * BK * D;
+      const T* Vt = Vc + grp * BK * D;
       f32x4 s[MK][NQT];
 #pragma unroll
       for (int mk = 0; mk < MK; ++mk)
@@ -353,7 +414,7 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
       for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
         for (int mk = 0; mk < MK; ++mk) {
-          const frag a = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
+          const frag a = ld8s<Lt>(Kt, mk * 16 + n, kb * 32 + 8 * g);
 #pragma unroll
           for (int nt = 0; nt < NQT; ++nt) E::mma(s[mk][nt], a, qf[nt][kb]);
         }
@@ -390,7 +451,7 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
           const float mnew = fmaxf(m2[nt], max4(mx2[nt]));
           const float alpha = mnew == -kInf ? 1.f : fexp2(m2[nt] - mnew);
           m2[nt] = mnew;
-          lrun[nt] *= alpha;
+          lacc[nt] *= alpha;
 #pragma unroll
           for (int md = 0; md < MD; ++md) oacc[md][nt] *= alpha;
         }
@@ -405,71 +466,82 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
         frag pf[NQT];
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt) {
-          float lsum = 0.f;
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-              const float e = fexp2(__builtin_fmaf(s[2 * kb2 + hh][nt][ii], c2, -mref[nt]));
-              s[2 * kb2 + hh][nt][ii] = e;
-              lsum += e;
-            }
-          lrun[nt] += lsum;
+            for (int ii = 0; ii < 4; ++ii)
+              s[2 * kb2 + hh][nt][ii] = fexp2(__builtin_fmaf(s[2 * kb2 + hh][nt][ii], c2, -mref[nt]));
           pf[nt] = pack44<T>(s[2 * kb2][nt], s[2 * kb2 + 1][nt]);
         }
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-          const frag a = ldT8<D>(Vc, kb2 * 32, md * 16, lane);
+          const frag a = ldT8<Lt>(Vt, kb2 * 32, md * 16, lane);
 #pragma unroll
           for (int nt = 0; nt < NQT; ++nt) E::mma(oacc[md][nt], a, pf[nt]);
         }
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) E::mma(lacc[nt], ones, pf[nt]);
       }
     }
-    if (more) {
-      kt.store(&smem[cur ^ 1][0][0][0], tid);
-      vt.store(&smem[cur ^ 1][1][0][0], tid);
-    }
+    wait_loads();  // the next pair has landed in LDS
     __syncthreads();
+  };
+  for (int i = 0; i < n_pairs; i += 2) {
+    pair_step(i, Kb0, Vb0, Kb1, Vb1);
+    if (i + 1 < n_pairs) pair_step(i + 1, Kb1, Vb1, Kb0, Vb0);
   }
 
-  // Merge: group 1 publishes (m2, lane-partial row sum, O^T) per lane; the
-  // matching lane of group 0 rescales both to the larger maximum and adds.
-  float* xfer = (float*)&smem[0][0][0][0];
-  constexpr int PER = 2 + MD * 4;  // floats per lane and query tile
-  static_assert(sizeof(smem) >= (size_t)NW * 64 * NQT * PER * sizeof(float), "merge area");
+  // Merge: group 1 publishes (m2, row sum, O^T) per lane; the matching lane
+  // of group 0 rescales both to the larger maximum and adds. The exchange
+  // spans three of the (now idle) tile buffers: O^T columns [0, D/2) in Kb0,
+  // [D/2, D) in Vb0, the two statistics in Kb1.
+  constexpr int HALF = MD / 2 * 4;  // floats per lane and query tile in each O half
+  static_assert(sizeof(Kb0) >= (size_t)NQT * NW * 64 * HALF * sizeof(float) &&
+                    sizeof(Kb1) >= (size_t)NQT * NW * 64 * 2 * sizeof(float),
+                "merge area");
+  float* xo0 = (float*)Kb0;
+  float* xo1 = (float*)Vb0;
+  float* xs = (float*)Kb1;
   if (grp == 1) {
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
-      float* x = xfer + ((size_t)(nt * NW + wq) * PER) * 64 + lane;
-      x[0] = m2[nt];
-      x[64] = lrun[nt];
+      const size_t slot = (size_t)(nt * NW + wq);
+      xs[(slot * 2 + 0) * 64 + lane] = m2[nt];
+      xs[(slot * 2 + 1) * 64 + lane] = lacc[nt][0];
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[(2 + md * 4 + e) * 64] = oacc[md][nt][e];
+        for (int e = 0; e < 4; ++e) {
+          float* x = md < MD / 2 ? xo0 : xo1;
+          x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane] = oacc[md][nt][e];
+        }
     }
   }
   __syncthreads();
   if (grp == 1 || !active) return;
+  float lrow[NQT];
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
-    const float* x = xfer + ((size_t)(nt * NW + wq) * PER) * 64 + lane;
-    const float mb = x[0];
+    const size_t slot = (size_t)(nt * NW + wq);
+    const float mb = xs[(slot * 2 + 0) * 64 + lane];
     const float mnew = fmaxf(m2[nt], mb);
     // both maxima are finite for every visible row: tile 0 (group 0) holds key 0
     const float fa = fexp2(m2[nt] - mnew), fb = mb == -kInf ? 0.f : fexp2(mb - mnew);
-    lrun[nt] = lrun[nt] * fa + x[64] * fb;
+    lrow[nt] = lacc[nt][0] * fa + xs[(slot * 2 + 1) * 64 + lane] * fb;
     m2[nt] = mnew;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) oacc[md][nt][e] = oacc[md][nt][e] * fa + x[(2 + md * 4 + e) * 64] * fb;
+      for (int e = 0; e < 4; ++e) {
+        const float* x = md < MD / 2 ? xo0 : xo1;
+        oacc[md][nt][e] = oacc[md][nt][e] * fa + x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane] * fb;
+      }
   }
   T* O = (T*)p.o + ((size_t)(b * p.hq + h) * p.q_cap + p.q_off) * D;
   float* LSE = p.lse + (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
-    const float l = sum4(lrun[nt]);
+    const float l = lrow[nt];
     const int row = wr0 + nt * 16 + n;
     if (row < p.len) {
       const float inv = 1.f / l;
@@ -530,18 +602,23 @@ struct BwdParams {
   float dv_scale;  // grad_scale
 };
 
-// dQ pass. Same walk and split as the forward: two groups of NW waves own the
-// same query rows and take the even / odd key tiles; per tile S^T = K Q^T and
-// dP^T = V dO^T with K, V read row-major from LDS, P from the stored LSE, and
+// dQ pass. Same walk, split and staging as the forward: two groups of NW
+// waves own the same query rows and take the even / odd key tiles of pairs
+// streamed into two statically named LDS buffers. Per tile S^T = K Q^T and
+// dP^T = V dO^T with K, V read row-major, P from the stored LSE, and
 // dQ^T += K^T dS^T with K read through the transposing path. Group 1 hands
 // its partial dQ to group 0 through LDS at the end.
 template <typename T, int D, int NQT, int BK, int NW>
 __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int NT = 2 * NW * 64, BQ = NW * NQT * 16;
+  using Lt = SwzLay<T, D>;
+  constexpr int BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, KB2 = BK / 32;
-  __shared__ __attribute__((aligned(16))) T smem[2][2][2][BK * Lay<T, D>::RS];  // [buffer][K|V][tile of pair]
+  __shared__ __attribute__((aligned(16))) T Kb0[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) T Vb0[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) T Kb1[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) T Vb1[2 * BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -569,9 +646,11 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
   const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
   const float c2 = p.c2;
 
-  RegTile<T, 2 * BK, D, NT> kt, vt;
-  kt.load(K, 0, L, tid);
-  vt.load(V, 0, L, tid);
+  auto stage = [&](T* kd, T* vd, int pair) {
+    stage_tile<T, 2 * BK, D, 2 * NW>(kd, K, 2 * pair * BK, L, wave, lane);
+    stage_tile<T, 2 * BK, D, 2 * NW>(vd, V, 2 * pair * BK, L, wave, lane);
+  };
+  stage(Kb0, Vb0, 0);
 
   frag qf[NQT][DK], df[NQT][DK];
   float lse2[NQT], dl[NQT];
@@ -593,23 +672,16 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  kt.store(&smem[0][0][0][0], tid);
-  vt.store(&smem[0][1][0][0], tid);
   wait_loads();
   __syncthreads();
 
-  for (int i = 0; i < n_pairs; ++i) {
-    const int cur = i & 1;
-    const bool more = i + 1 < n_pairs;
-    if (more) {
-      kt.load(K, (2 * i + 2) * BK, L, tid);
-      vt.load(V, (2 * i + 2) * BK, L, tid);
-    }
+  auto pair_step = [&](int i, const T* Kc, const T* Vc, T* Kn, T* Vn) {
+    if (i + 1 < n_pairs) stage(Kn, Vn, i + 1);
     const int j = 2 * i + grp;  // this group's key tile
     const int kb0 = j * BK;
     if (active && j < n_tiles && kb0 <= wq_hi) {
-      const T* Kc = smem[cur][0][grp];
-      const T* Vc = smem[cur][1][grp];
+      const T* Kt = Kc + grp * BK * D;
+      const T* Vt = Vc + grp * BK * D;
       const bool diag = kb0 + BK - 1 > wq_lo;  // tile crosses this wave's diagonal
       // One 32-key half at a time keeps only half the tile's S and dP live.
 #pragma unroll
@@ -627,8 +699,8 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int mk = 2 * kb2 + hh;
-            const frag ak = ld8s<D>(Kc, mk * 16 + n, kb * 32 + 8 * g);
-            const frag av = ld8s<D>(Vc, mk * 16 + n, kb * 32 + 8 * g);
+            const frag ak = ld8s<Lt>(Kt, mk * 16 + n, kb * 32 + 8 * g);
+            const frag av = ld8s<Lt>(Vt, mk * 16 + n, kb * 32 + 8 * g);
 #pragma unroll
             for (int nt = 0; nt < NQT; ++nt) {
               E::mma(s[hh][nt], ak, qf[nt][kb]);
@@ -651,31 +723,37 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-          const frag a = ldT8<D>(Kc, kb2 * 32, md * 16, lane);
+          const frag a = ldT8<Lt>(Kt, kb2 * 32, md * 16, lane);
 #pragma unroll
           for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], a, dsf[nt]);
         }
       }
     }
-    if (more) {
-      kt.store(&smem[cur ^ 1][0][0][0], tid);
-      vt.store(&smem[cur ^ 1][1][0][0], tid);
-    }
+    wait_loads();  // the next pair has landed in LDS
     __syncthreads();
+  };
+  for (int i = 0; i < n_pairs; i += 2) {
+    pair_step(i, Kb0, Vb0, Kb1, Vb1);
+    if (i + 1 < n_pairs) pair_step(i + 1, Kb1, Vb1, Kb0, Vb0);
   }
 
-  // Merge: group 1 publishes its partial dQ^T per lane, group 0 adds it.
-  float* xfer = (float*)&smem[0][0][0][0];
-  constexpr int PER = MD * 4;
-  static_assert(sizeof(smem) >= (size_t)NW * 64 * NQT * PER * sizeof(float), "merge area");
+  // Merge: group 1 publishes its partial dQ^T per lane (columns [0, D/2) in
+  // Kb0, [D/2, D) in Vb0), group 0 adds it.
+  constexpr int HALF = MD / 2 * 4;
+  static_assert(sizeof(Kb0) >= (size_t)NQT * NW * 64 * HALF * sizeof(float), "merge area");
+  float* xo0 = (float*)Kb0;
+  float* xo1 = (float*)Vb0;
   if (grp == 1) {
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
-      float* x = xfer + ((size_t)(nt * NW + wq) * PER) * 64 + lane;
+      const size_t slot = (size_t)(nt * NW + wq);
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[(md * 4 + e) * 64] = acc[md][nt][e];
+        for (int e = 0; e < 4; ++e) {
+          float* x = md < MD / 2 ? xo0 : xo1;
+          x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane] = acc[md][nt][e];
+        }
     }
   }
   __syncthreads();
@@ -683,13 +761,14 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
   float* DQ = p.dq + qhead * D;
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
-    const float* x = xfer + ((size_t)(nt * NW + wq) * PER) * 64 + lane;
+    const size_t slot = (size_t)(nt * NW + wq);
     const int row = wr0 + nt * 16 + n;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
+      const float* x = md < MD / 2 ? xo0 : xo1;
       f32x4 v = acc[md][nt];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] += x[(md * 4 + e) * 64];
+      for (int e = 0; e < 4; ++e) v[e] += x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane];
       if (row < p.len) *(f32x4*)(DQ + (size_t)row * D + md * 16 + 4 * g) = v * p.dq_scale;
     }
   }
@@ -716,8 +795,8 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   constexpr int NT = 2 * NP * 64, BKV = NP * NKT * 16, NB = 3;
   constexpr int DK = D / 32, MD = D / 16, MQ = BQ / 16, KQ = BQ / 32;
   static_assert(2 * BQ <= NT, "row statistics: one value per thread");
-  __shared__ __attribute__((aligned(16))) T Qs[NB][BQ * Lay<T, D>::RS];
-  __shared__ __attribute__((aligned(16))) T Ds[NB][BQ * Lay<T, D>::RS];
+  __shared__ __attribute__((aligned(16))) T Qs[NB][BQ * PadLay<T, D>::RS];
+  __shared__ __attribute__((aligned(16))) T Ds[NB][BQ * PadLay<T, D>::RS];
   // per buffer: LSE*log2(e) of the block's rows in [0, BQ), delta in [BQ, 2BQ)
   __shared__ __attribute__((aligned(16))) float stat_s[NB][2 * BQ];
   // P of a pair's block as the A fragments of dV: [block parity][pair][kq][nk][lane]
@@ -821,7 +900,7 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
       for (int kb = 0; kb < DK; ++kb)
 #pragma unroll
         for (int mq = 0; mq < MQ; ++mq) {
-          const frag a = ld8s<D>(A, mq * 16 + n, kb * 32 + 8 * g);
+          const frag a = ld8s<PadLay<T, D>>(A, mq * 16 + n, kb * 32 + 8 * g);
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk) E::mma(s[mq][nk], a, kv[nk][kb]);
         }
@@ -873,7 +952,7 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
       for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
-          const frag x = ldT8<D>(X, kq * 32, md * 16, lane);
+          const frag x = ldT8<PadLay<T, D>>(X, kq * 32, md * 16, lane);
 #pragma unroll
           for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], wf[kq][nk], x);
         }
