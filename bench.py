@@ -92,8 +92,8 @@ def cpu_baseline(wl, inp_raw, n_heads=8):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="8b_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -138,18 +138,21 @@ def main():
 
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     B.profile_start()
     t_wall = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         selected = step()
+        marks[i].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     B.profile_stop()
     ms = e0.elapsed_time(e1) / args.steps
+    per_step = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)]
     prof = B.profile_read()
     log(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms/step)")
 
@@ -189,6 +192,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(min(per_step)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
