@@ -8,10 +8,16 @@
         --stats S.csv --fetch F.csv --write W.csv --cal-fetch CF.csv \\
         --cal-write CW.csv --kernel dkdv --workload 8b_layer --out profiles/X.md \\
         --commands "..."
+        [--mfma M.csv]
         Writes a markdown summary: per-kernel average durations from the
         kernel-trace statistics, and for one kernel the FETCH_SIZE/WRITE_SIZE
         per dispatch scaled by what the same counters read for the copy of
         known size, plus the SHA-256 of the kernel source it was measured on.
+        With --mfma (a run collecting SQ_VALU_MFMA_BUSY_CYCLES and
+        GRBM_GUI_ACTIVE) it adds each kernel's matrix-core busy fraction:
+        SQ_VALU_MFMA_BUSY_CYCLES sums over the 1024 SIMDs and
+        GRBM_GUI_ACTIVE over the 8 XCDs, so busy / (GRBM / 8) / 1024 is the
+        mean fraction of elapsed cycles in which a SIMD's matrix core was busy.
 """
 from __future__ import annotations
 
@@ -25,6 +31,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(HERE, "csrc", "kernels.hip")
 COPY_BYTES = 1 << 30
+N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 SHORT = {"fwd_kernel": "fwd", "dkdv_kernel": "dkdv", "dq_kernel": "dq", "delta_kernel": "delta",
          "zero_kernel": "zero", "accumulate_kernel": "accumulate"}
@@ -92,7 +99,21 @@ def summarize_main(args):
                   f"- FETCH_SIZE {statistics.mean(f):.0f} KiB -> {fetch_b / 1e6:.1f} MB",
                   f"- WRITE_SIZE {statistics.mean(w):.0f} KiB -> {write_b / 1e6:.1f} MB",
                   "", f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}"]
-    lines += [f"kernel_source_sha256: {kernel_source_sha256()}", ""]
+    if args.mfma:
+        busy, active = {}, {}
+        for r in csv.DictReader(open(args.mfma)):
+            k = short_name(r["Kernel_Name"])
+            tgt = busy if r["Counter_Name"] == "SQ_VALU_MFMA_BUSY_CYCLES" else \
+                active if r["Counter_Name"] == "GRBM_GUI_ACTIVE" else None
+            if tgt is not None:
+                tgt[k] = tgt.get(k, 0.0) + float(r["Counter_Value"])
+        lines += ["", "## Matrix-core busy fraction per kernel", "",
+                  "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8) / 1024, summed over the run's dispatches", "",
+                  "| kernel | MFMA busy |", "|---|---|"]
+        for k in sorted(busy):
+            if active.get(k):
+                lines.append(f"| {k} | {100.0 * busy[k] / (active[k] / N_XCD) / N_SIMD:.1f}% |")
+    lines += ["", f"kernel_source_sha256: {kernel_source_sha256()}", ""]
     with open(args.out, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
@@ -119,7 +140,7 @@ def main(argv=None):
     sub.add_parser("copy")
     s = sub.add_parser("summarize")
     for opt in ("--stats", "--fetch", "--write", "--cal-fetch", "--cal-write", "--kernel", "--workload",
-                "--out", "--commands"):
+                "--out", "--commands", "--mfma"):
         s.add_argument(opt, default=None)
     args = ap.parse_args(argv)
     if args.cmd == "copy":
