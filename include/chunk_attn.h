@@ -137,6 +137,39 @@ int sparse_chunk_bwd(const chunk_attn_desc* desc, int32_t seq_len, int32_t t, ui
                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
                      int32_t* selected_out, void* ws, size_t ws_bytes, void* stream);
 
+/* The projections on either side of the attention of chunk i, which complete
+ * one attention layer's chunked backward. The layer input H_in is
+ * [batch][h_capacity][d_model] in dtype, the chunk's positions at rows
+ * h_row_offset.. (+chunk_len); wq is [d_model][n_q_heads*head_dim] and wk, wv
+ * [d_model][n_kv_heads*head_dim], row-major in dtype; column h*head_dim + c of a
+ * projection is element c of head h. d_model must be a multiple of 64.
+ *
+ * qkv_proj_fwd: Q^(i) = H_in^(i) W_q into q rows [q_row_offset, +chunk_len) of
+ * every q head, and K^(i) = H_in^(i) W_k, V^(i) = H_in^(i) W_v into k, v rows
+ * [chunk_start, +chunk_len) (appending the chunk to the caches), in dtype.
+ *
+ * qkv_proj_bwd: the attention weight gradients of the StreamBP review, major
+ * comment 1: dW_q += H_in^(i)^T dQ^(i), and dW_k += H_in^T dK, dW_v += H_in^T dV.
+ * The review writes the last two per chunk over the prefix; summed over the
+ * chunks they equal H_in^T times the accumulated dK, dV, and here each chunk
+ * takes its own rows [chunk_start, +chunk_len) of dk_acc, dv_acc, which are
+ * final once chunk_attn_bwd of that chunk has run in a descending sweep (no
+ * later chunk touches them). Also writes the input gradient of the chunk's
+ * rows, dh = dQ W_q^T + dK W_k^T + dV W_v^T (float32, OVERWRITTEN;
+ * [batch][h_capacity][d_model], same rows as H_in). dq is the float32 output of
+ * chunk_attn_bwd for this chunk; dwq, dwk, dwv are float32 accumulators of the
+ * weights' shapes, INCREMENTED (the caller zeroes them before a sweep). The
+ * float32 gradients are rounded to dtype before they enter the products
+ * (float32 accumulation). Errors as for chunk_attn_fwd, plus CA_ERR_SHAPE for
+ * d_model or the H_in rows. */
+int qkv_proj_fwd(const chunk_attn_desc* desc, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
+                 const void* h, const void* wq, const void* wk, const void* wv, void* q, void* k, void* v,
+                 void* stream);
+int qkv_proj_bwd(const chunk_attn_desc* desc, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
+                 const void* h, const void* wq, const void* wk, const void* wv, const float* dq,
+                 const float* dk_acc, const float* dv_acc, float* dwq, float* dwk, float* dwv, float* dh,
+                 void* stream);
+
 /* Kernel timing for benchmarks (instrumentation only; results are unchanged).
  * chunk_attn_profile_start() clears the record and, until
  * chunk_attn_profile_stop(), brackets every kernel this library launches with
@@ -152,7 +185,8 @@ enum {
   CA_KERNEL_DQ = 3,         /* dQ of the chunk */
   CA_KERNEL_ACCUMULATE = 4, /* prefix_grad_accumulate */
   CA_KERNEL_ZERO = 5,       /* zero fill used by sparse_chunk_bwd */
-  CA_KERNEL_COUNT = 6
+  CA_KERNEL_PROJ = 6,       /* projection GEMMs of qkv_proj_fwd / qkv_proj_bwd */
+  CA_KERNEL_COUNT = 7
 };
 int chunk_attn_profile_start(void);
 int chunk_attn_profile_stop(void);

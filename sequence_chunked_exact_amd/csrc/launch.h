@@ -39,6 +39,24 @@ hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads,
 void prof_begin(int kernel, hipStream_t st);
 void prof_end(int kernel, hipStream_t st);
 
+// Projections around one chunk's attention. h is [batch][h_cap][d_model]
+// (rows h_off.. are the chunk's positions); wq is [d_model][hq*head_dim], wk and
+// wv [d_model][hkv*head_dim]; q, k, v, dq, dk, dv use the attention layout
+// (chunk rows at q_off in the q-side tensors, at start in k, v, dk, dv).
+struct ProjShape {
+  int batch, d_model, hq, hkv, head_dim;
+  int h_cap, h_off, q_cap, q_off, kv_cap, start, len;
+  int dtype;
+};
+// q, k, v rows of the chunk = H^(i) W (written in dtype).
+hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
+                           void* q, void* k, void* v, hipStream_t st);
+// dW += H^(i)^T G for G = dq, dk, dv rows of the chunk; dh rows of the chunk
+// = dq wq^T + dk wk^T + dv wv^T (float32).
+hipError_t launch_proj_bwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
+                           const float* dq, const float* dk, const float* dv, float* dwq, float* dwk, float* dwv,
+                           float* dh, hipStream_t st);
+
 // Fill n floats with zero (a kernel, so it is safe inside captured graphs).
 hipError_t launch_zero(float* p, size_t n, hipStream_t st);
 

@@ -129,6 +129,66 @@ def make_inputs(wl: Workload, seq_len: Optional[int] = None, keep_f64: bool = Tr
     return Inputs(wl, f64, raw)
 
 
+@dataclasses.dataclass(frozen=True)
+class LayerWorkload:
+    """An attention layer with its QKV projections: layer input H_in [B, T, d_model],
+    weights W_q [d_model, Hq*d], W_k/W_v [d_model, Hkv*d], incoming gradient dO."""
+    name: str
+    batch: int
+    seq_len: int
+    chunk: int
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str
+    seed: int
+
+    @property
+    def n_chunks(self) -> int:
+        return -(-self.seq_len // self.chunk)
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+LAYER_WORKLOADS = {
+    # LLaMA3-8B attention layer: d_model 4096, 32 query / 8 kv heads of 128
+    "8b_attn_layer": LayerWorkload("8b_attn_layer", 1, 16384, 1024, 4096, 32, 8, 128, "bf16", 7),
+}
+
+
+def make_layer_inputs(wl: LayerWorkload, seq_len: Optional[int] = None, keep_f64: bool = True) -> Inputs:
+    """Draw H_in ~ N(0, 1), weights ~ N(0, 1/d_model) (so Q, K, V entries are ~N(0, 1)),
+    and dO ~ N(0, 1/d), rounded to the storage type like make_inputs."""
+    T = wl.seq_len if seq_len is None else seq_len
+    B, Hq, Hkv, d, dm = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.d_model
+    rng = np.random.default_rng(wl.seed)
+    ws = 1.0 / math.sqrt(dm)
+    arrays = {
+        "h": _draw(rng, (B, T, dm), 1.0),
+        "wq": _draw(rng, (dm, Hq * d), ws),
+        "wk": _draw(rng, (dm, Hkv * d), ws),
+        "wv": _draw(rng, (dm, Hkv * d), ws),
+        "do": _draw(rng, (B, Hq, T, d), 1.0 / math.sqrt(d)),
+    }
+    raw, f64 = {}, {}
+    for name, a in arrays.items():
+        if wl.dtype == "bf16":
+            bits = round_to_bf16_bits(a)
+            raw[name] = bits
+            if keep_f64:
+                f64[name] = bf16_bits_to_f64(bits)
+        else:
+            f32 = a.astype(np.float32)
+            raw[name] = f32
+            if keep_f64:
+                f64[name] = f32.astype(np.float64)
+        arrays[name] = None
+    return Inputs(wl, f64, raw)
+
+
 def to_torch(raw: np.ndarray, device="cpu"):
     """Storage array -> torch tensor (bfloat16 for uint16 bits, float32 otherwise)."""
     import torch
