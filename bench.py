@@ -8,6 +8,13 @@ in HBM before timing starts. Prints one JSON line on stdout.
 
 FLOPs are causal only: 4*d per visible (query, key) pair and q head for the
 forward (S and PV) and 10*d for the backward (S recompute, dP, dV, dQ, dK).
+
+With --layer it measures instead the whole attention layer's chunked step on
+an LLaMA3-8B-shaped layer: per chunk the QKV projections then the chunk
+forward, then per chunk in descending order the chunk backward then the
+projection backward (weight gradients and the input gradient). That mode
+prints its own JSON line; its FLOPs add 2*d_model*(Hq+2*Hkv)*d per position
+for each of the projection forward, the weight gradients and dH_in.
 """
 from __future__ import annotations
 
@@ -89,6 +96,153 @@ def cpu_baseline(wl, inp_raw, n_heads=8):
             "seconds": dt, "gflops": rate / 1e9}
 
 
+def layer_cpu_baseline(wl, raw, rows=2048, n_heads=4):
+    """The float64 oracle on a bounded sample of the layer step, extrapolated by FLOPs:
+    the projections' forward and backward over the first `rows` positions, and the
+    attention forward + backward of `n_heads` query heads over all positions."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import projection as P
+    from sequence_chunked_exact_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    f = {n: (W.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)) for n, a in raw.items()}
+    Hq, Hkv, d, dm, T = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.d_model, wl.seq_len
+    G = Hq // Hkv
+    t0 = time.perf_counter()
+    h = f["h"][:, :rows]
+    q, k, v = P.qkv_forward(h, f["wq"], f["wk"], f["wv"], Hq, Hkv)
+    P.qkv_backward(h, f["wq"], f["wk"], f["wv"], q, k, v)
+    t_proj = time.perf_counter() - t0
+    t_attn = 0.0
+    for hh in range(n_heads):
+        kv = hh // G
+        qh, kh, vh = P.qkv_forward(f["h"][:1], f["wq"][:, hh * d:(hh + 1) * d], f["wk"][:, kv * d:(kv + 1) * d],
+                                   f["wv"][:, kv * d:(kv + 1) * d], 1, 1)
+        t1 = time.perf_counter()
+        A.forward(qh, kh, vh, wl.softmax_scale)
+        A.backward(qh, kh, vh, f["do"][:1, hh:hh + 1], wl.softmax_scale)
+        t_attn += time.perf_counter() - t1
+    proj_rate = 3 * 2 * rows * dm * (Hq + 2 * Hkv) * d / t_proj
+    pairs = T * (T + 1) // 2
+    attn_rate = 14 * d * pairs * n_heads / t_attn
+    Bt = f["h"].shape[0]
+    total_s = Bt * (3 * 2 * T * dm * (Hq + 2 * Hkv) * d / proj_rate + 14 * d * pairs * Hq / attn_rate)
+    return {"value": Bt * T / total_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle: projections forward+backward over the first {rows} of {T} positions "
+                      f"({t_proj:.1f} s) and attention forward+backward of {n_heads} of {Hq} query heads over "
+                      f"all positions ({t_attn:.1f} s), each extrapolated to the whole layer by FLOPs",
+            "seconds": t_proj + t_attn}
+
+
+def layer_main(args):
+    import numpy as np
+    import torch
+    from sequence_chunked_exact_amd import binding as B
+    from sequence_chunked_exact_amd import workloads as W
+
+    wl = W.LAYER_WORKLOADS["8b_attn_layer"]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {wl.name} inputs")
+    inp = W.make_layer_inputs(wl, keep_f64=False)
+    h, wq, wk, wv, do = (W.to_torch(inp.raw[n], dev) for n in ("h", "wq", "wk", "wv", "do"))
+    Bt, T, dm = h.shape
+    Hq, Hkv, d, C = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.chunk
+    sc = wl.softmax_scale
+    f32 = torch.float32
+    q = torch.zeros(Bt, Hq, T, d, dtype=h.dtype, device=dev)
+    k = torch.zeros(Bt, Hkv, T, d, dtype=h.dtype, device=dev)
+    v = torch.zeros_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty(Bt, Hq, T, dtype=f32, device=dev)
+    dq = torch.zeros(Bt, Hq, T, d, dtype=f32, device=dev)
+    dk = torch.zeros(Bt, Hkv, T, d, dtype=f32, device=dev)
+    dv = torch.zeros_like(dk)
+    dwq = torch.zeros(dm, Hq * d, dtype=f32, device=dev)
+    dwk = torch.zeros(dm, Hkv * d, dtype=f32, device=dev)
+    dwv = torch.zeros_like(dwk)
+    dh = torch.empty(Bt, T, dm, dtype=f32, device=dev)
+    starts = list(range(0, T, C))
+    ws = torch.empty(max(B.chunk_attn_workspace_size(B.make_desc(q, k, chunk_start=0, chunk_len=C), B.CA_OP_BWD),
+                         256), dtype=torch.uint8, device=dev)
+
+    def step():
+        for s in starts:
+            c = min(C, T - s)
+            B.qkv_proj_fwd(h, wq, wk, wv, q, k, v, chunk_start=s, chunk_len=c, q_row_offset=s)
+            B.chunk_attn_fwd(q, k, v, o, lse, chunk_start=s, chunk_len=c, q_row_offset=s, softmax_scale=sc)
+        for t_ in (dk, dv, dwq, dwk, dwv):
+            t_.zero_()
+        for s in reversed(starts):
+            c = min(C, T - s)
+            B.chunk_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, chunk_start=s, chunk_len=c, q_row_offset=s,
+                             softmax_scale=sc, workspace=ws)
+            B.qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, chunk_start=s, chunk_len=c,
+                           q_row_offset=s)
+
+    log(f"[bench] layer warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} layer steps")
+    B.profile_start()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    B.profile_stop()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = B.profile_read()
+    pairs = sum(causal_pairs(s, min(C, T - s)) for s in starts)
+    attn_flops = 14 * d * Hq * pairs
+    proj_flops = 3 * 2 * Bt * T * dm * (Hq + 2 * Hkv) * d
+    total = attn_flops + proj_flops
+    kernels = {n_: {"launches_per_step": c_ / args.steps, "ms_per_step": t_ / args.steps, "avg_us": t_ / c_ * 1e3}
+               for n_, (c_, t_) in prof.items() if c_}
+    log(f"[bench] {ms:.3f} ms/layer step; kernels " + json.dumps(kernels))
+    from sequence_chunked_exact_amd.profile_summary import read_traffic
+    n_proj, t_proj = prof["proj"]
+    proj_per_launch = proj_flops / (n_proj / args.steps)
+    proj_achieved = proj_per_launch / (t_proj / n_proj * 1e-3) / 1e12
+    out = {
+        "metric": "chunked attention layer (QKV projections + causal attn) fwd+bwd tokens/s, 1 GPU",
+        "value": Bt * T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "tflops": total / (ms * 1e-3) / 1e12,
+        "pct_bf16_peak": 100.0 * total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "config": {"workload": wl.name, "batch": Bt, "seq_len": T, "chunk": C, "d_model": dm, "n_q_heads": Hq,
+                   "n_kv_heads": Hkv, "head_dim": d, "softmax_scale": sc, "flops_per_step": total,
+                   "projection_flops_per_step": proj_flops},
+        "kernels": kernels,
+        "roofline": {"kernel": "proj", "bound": "mfma", "achieved": proj_achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": proj_achieved / PEAK_BF16_TFLOPS,
+                     "traffic": read_traffic(os.path.join(ROOT, "profiles", f"proj_{wl.name}.md"), "proj"),
+                     "avg_launch_us": t_proj / n_proj * 1e3, "flops_per_launch": proj_per_launch},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = layer_cpu_baseline(wl, inp.raw)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,11 +250,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="8b_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layer", action="store_true",
+                    help="measure the whole attention layer step (QKV projections + attention)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.layer:
+        return layer_main(args)
 
     import numpy as np
     import torch
@@ -180,7 +339,7 @@ def main():
         roof.update({"achieved": achieved, "frac": achieved / PEAK_BF16_TFLOPS,
                      "avg_launch_us": avg_s * 1e6, "flops_per_launch": per_launch_flops})
     from sequence_chunked_exact_amd.profile_summary import read_traffic
-    roof["traffic"] = read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{wl.name}.md"))
+    roof["traffic"] = read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{wl.name}.md"), dom)
     fwd_ms = kernels.get("fwd", {}).get("ms_per_step", 0.0)
     bwd_ms = sum(kernels.get(k_, {}).get("ms_per_step", 0.0) for k_ in ("delta", "dkdv", "dq", "zero"))
 

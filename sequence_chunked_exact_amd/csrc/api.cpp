@@ -1,6 +1,6 @@
 // C-ABI layer: argument checks (all before any device call), workspace sizing,
 // the SpaCO chunk selector and the sparse backward driver. Kernels live in
-// kernels.hip; this file only validates and enqueues.
+// attention.hip and projection.hip; this file only validates and enqueues.
 #include "chunk_attn.h"
 
 #include <hip/hip_runtime.h>
@@ -245,7 +245,7 @@ int prefix_grad_accumulate(float* acc, const float* src, int32_t batch, int32_t 
 }
 
 namespace {
-int check_proj(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset) {
+static int check_proj(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset) {
   int rc = check_desc(d, false);
   if (rc) return rc;
   if (d_model < 64 || d_model > 65536 || d_model % 64 != 0)
@@ -258,7 +258,7 @@ int check_proj(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, in
     return fail(CA_ERR_SHAPE, "projection tensors too large");
   return CA_OK;
 }
-ca::ProjShape proj_shape(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset) {
+static ca::ProjShape proj_shape(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset) {
   ca::ProjShape s;
   s.batch = d->batch;
   s.d_model = d_model;

@@ -9,17 +9,8 @@
 //   dS = P * (dO V^T - delta), delta_r = dO_r . O_r
 //   dQ = scale dS K,  dK += scale dS^T Q,  dV += P^T dO   (summed over the group)
 //
-// Matrix products run on v_mfma_f32_16x16x32_bf16 (bf16 storage) or
-// v_mfma_f32_16x16x4_f32 (float32 storage, eight of them per 32-deep step),
-// always accumulating in float32. For a 16x16 output tile, lane l (n = l % 16,
-// g = l / 16) holds rows 4g..4g+3 of column n. A and B operands give each lane
-// 8 contraction slots; lane l feeds row/column n. Two slot orders are used:
-//   contiguous: slot s <-> index 8g + s (operands read straight from memory)
-//   tile order: slot s <-> 4g + s for s < 4, 16 + 4g + (s - 4) for s >= 4,
-// the second being what a lane already holds from two stacked output tiles, so
-// P and dS feed the next product from registers with no data movement. Both
-// operands of a product always use the same order, which is all a k-reduction
-// needs.
+// Matrix products and their fragment slot orders follow the conventions in
+// device_common.h; products accumulate in float32.
 //
 // LDS holds every streamed tile once, row-major, with its 16-byte chunks
 // XOR-swizzled by row so that both access patterns are free of bank
@@ -39,272 +30,10 @@
 //  * softmax runs in the exp2 domain with the scale folded into one FMA, and the
 //    running maximum is only moved (rescaling O and the row sum) when a new
 //    score exceeds it by more than 2^8, which keeps every exponent <= 2^8.
-#include "launch.h"
-
-#include "chunk_attn.h"
-
-#include <math.h>
+#include "device_common.h"
 
 namespace ca {
 namespace {
-
-typedef __bf16 bf16;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kInf = __builtin_huge_valf();
-constexpr float kRescale = 8.f;  // lazy-rescale threshold, log2 units
-
-template <typename T>
-struct Elt;
-
-template <>
-struct Elt<bf16> {
-  using frag = bf16x8;  // a lane's 8 contraction slots
-  using vec = bf16x8;   // 16-byte memory vector
-  using vec8 = bf16x8;  // 8 elements
-  using quad = bf16x4;
-  static constexpr int VEC = 8;
-  static __device__ __forceinline__ void mma(f32x4& c, const frag& a, const frag& b) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Elt<float> {
-  using frag = f32x8;
-  using vec = f32x4;
-  using vec8 = f32x8;
-  using quad = f32x4;
-  static constexpr int VEC = 4;
-  static __device__ __forceinline__ void mma(f32x4& c, const frag& a, const frag& b) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
-  }
-};
-
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Two row-major [rows][D] LDS tile layouts; both keep the two read patterns
-// used here free of bank conflicts: 16 lanes reading one 16-byte chunk
-// column from 16 consecutive rows (row-major fragments), and the transposing
-// read of 16 rows x 32 bytes, which lands on every bank exactly twice (its
-// minimum: 512 bytes in two passes).
-//
-// PadLay: rows padded by 32 bytes (row stride RS = D + 32 / sizeof(T)
-// elements, an odd multiple of 8 banks for every head size here), so 16
-// consecutive rows start in 16 different bank groups. A lane's address is a
-// loop-invariant base plus a constant offset. Used for tiles written from
-// registers.
-template <typename T, int D>
-struct PadLay {
-  static constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
-  static constexpr int RS = D + 2 * EPC;      // row stride in elements
-  static_assert(((RS * sizeof(T) / 4 / 8) & 1) == 1, "row stride must be an odd multiple of 8 banks");
-  static __device__ __forceinline__ int off(int r, int c) { return r * RS + c; }
-};
-
-// SwzLay: unpadded rows (stride D), the 16-byte chunk c of row r stored at
-// chunk position c ^ swz(r). The map (r mod 16, with bit 3 ^= bit 0 and bit
-// 2 ^= bit 3) was picked by measuring gfx950's LDS bank-conflict counter over
-// a family of candidate maps; it is the simplest one under which both read
-// patterns run conflict-free. Used for tiles filled by direct global->LDS
-// loads, which write each wave's 64 x 16 bytes contiguously.
-template <typename T, int D>
-struct SwzLay {
-  static constexpr int EPC = 16 / sizeof(T);
-  static constexpr int CH = D / EPC;  // chunks per row
-  static constexpr int RS = D;
-  static __device__ __forceinline__ int swz(int r) {
-    const int x = (r ^ ((r & 1) << 3) ^ (((r >> 3) & 1) << 2)) & 15;
-    return x & (CH - 1);
-  }
-  static __device__ __forceinline__ int off(int r, int c) {
-    return r * D + (((c / EPC) ^ swz(r)) * EPC) + (c % EPC);
-  }
-};
-
-// 8 consecutive elements of row r from column c (c % 8 == 0), contiguous order.
-template <class Lt>
-__device__ __forceinline__ bf16x8 ld8s(const bf16* t, int r, int c) {
-  return *(const bf16x8*)(t + Lt::off(r, c));
-}
-template <class Lt>
-__device__ __forceinline__ f32x8 ld8s(const float* t, int r, int c) {
-  const f32x4 a = *(const f32x4*)(t + Lt::off(r, c));
-  const f32x4 b = *(const f32x4*)(t + Lt::off(r, c + 4));
-  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// This lane's {t[rb + k][c0 + n] : k = 0..3} (n = lane % 16; rb a multiple of 4,
-// the same for the 16 lanes of a group). bf16 uses the transposing LDS read:
-// lane j of a group points at row rb + j/4, columns c0 + 4(j%4) .. +3, and the
-// hardware hands lane i element k of lane 4k + i/4's four.
-template <class Lt>
-__device__ __forceinline__ bf16x4 ldT4(const bf16* t, int rb, int c0, int lane) {
-  const int j = lane & 15;
-  const bf16* p = t + Lt::off(rb + (j >> 2), c0 + 4 * (j & 3));
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<bf16*>(p)));
-  return __builtin_bit_cast(bf16x4, v);
-}
-template <class Lt>
-__device__ __forceinline__ f32x4 ldT4(const float* t, int rb, int c0, int lane) {
-  const int n = lane & 15;
-  f32x4 v;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = t[Lt::off(rb + k, c0 + n)];
-  return v;
-}
-// Fragment of t[kbase + tile-order slots][c0 + n] (operand contracted over rows).
-template <class Lt>
-__device__ __forceinline__ bf16x8 ldT8(const bf16* t, int kbase, int c0, int lane) {
-  const int g = lane >> 4;
-  const bf16x4 a = ldT4<Lt>(t, kbase + 4 * g, c0, lane), b = ldT4<Lt>(t, kbase + 16 + 4 * g, c0, lane);
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-template <class Lt>
-__device__ __forceinline__ f32x8 ldT8(const float* t, int kbase, int c0, int lane) {
-  const int g = lane >> 4;
-  const f32x4 a = ldT4<Lt>(t, kbase + 4 * g, c0, lane), b = ldT4<Lt>(t, kbase + 16 + 4 * g, c0, lane);
-  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// 8 consecutive elements from global memory.
-__device__ __forceinline__ bf16x8 ldg8(const bf16* p) { return *(const bf16x8*)p; }
-__device__ __forceinline__ f32x8 ldg8(const float* p) {
-  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// A fragment of ones: as the A operand of a product with P^T it gives every
-// output lane the sum of P over the 32 contracted rows.
-template <typename T>
-__device__ __forceinline__ typename Elt<T>::frag ones_frag() {
-  typename Elt<T>::frag f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = (T)1.f;
-  return f;
-}
-
-// Two stacked output tiles' registers -> fragment in tile slot order.
-template <typename T>
-__device__ __forceinline__ typename Elt<T>::frag pack44(const f32x4& lo, const f32x4& hi) {
-  typename Elt<T>::frag f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[i] = (T)lo[i];
-    f[4 + i] = (T)hi[i];
-  }
-  return f;
-}
-
-template <typename T>
-__device__ __forceinline__ typename Elt<T>::frag negate(const typename Elt<T>::frag& f) {
-  typename Elt<T>::frag r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = -f[i];
-  return r;
-}
-
-template <typename T>
-__device__ __forceinline__ void store4(T* dst, const f32x4& x, float mul) {
-  typename Elt<T>::quad v;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = (T)(x[i] * mul);
-  *(typename Elt<T>::quad*)dst = v;
-}
-
-// Maximum / sum over the 4 lanes l, l^16, l^32, l^48 (the 4 row groups of one
-// output column).
-__device__ __forceinline__ float max4(float m) {
-  m = fmaxf(m, __shfl_xor(m, 16));
-  return fmaxf(m, __shfl_xor(m, 32));
-}
-
-// Workgroups go to the 8 XCDs round-robin by linear id, and each XCD has its
-// own L2. This maps the linear id to a logical work index so that every XCD
-// receives one contiguous range of the logical order (heads outermost): the
-// workgroups streaming the same K/V (forward, dQ) or the same Q/dO (dK/dV)
-// then share one L2. Within a range the order is ascending, i.e. each XCD
-// starts with the first (longest) tiles of its heads.
-__device__ __forceinline__ int xcd_order(int id, int n) {
-  constexpr int X = 8;
-  const int per = n / X;
-  return id < per * X ? (id % X) * per + id / X : id;
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Stream rows [row0, row0 + ROWS) of a row-major [*, D] head into a SwzLay
-// LDS tile with direct global->LDS loads, shared by NW waves: each wave
-// instruction fills 64 consecutive 16-byte LDS slots, so lane l fetches the
-// global chunk that belongs in its slot (the swizzle is applied on the global
-// side, and each instruction still reads whole rows). Rows at or beyond
-// `limit` (>= 1) re-read row limit-1; every consumer gives such rows zero
-// weight (keys past the prefix are causally masked).
-template <typename T, int ROWS, int D, int NW>
-__device__ __forceinline__ void stage_tile(T* lds, const T* head, int row0, int limit, int wave, int lane) {
-  using Lt = SwzLay<T, D>;
-  constexpr int CH = Lt::CH, RPI = 64 / CH, PER_WAVE = ROWS / NW;
-  static_assert(CH <= 64 && PER_WAVE % RPI == 0, "tile rows per wave must fill whole instructions");
-#if defined(__HIP_DEVICE_COMPILE__)  // the LDS-loading builtin exists only in the device pass
-  const int rl = lane / CH, slot = lane % CH;
-#pragma unroll
-  for (int i = 0; i < PER_WAVE / RPI; ++i) {
-    const int rb = wave * PER_WAVE + i * RPI;  // wave-uniform first row of this instruction
-    const int r = rb + rl;
-    const int c = slot ^ Lt::swz(r);
-    const T* src = head + (size_t)min(row0 + r, limit - 1) * D + c * Lt::EPC;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + rb * D), 16, 0, 0);
-  }
-#endif
-}
-
-// A [ROWS][D] tile staged through registers: thread tid fetches R rows of
-// one 16-byte column vector and later writes them into a PadLay LDS tile
-// (threads beyond the tile's ROWS * D / VEC vectors fetch a duplicate and
-// store nothing). Rows at or beyond `limit` (>= 1) re-read row limit-1;
-// every consumer gives such rows zero weight (keys past the prefix are
-// causally masked, query rows past the chunk get LSE = +inf). Plain loads
-// into registers let the next tile's fetch overlap the current tile's math
-// without any LDS ordering.
-template <typename T, int ROWS, int D, int NT>
-struct RegTile {
-  using V = typename Elt<T>::vec;
-  static constexpr int VEC = Elt<T>::VEC;
-  static constexpr int NDV = D / VEC;      // column vectors per row
-  static constexpr int GROUPS = NT / NDV;  // row groups
-  static constexpr bool SPARE = GROUPS > ROWS;
-  static constexpr int R = SPARE ? 1 : ROWS / GROUPS;  // rows per thread
-  static_assert(NT % NDV == 0 && (SPARE || ROWS % GROUPS == 0), "tile/thread shape");
-  V r[R];
-
-  __device__ __forceinline__ void load(const T* head, int row0, int limit, int tid) {
-    const int dv = tid % NDV, grp = SPARE ? min(tid / NDV, ROWS - 1) : tid / NDV;
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-      r[i] = *(const V*)(head + (size_t)min(row0 + grp * R + i, limit - 1) * D + dv * VEC);
-  }
-  __device__ __forceinline__ void store(T* lds, int tid) const {
-    const int dv = tid % NDV, grp = tid / NDV;
-    if (SPARE && grp >= ROWS) return;
-#pragma unroll
-    for (int i = 0; i < R; ++i) *(V*)(lds + PadLay<T, D>::off(grp * R + i, dv * VEC)) = r[i];
-  }
-};
-
-// Wait for every load this wave has in flight. Called once before a main
-// loop: wait counting in the compiler cannot tell the first iteration from
-// the others, so a register loaded before the loop and first read inside it
-// would otherwise wait, in every iteration, on the in-order load counter for
-// the next tile's prefetch as well.
-__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ----------------------------------------------------------------------------
 // Forward. 1-D grid over (batch, q head, query tile). A workgroup has two
@@ -1012,215 +741,6 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
     ((f32x4*)p)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (blockIdx.x == 0 && threadIdx.x < n % 4) p[n4 * 4 + threadIdx.x] = 0.f;
 }
-
-// ----------------------------------------------------------------------------
-// Projection GEMMs around the attention of a chunk (the QKV projections and
-// their weight and input gradients): C = A B, A [M][K], B [K][N], float32
-// accumulation on the matrix cores. Operands and output are read through
-// strided views, so that per-head [heads][rows][d] tensors take part as
-// [rows][heads*d] matrices without copies. A 4-wave workgroup owns a 128x128
-// output tile (2x2 waves of 64x64); 64-deep k slices are staged through
-// registers (converted to the compute type) into double-buffered LDS. An
-// operand whose stored layout has k along its rows ("mn-contiguous") is read
-// through the transposing path, the other with two 8-byte reads per lane, both
-// in the tile slot order.
-// ----------------------------------------------------------------------------
-struct MatView {
-  const void* p;  // element (r, c) of batch b at p + b*bs + r*rs + (c / hd)*hs + c % hd
-  long long rs, hs, bs;
-  int hd;
-};
-__device__ __forceinline__ long long mv_index(const MatView& v, int b, int r, int c) {
-  return (long long)b * v.bs + (long long)r * v.rs + (long long)(c / v.hd) * v.hs + (c % v.hd);
-}
-
-struct GemmParams {
-  MatView a, b, c;
-  int M, N, K;
-  float beta;  // float32 output: c = acc + beta * c (beta 0 overwrites)
-};
-
-// 8 source elements at (r, c..c+7) converted to T (zero if `zero`).
-template <typename T, typename S>
-__device__ __forceinline__ typename Elt<T>::vec8 load8_as(const S* p, bool zero);
-template <>
-__device__ __forceinline__ bf16x8 load8_as<bf16, bf16>(const bf16* p, bool zero) {
-  return zero ? bf16x8{} : *(const bf16x8*)p;
-}
-template <>
-__device__ __forceinline__ bf16x8 load8_as<bf16, float>(const float* p, bool zero) {
-  bf16x8 r{};
-  if (!zero) {
-    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r[i] = (bf16)a[i];
-      r[4 + i] = (bf16)b[i];
-    }
-  }
-  return r;
-}
-template <>
-__device__ __forceinline__ f32x8 load8_as<float, float>(const float* p, bool zero) {
-  f32x8 r{};
-  if (!zero) {
-    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-    r = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  }
-  return r;
-}
-template <typename T>
-__device__ __forceinline__ void store8(T* lds, const typename Elt<T>::vec8& v);
-template <>
-__device__ __forceinline__ void store8<bf16>(bf16* lds, const bf16x8& v) {
-  *(bf16x8*)lds = v;
-}
-template <>
-__device__ __forceinline__ void store8<float>(float* lds, const f32x8& v) {
-  *(f32x4*)lds = f32x4{v[0], v[1], v[2], v[3]};
-  *(f32x4*)(lds + 4) = f32x4{v[4], v[5], v[6], v[7]};
-}
-
-// Fragment of row r, columns kbase + tile-order slots (4g + s, 16 + 4g + s - 4).
-template <class Lt>
-__device__ __forceinline__ bf16x8 ld8t(const bf16* t, int r, int kbase, int g) {
-  const bf16x4 a = *(const bf16x4*)(t + Lt::off(r, kbase + 4 * g));
-  const bf16x4 b = *(const bf16x4*)(t + Lt::off(r, kbase + 16 + 4 * g));
-  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-template <class Lt>
-__device__ __forceinline__ f32x8 ld8t(const float* t, int r, int kbase, int g) {
-  const f32x4 a = *(const f32x4*)(t + Lt::off(r, kbase + 4 * g));
-  const f32x4 b = *(const f32x4*)(t + Lt::off(r, kbase + 16 + 4 * g));
-  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
-
-// One 64-deep k slice of an operand, staged through registers. MN: the stored
-// matrix has k along its rows ([64][128] tile), otherwise along its columns
-// ([128][64] tile). Rows or columns past the matrix re-read its last one
-// (those outputs are never stored); k past K reads zero.
-template <typename T, typename S, bool MN>
-struct GemmStage {
-  static constexpr int ROWS = MN ? 64 : 128, COLS = MN ? 128 : 64;
-  static constexpr int VPR = COLS / 8, NV = ROWS * VPR / 256;  // 8-element vectors
-  using Lt = PadLay<T, COLS>;
-  typename Elt<T>::vec8 r[NV];
-  __device__ __forceinline__ void load(const MatView& v, int b, int mn0, int k0, int MNext, int K, int tid) {
-    const S* base = (const S*)v.p;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int vi = tid + i * 256, row = vi / VPR, col = (vi % VPR) * 8;
-      int rr, cc;
-      bool zero;
-      if (MN) {  // rows: k, columns: m or n
-        rr = k0 + row;
-        cc = min(mn0 + col, MNext - 8);
-        zero = rr >= K;
-        rr = min(rr, K - 1);
-      } else {  // rows: m or n, columns: k
-        rr = min(mn0 + row, MNext - 1);
-        cc = k0 + col;
-        zero = cc >= K;
-        cc = min(cc, K - 8);
-      }
-      r[i] = load8_as<T, S>(base + mv_index(v, b, rr, cc), zero);
-    }
-  }
-  __device__ __forceinline__ void store(T* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int vi = tid + i * 256;
-      store8<T>(lds + Lt::off(vi / VPR, (vi % VPR) * 8), r[i]);
-    }
-  }
-};
-
-template <typename T, typename SA, typename SB, bool A_MN, bool B_MN, bool OUT_F32>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
-  using E = Elt<T>;
-  using frag = typename E::frag;
-  using StA = GemmStage<T, SA, A_MN>;
-  using StB = GemmStage<T, SB, B_MN>;
-  constexpr int TA = StA::ROWS * StA::Lt::RS, TB = StB::ROWS * StB::Lt::RS;
-  __shared__ __attribute__((aligned(16))) T As[2][TA];
-  __shared__ __attribute__((aligned(16))) T Bs[2][TB];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128, b = blockIdx.z;
-  const int nk = (p.K + 63) / 64;
-
-  StA sa;
-  StB sb;
-  sa.load(p.a, b, m0, 0, p.M, p.K, tid);
-  sb.load(p.b, b, n0, 0, p.N, p.K, tid);
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  sa.store(As[0], tid);
-  sb.store(Bs[0], tid);
-  wait_loads();
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      sa.load(p.a, b, m0, (kt + 1) * 64, p.M, p.K, tid);
-      sb.load(p.b, b, n0, (kt + 1) * 64, p.N, p.K, tid);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      frag af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int mr = wm * 64 + i * 16;
-        af[i] = A_MN ? ldT8<typename StA::Lt>(As[cur], ks * 32, mr, lane)
-                     : ld8t<typename StA::Lt>(As[cur], mr + n, ks * 32, g);
-        const int nr = wn * 64 + i * 16;
-        bfr[i] = B_MN ? ldT8<typename StB::Lt>(Bs[cur], ks * 32, nr, lane)
-                      : ld8t<typename StB::Lt>(Bs[cur], nr + n, ks * 32, g);
-      }
-      // C^T tiles: the n-side fragment is the A operand, so a lane ends up
-      // holding 4 consecutive n of one m row (rows 4g..4g+3 of C^T).
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) E::mma(acc[i][j], bfr[j], af[i]);
-    }
-    if (more) {
-      sa.store(As[cur ^ 1], tid);
-      sb.store(Bs[cur ^ 1], tid);
-    }
-    __syncthreads();
-  }
-
-  // acc[i][j] holds C[m][n .. n+3] for m = m0 + wm*64 + i*16 + (lane % 16),
-  // n = n0 + wn*64 + j*16 + 4g (C^T tile rows 4g..4g+3); N is a multiple of 4
-  // and a head split never cuts such a group.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 64 + i * 16 + n;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nb = n0 + wn * 64 + j * 16 + 4 * g;
-      if (nb >= p.N) continue;
-      const long long idx = mv_index(p.c, b, m, nb);
-      if (OUT_F32) {
-        f32x4* c = (f32x4*)((float*)p.c.p + idx);
-        *c = p.beta == 0.f ? acc[i][j] : acc[i][j] + p.beta * *c;
-      } else {
-        store4<T>((T*)p.c.p + idx, acc[i][j], 1.f);
-      }
-    }
-  }
-}
-
 // ----------------------------------------------------------------------------
 // Tile configurations per (type, head_dim).
 // ----------------------------------------------------------------------------
@@ -1340,92 +860,6 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t st) {
   hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, st, p, n);
   prof_end(CA_KERNEL_ZERO, st);
   return hipGetLastError();
-}
-
-
-namespace {
-template <typename T, typename SA, typename SB, bool A_MN, bool B_MN, bool OUT_F32>
-hipError_t gemm_launch(const GemmParams& p, int batch, hipStream_t st) {
-  prof_begin(CA_KERNEL_PROJ, st);
-  hipLaunchKernelGGL((gemm_kernel<T, SA, SB, A_MN, B_MN, OUT_F32>), dim3((p.N + 127) / 128, (p.M + 127) / 128, batch),
-                     dim3(256), 0, st, p);
-  prof_end(CA_KERNEL_PROJ, st);
-  return hipGetLastError();
-}
-constexpr int kNoSplit = 1 << 30;
-
-template <typename T>
-hipError_t proj_fwd_impl(const ProjShape& s, const void* h, const void* const w[3], void* const out[3],
-                         hipStream_t st) {
-  const int d = s.head_dim;
-  for (int t = 0; t < 3; ++t) {
-    const bool isq = t == 0;
-    const int H = isq ? s.hq : s.hkv, cap = isq ? s.q_cap : s.kv_cap, off = isq ? s.q_off : s.start;
-    GemmParams p{};
-    p.M = s.len;
-    p.N = H * d;
-    p.K = s.d_model;
-    p.a = {(const T*)h + (size_t)s.h_off * s.d_model, s.d_model, 0, (long long)s.h_cap * s.d_model, kNoSplit};
-    p.b = {w[t], (long long)H * d, 0, 0, kNoSplit};
-    p.c = {(T*)out[t] + (size_t)off * d, d, (long long)cap * d, (long long)H * cap * d, d};
-    hipError_t e = gemm_launch<T, T, T, false, true, false>(p, s.batch, st);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-template <typename T>
-hipError_t proj_bwd_impl(const ProjShape& s, const void* h, const void* const w[3], const float* const g[3],
-                         float* const dw[3], float* dh, hipStream_t st) {
-  const int d = s.head_dim;
-  for (int t = 0; t < 3; ++t) {
-    const bool isq = t == 0;
-    const int H = isq ? s.hq : s.hkv, cap = isq ? s.q_cap : s.kv_cap, off = isq ? s.q_off : s.start;
-    // dW += H_in^T G over the chunk's rows (one launch per batch entry: the
-    // batch is summed into the same weight gradient).
-    for (int b = 0; b < s.batch; ++b) {
-      GemmParams p{};
-      p.M = s.d_model;
-      p.N = H * d;
-      p.K = s.len;
-      p.a = {(const T*)h + ((size_t)b * s.h_cap + s.h_off) * s.d_model, s.d_model, 0, 0, kNoSplit};
-      p.b = {g[t] + ((size_t)b * H * cap + off) * d, d, (long long)cap * d, 0, d};
-      p.c = {dw[t], (long long)H * d, 0, 0, kNoSplit};
-      p.beta = 1.f;
-      hipError_t e = gemm_launch<T, T, float, true, true, true>(p, 1, st);
-      if (e != hipSuccess) return e;
-    }
-    // dH (+)= G W^T
-    GemmParams p{};
-    p.M = s.len;
-    p.N = s.d_model;
-    p.K = H * d;
-    p.a = {g[t] + (size_t)off * d, d, (long long)cap * d, (long long)H * cap * d, d};
-    p.b = {w[t], (long long)H * d, 0, 0, kNoSplit};
-    p.c = {dh + (size_t)s.h_off * s.d_model, s.d_model, 0, (long long)s.h_cap * s.d_model, kNoSplit};
-    p.beta = t == 0 ? 0.f : 1.f;
-    hipError_t e = gemm_launch<T, float, T, false, false, true>(p, s.batch, st);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-}  // namespace
-
-hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
-                           void* q, void* k, void* v, hipStream_t st) {
-  const void* const w[3] = {wq, wk, wv};
-  void* const out[3] = {q, k, v};
-  return s.dtype == CA_BF16 ? proj_fwd_impl<bf16>(s, h, w, out, st) : proj_fwd_impl<float>(s, h, w, out, st);
-}
-
-hipError_t launch_proj_bwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
-                           const float* dq, const float* dk, const float* dv, float* dwq, float* dwk, float* dwv,
-                           float* dh, hipStream_t st) {
-  const void* const w[3] = {wq, wk, wv};
-  const float* const g[3] = {dq, dk, dv};
-  float* const dw[3] = {dwq, dwk, dwv};
-  return s.dtype == CA_BF16 ? proj_bwd_impl<bf16>(s, h, w, g, dw, dh, st)
-                            : proj_bwd_impl<float>(s, h, w, g, dw, dh, st);
 }
 
 }  // namespace ca

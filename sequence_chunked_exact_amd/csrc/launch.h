@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI layer (api.cpp) and the HIP kernels
-// (kernels.hip). Arguments are already validated when these are called.
+// (attention.hip, projection.hip). Arguments are already validated when these are called.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,0 +1,297 @@
+// Projection GEMMs around the attention of one chunk for gfx950 (CDNA4): the
+// QKV projections and their weight and input gradients: C = A B, A [M][K], B [K][N], float32
+// accumulation on the matrix cores. Operands and output are read through
+// strided views, so that per-head [heads][rows][d] tensors take part as
+// [rows][heads*d] matrices without copies. A 4-wave workgroup owns a 128x128
+// output tile (2x2 waves of 64x64); 64-deep k slices are staged through
+// registers (converted to the compute type) into double-buffered LDS. An
+// operand whose stored layout has k along its rows ("mn-contiguous") is read
+// through the transposing path, the other with two 8-byte reads per lane, both
+// in the tile slot order.
+
+#include "device_common.h"
+
+namespace ca {
+namespace {
+
+struct MatView {
+  const void* p;  // element (r, c) of batch b at p + b*bs + r*rs + (c / hd)*hs + c % hd
+  long long rs, hs, bs;
+  int hd;
+};
+__device__ __forceinline__ long long mv_index(const MatView& v, int b, int r, int c) {
+  return (long long)b * v.bs + (long long)r * v.rs + (long long)(c / v.hd) * v.hs + (c % v.hd);
+}
+
+struct GemmParams {
+  MatView a, b, c;
+  int M, N, K;
+  float beta;  // float32 output: c = acc + beta * c (beta 0 overwrites)
+};
+
+// 8 source elements at (r, c..c+7) converted to T (zero if `zero`).
+template <typename T, typename S>
+__device__ __forceinline__ typename Elt<T>::vec8 load8_as(const S* p, bool zero);
+template <>
+__device__ __forceinline__ bf16x8 load8_as<bf16, bf16>(const bf16* p, bool zero) {
+  return zero ? bf16x8{} : *(const bf16x8*)p;
+}
+template <>
+__device__ __forceinline__ bf16x8 load8_as<bf16, float>(const float* p, bool zero) {
+  bf16x8 r{};
+  if (!zero) {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = (bf16)a[i];
+      r[4 + i] = (bf16)b[i];
+    }
+  }
+  return r;
+}
+template <>
+__device__ __forceinline__ f32x8 load8_as<float, float>(const float* p, bool zero) {
+  f32x8 r{};
+  if (!zero) {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+    r = f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* lds, const typename Elt<T>::vec8& v);
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16* lds, const bf16x8& v) {
+  *(bf16x8*)lds = v;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* lds, const f32x8& v) {
+  *(f32x4*)lds = f32x4{v[0], v[1], v[2], v[3]};
+  *(f32x4*)(lds + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// Fragment of row r, columns kbase + tile-order slots (4g + s, 16 + 4g + s - 4).
+template <class Lt>
+__device__ __forceinline__ bf16x8 ld8t(const bf16* t, int r, int kbase, int g) {
+  const bf16x4 a = *(const bf16x4*)(t + Lt::off(r, kbase + 4 * g));
+  const bf16x4 b = *(const bf16x4*)(t + Lt::off(r, kbase + 16 + 4 * g));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <class Lt>
+__device__ __forceinline__ f32x8 ld8t(const float* t, int r, int kbase, int g) {
+  const f32x4 a = *(const f32x4*)(t + Lt::off(r, kbase + 4 * g));
+  const f32x4 b = *(const f32x4*)(t + Lt::off(r, kbase + 16 + 4 * g));
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// One 64-deep k slice of an operand, staged through registers. MN: the stored
+// matrix has k along its rows ([64][128] tile), otherwise along its columns
+// ([128][64] tile). Rows or columns past the matrix re-read its last one
+// (those outputs are never stored); k past K reads zero.
+template <typename T, typename S, bool MN>
+struct GemmStage {
+  static constexpr int ROWS = MN ? 64 : 128, COLS = MN ? 128 : 64;
+  static constexpr int VPR = COLS / 8, NV = ROWS * VPR / 256;  // 8-element vectors
+  using Lt = PadLay<T, COLS>;
+  typename Elt<T>::vec8 r[NV];
+  __device__ __forceinline__ void load(const MatView& v, int b, int mn0, int k0, int MNext, int K, int tid) {
+    const S* base = (const S*)v.p;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = tid + i * 256, row = vi / VPR, col = (vi % VPR) * 8;
+      int rr, cc;
+      bool zero;
+      if (MN) {  // rows: k, columns: m or n
+        rr = k0 + row;
+        cc = min(mn0 + col, MNext - 8);
+        zero = rr >= K;
+        rr = min(rr, K - 1);
+      } else {  // rows: m or n, columns: k
+        rr = min(mn0 + row, MNext - 1);
+        cc = k0 + col;
+        zero = cc >= K;
+        cc = min(cc, K - 8);
+      }
+      r[i] = load8_as<T, S>(base + mv_index(v, b, rr, cc), zero);
+    }
+  }
+  __device__ __forceinline__ void store(T* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = tid + i * 256;
+      store8<T>(lds + Lt::off(vi / VPR, (vi % VPR) * 8), r[i]);
+    }
+  }
+};
+
+template <typename T, typename SA, typename SB, bool A_MN, bool B_MN, bool OUT_F32>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
+  using E = Elt<T>;
+  using frag = typename E::frag;
+  using StA = GemmStage<T, SA, A_MN>;
+  using StB = GemmStage<T, SB, B_MN>;
+  constexpr int TA = StA::ROWS * StA::Lt::RS, TB = StB::ROWS * StB::Lt::RS;
+  __shared__ __attribute__((aligned(16))) T As[2][TA];
+  __shared__ __attribute__((aligned(16))) T Bs[2][TB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128, b = blockIdx.z;
+  const int nk = (p.K + 63) / 64;
+
+  StA sa;
+  StB sb;
+  sa.load(p.a, b, m0, 0, p.M, p.K, tid);
+  sb.load(p.b, b, n0, 0, p.N, p.K, tid);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  sa.store(As[0], tid);
+  sb.store(Bs[0], tid);
+  wait_loads();
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      sa.load(p.a, b, m0, (kt + 1) * 64, p.M, p.K, tid);
+      sb.load(p.b, b, n0, (kt + 1) * 64, p.N, p.K, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      frag af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mr = wm * 64 + i * 16;
+        af[i] = A_MN ? ldT8<typename StA::Lt>(As[cur], ks * 32, mr, lane)
+                     : ld8t<typename StA::Lt>(As[cur], mr + n, ks * 32, g);
+        const int nr = wn * 64 + i * 16;
+        bfr[i] = B_MN ? ldT8<typename StB::Lt>(Bs[cur], ks * 32, nr, lane)
+                      : ld8t<typename StB::Lt>(Bs[cur], nr + n, ks * 32, g);
+      }
+      // C^T tiles: the n-side fragment is the A operand, so a lane ends up
+      // holding 4 consecutive n of one m row (rows 4g..4g+3 of C^T).
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) E::mma(acc[i][j], bfr[j], af[i]);
+    }
+    if (more) {
+      sa.store(As[cur ^ 1], tid);
+      sb.store(Bs[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // acc[i][j] holds C[m][n .. n+3] for m = m0 + wm*64 + i*16 + (lane % 16),
+  // n = n0 + wn*64 + j*16 + 4g (C^T tile rows 4g..4g+3); N is a multiple of 4
+  // and a head split never cuts such a group.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 64 + i * 16 + n;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nb = n0 + wn * 64 + j * 16 + 4 * g;
+      if (nb >= p.N) continue;
+      const long long idx = mv_index(p.c, b, m, nb);
+      if (OUT_F32) {
+        f32x4* c = (f32x4*)((float*)p.c.p + idx);
+        *c = p.beta == 0.f ? acc[i][j] : acc[i][j] + p.beta * *c;
+      } else {
+        store4<T>((T*)p.c.p + idx, acc[i][j], 1.f);
+      }
+    }
+  }
+}
+
+template <typename T, typename SA, typename SB, bool A_MN, bool B_MN, bool OUT_F32>
+hipError_t gemm_launch(const GemmParams& p, int batch, hipStream_t st) {
+  prof_begin(CA_KERNEL_PROJ, st);
+  hipLaunchKernelGGL((gemm_kernel<T, SA, SB, A_MN, B_MN, OUT_F32>), dim3((p.N + 127) / 128, (p.M + 127) / 128, batch),
+                     dim3(256), 0, st, p);
+  prof_end(CA_KERNEL_PROJ, st);
+  return hipGetLastError();
+}
+constexpr int kNoSplit = 1 << 30;
+
+template <typename T>
+hipError_t proj_fwd_impl(const ProjShape& s, const void* h, const void* const w[3], void* const out[3],
+                         hipStream_t st) {
+  const int d = s.head_dim;
+  for (int t = 0; t < 3; ++t) {
+    const bool isq = t == 0;
+    const int H = isq ? s.hq : s.hkv, cap = isq ? s.q_cap : s.kv_cap, off = isq ? s.q_off : s.start;
+    GemmParams p{};
+    p.M = s.len;
+    p.N = H * d;
+    p.K = s.d_model;
+    p.a = {(const T*)h + (size_t)s.h_off * s.d_model, s.d_model, 0, (long long)s.h_cap * s.d_model, kNoSplit};
+    p.b = {w[t], (long long)H * d, 0, 0, kNoSplit};
+    p.c = {(T*)out[t] + (size_t)off * d, d, (long long)cap * d, (long long)H * cap * d, d};
+    hipError_t e = gemm_launch<T, T, T, false, true, false>(p, s.batch, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename T>
+hipError_t proj_bwd_impl(const ProjShape& s, const void* h, const void* const w[3], const float* const g[3],
+                         float* const dw[3], float* dh, hipStream_t st) {
+  const int d = s.head_dim;
+  for (int t = 0; t < 3; ++t) {
+    const bool isq = t == 0;
+    const int H = isq ? s.hq : s.hkv, cap = isq ? s.q_cap : s.kv_cap, off = isq ? s.q_off : s.start;
+    // dW += H_in^T G over the chunk's rows (one launch per batch entry: the
+    // batch is summed into the same weight gradient).
+    for (int b = 0; b < s.batch; ++b) {
+      GemmParams p{};
+      p.M = s.d_model;
+      p.N = H * d;
+      p.K = s.len;
+      p.a = {(const T*)h + ((size_t)b * s.h_cap + s.h_off) * s.d_model, s.d_model, 0, 0, kNoSplit};
+      p.b = {g[t] + ((size_t)b * H * cap + off) * d, d, (long long)cap * d, 0, d};
+      p.c = {dw[t], (long long)H * d, 0, 0, kNoSplit};
+      p.beta = 1.f;
+      hipError_t e = gemm_launch<T, T, float, true, true, true>(p, 1, st);
+      if (e != hipSuccess) return e;
+    }
+    // dH (+)= G W^T
+    GemmParams p{};
+    p.M = s.len;
+    p.N = s.d_model;
+    p.K = H * d;
+    p.a = {g[t] + (size_t)off * d, d, (long long)cap * d, (long long)H * cap * d, d};
+    p.b = {w[t], (long long)H * d, 0, 0, kNoSplit};
+    p.c = {dh + (size_t)s.h_off * s.d_model, s.d_model, 0, (long long)s.h_cap * s.d_model, kNoSplit};
+    p.beta = t == 0 ? 0.f : 1.f;
+    hipError_t e = gemm_launch<T, float, T, false, false, true>(p, s.batch, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
+                           void* q, void* k, void* v, hipStream_t st) {
+  const void* const w[3] = {wq, wk, wv};
+  void* const out[3] = {q, k, v};
+  return s.dtype == CA_BF16 ? proj_fwd_impl<bf16>(s, h, w, out, st) : proj_fwd_impl<float>(s, h, w, out, st);
+}
+
+hipError_t launch_proj_bwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
+                           const float* dq, const float* dk, const float* dv, float* dwq, float* dwk, float* dwv,
+                           float* dh, hipStream_t st) {
+  const void* const w[3] = {wq, wk, wv};
+  const float* const g[3] = {dq, dk, dv};
+  float* const dw[3] = {dwq, dwk, dwv};
+  return s.dtype == CA_BF16 ? proj_bwd_impl<bf16>(s, h, w, g, dw, dh, st)
+                            : proj_bwd_impl<float>(s, h, w, g, dw, dh, st);
+}
+
+}  // namespace ca

@@ -29,17 +29,26 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(HERE, "csrc", "kernels.hip")
+CSRC = os.path.join(HERE, "csrc")
 COPY_BYTES = 1 << 30
 N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 SHORT = {"fwd_kernel": "fwd", "dkdv_kernel": "dkdv", "dq_kernel": "dq", "delta_kernel": "delta",
-         "zero_kernel": "zero", "accumulate_kernel": "accumulate"}
+         "zero_kernel": "zero", "accumulate_kernel": "accumulate", "gemm_kernel": "proj"}
 
 
-def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_sources(kernel: str) -> list:
+    """The source files a kernel is built from (the shared device header and its own file)."""
+    own = "projection.hip" if kernel == "proj" else "attention.hip"
+    return [os.path.join(CSRC, "device_common.h"), os.path.join(CSRC, own)]
+
+
+def kernel_source_sha256(kernel: str) -> str:
+    h = hashlib.sha256()
+    for path in kernel_sources(kernel):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def short_name(full: str) -> str:
@@ -113,15 +122,16 @@ def summarize_main(args):
         for k in sorted(busy):
             if active.get(k):
                 lines.append(f"| {k} | {100.0 * busy[k] / (active[k] / N_XCD) / N_SIMD:.1f}% |")
-    lines += ["", f"kernel_source_sha256: {kernel_source_sha256()}", ""]
+    lines += ["", f"kernel_source_sha256: {kernel_source_sha256(args.kernel)}", ""]
     with open(args.out, "w") as fh:
         fh.write("\n".join(lines))
     print("\n".join(lines))
     return out
 
 
-def read_traffic(path: str):
-    """traffic_bytes_per_launch from a summary, or None if missing or stale."""
+def read_traffic(path: str, kernel: str):
+    """traffic_bytes_per_launch from a summary, or None if missing or stale (the
+    kernel's sources have changed since the counters were taken)."""
     if not os.path.exists(path):
         return None
     vals = {}
@@ -129,7 +139,7 @@ def read_traffic(path: str):
         if ":" in ln and ln.split(":")[0].strip() in ("traffic_bytes_per_launch", "kernel_source_sha256"):
             k, v = ln.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256") != kernel_source_sha256() or "traffic_bytes_per_launch" not in vals:
+    if vals.get("kernel_source_sha256") != kernel_source_sha256(kernel) or "traffic_bytes_per_launch" not in vals:
         return None
     return float(vals["traffic_bytes_per_launch"])
 

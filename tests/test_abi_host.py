@@ -33,6 +33,20 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(so, name), name
 
 
+def test_no_undeclared_c_exports():
+    # Every unmangled function the library exports is one the header declares.
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.split()[1:2] == ["T"]}
+    c_names = {n for n in exported if not n.startswith("_")}
+    assert c_names <= set(declared_functions()), sorted(c_names - set(declared_functions()))
+
+
 def test_one_hip_runtime_when_loaded_before_torch():
     # A caller that imports the binding before torch must still end up with a
     # single HIP runtime in the process (the library shares torch's).
