@@ -55,9 +55,9 @@ def qkv_backward(h, wq, wk, wv, dq, dk, dv):
     dW_q, dW_k, dW_v (summed over the batch) and dH_in [B, T, d_model]."""
     h = np.asarray(h, dtype=np.float64)
     gq, gk, gv = (heads_to_cols(np.asarray(x, dtype=np.float64)) for x in (dq, dk, dv))
-    dwq = np.einsum("btm,btn->mn", h, gq)
-    dwk = np.einsum("btm,btn->mn", h, gk)
-    dwv = np.einsum("btm,btn->mn", h, gv)
+    dwq = sum(h[b].T @ gq[b] for b in range(h.shape[0]))
+    dwk = sum(h[b].T @ gk[b] for b in range(h.shape[0]))
+    dwv = sum(h[b].T @ gv[b] for b in range(h.shape[0]))
     wq, wk, wv = (np.asarray(w, dtype=np.float64) for w in (wq, wk, wv))
     dh = gq @ wq.T + gk @ wk.T + gv @ wv.T
     return dwq, dwk, dwv, dh
