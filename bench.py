@@ -167,8 +167,9 @@ def layer_main(args):
     dwv = torch.zeros_like(dwk)
     dh = torch.empty(Bt, T, dm, dtype=f32, device=dev)
     starts = list(range(0, T, C))
-    ws = torch.empty(max(B.chunk_attn_workspace_size(B.make_desc(q, k, chunk_start=0, chunk_len=C), B.CA_OP_BWD),
-                         256), dtype=torch.uint8, device=dev)
+    desc = B.make_desc(q, k, chunk_start=0, chunk_len=C)
+    ws = torch.empty(max(B.chunk_attn_workspace_size(desc, B.CA_OP_BWD), 256), dtype=torch.uint8, device=dev)
+    pws = torch.empty(max(B.chunk_attn_workspace_size(desc, B.CA_OP_PROJ_BWD), 256), dtype=torch.uint8, device=dev)
 
     def step():
         for s in starts:
@@ -182,7 +183,7 @@ def layer_main(args):
             B.chunk_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, chunk_start=s, chunk_len=c, q_row_offset=s,
                              softmax_scale=sc, workspace=ws)
             B.qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, chunk_start=s, chunk_len=c,
-                           q_row_offset=s)
+                           q_row_offset=s, workspace=pws)
 
     log(f"[bench] layer warmup {args.warmup}")
     for _ in range(args.warmup):

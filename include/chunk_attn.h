@@ -60,7 +60,7 @@ enum {
 
 enum { CA_F32 = 0, CA_BF16 = 1 };
 
-enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2 };
+enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2, CA_OP_PROJ_BWD = 3 };
 
 typedef struct {
   int32_t batch;         /* >= 1 */
@@ -79,7 +79,10 @@ typedef struct {
 /* Bytes of workspace the op needs for this descriptor (0 if none; the op then
  * accepts ws == NULL). op is CA_OP_*. For CA_OP_SPARSE_BWD the descriptor is
  * the whole-sequence one that sparse_chunk_bwd takes and chunk_len must be the
- * chunk size. Returns 0 for an invalid descriptor. */
+ * chunk size. CA_OP_PROJ_BWD sizes qkv_proj_bwd's workspace (bf16 layers:
+ * batch * round_up(chunk_len, 64) * (Hq + 2 Hkv) * head_dim bf16 values, the
+ * chunk's gradients rounded to bf16; float32 layers: none). Returns 0 for an
+ * invalid descriptor. */
 size_t chunk_attn_workspace_size(const chunk_attn_desc* desc, int32_t op);
 
 /* Forward of one chunk (the inference-mode pass that fills the caches in SeCO,
@@ -160,15 +163,17 @@ int sparse_chunk_bwd(const chunk_attn_desc* desc, int32_t seq_len, int32_t t, ui
  * chunk_attn_bwd for this chunk; dwq, dwk, dwv are float32 accumulators of the
  * weights' shapes, INCREMENTED (the caller zeroes them before a sweep). The
  * float32 gradients are rounded to dtype before they enter the products
- * (float32 accumulation). Errors as for chunk_attn_fwd, plus CA_ERR_SHAPE for
- * d_model or the H_in rows. */
+ * (float32 accumulation). ws: chunk_attn_workspace_size(desc, CA_OP_PROJ_BWD)
+ * bytes of device memory, 16-byte aligned, owned by the caller (contents on
+ * return unspecified). Errors as for chunk_attn_fwd, plus CA_ERR_SHAPE for
+ * d_model or the H_in rows and CA_ERR_WORKSPACE for a missing or short ws. */
 int qkv_proj_fwd(const chunk_attn_desc* desc, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
                  const void* h, const void* wq, const void* wk, const void* wv, void* q, void* k, void* v,
                  void* stream);
 int qkv_proj_bwd(const chunk_attn_desc* desc, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
                  const void* h, const void* wq, const void* wk, const void* wv, const float* dq,
                  const float* dk_acc, const float* dv_acc, float* dwq, float* dwk, float* dwv, float* dh,
-                 void* stream);
+                 void* ws, size_t ws_bytes, void* stream);
 
 /* Kernel timing for benchmarks (instrumentation only; results are unchanged).
  * chunk_attn_profile_start() clears the record and, until
@@ -186,7 +191,8 @@ enum {
   CA_KERNEL_ACCUMULATE = 4, /* prefix_grad_accumulate */
   CA_KERNEL_ZERO = 5,       /* zero fill used by sparse_chunk_bwd */
   CA_KERNEL_PROJ = 6,       /* projection GEMMs of qkv_proj_fwd / qkv_proj_bwd */
-  CA_KERNEL_COUNT = 7
+  CA_KERNEL_PROJ_PREP = 7,  /* qkv_proj_bwd: the chunk's gradients rounded to bf16 */
+  CA_KERNEL_COUNT = 8
 };
 int chunk_attn_profile_start(void);
 int chunk_attn_profile_stop(void);

@@ -22,8 +22,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libchunk_attn.so")
 
 CA_F32, CA_BF16 = 0, 1
-CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD = 0, 1, 2
-KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6}
+CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD, CA_OP_PROJ_BWD = 0, 1, 2, 3
+KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7}
 ERRORS = {0: "CA_OK", -1: "CA_ERR_NULL", -2: "CA_ERR_SHAPE", -3: "CA_ERR_DTYPE", -4: "CA_ERR_ALIGN",
           -5: "CA_ERR_WORKSPACE", -6: "CA_ERR_UNSUPPORTED", -7: "CA_ERR_HIP"}
 
@@ -66,7 +66,7 @@ def _load() -> ctypes.CDLL:
         "sparse_chunk_bwd": (ctypes.c_int, [D, I32, I32, U64, P, P, P, P, P, P, P, P, P,
                                             ctypes.POINTER(I32), P, SZ, P]),
         "qkv_proj_fwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P]),
-        "qkv_proj_bwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "qkv_proj_bwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "chunk_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "chunk_attn_last_error": (ctypes.c_char_p, []),
         "chunk_attn_profile_start": (ctypes.c_int, []),
@@ -180,16 +180,17 @@ def qkv_proj_fwd(h, wq, wk, wv, q, k, v, *, chunk_start: int, chunk_len: int, q_
 
 
 def qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh, *, chunk_start: int,
-                 chunk_len: int, q_row_offset: int = 0, h_row_offset: Optional[int] = None):
+                 chunk_len: int, q_row_offset: int = 0, h_row_offset: Optional[int] = None, workspace=None):
     """Projection gradients of one chunk: dW += H_in^T (dQ, dK, dV rows of the chunk), dh rows of
     the chunk = dQ Wq^T + dK Wk^T + dV Wv^T. q and k only give the descriptor's shapes."""
     _contig(h, wq, wk, wv, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh)
     desc = make_desc(q, k, chunk_start=chunk_start, chunk_len=chunk_len, q_row_offset=q_row_offset)
     B, Th, dm = h.shape
     hoff = chunk_start if h_row_offset is None else h_row_offset
+    ws, nbytes = _workspace(desc, CA_OP_PROJ_BWD, h, workspace)
     _check(lib.qkv_proj_bwd(ctypes.byref(desc), dm, Th, int(hoff), _ptr(h), _ptr(wq), _ptr(wk), _ptr(wv),
                             _ptr(dq), _ptr(dk_acc), _ptr(dv_acc), _ptr(dwq), _ptr(dwk), _ptr(dwv), _ptr(dh),
-                            _stream(h)))
+                            None if ws is None else _ptr(ws), nbytes, _stream(h)))
 
 
 def chunk_select(k: int, t: int, seed: int) -> list:

@@ -175,6 +175,39 @@ void prof_end(int kernel, hipStream_t st) {
 }
 }  // namespace ca
 
+namespace {
+int check_proj(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset) {
+  int rc = check_desc(d, false);
+  if (rc) return rc;
+  if (d_model < 64 || d_model > 65536 || d_model % 64 != 0)
+    return fail(CA_ERR_SHAPE, "d_model %d (a multiple of 64 in [64, 65536])", d_model);
+  if (h_row_offset < 0 || h_capacity < 1 || (int64_t)h_row_offset + d->chunk_len > h_capacity)
+    return fail(CA_ERR_SHAPE, "h rows [%d, %lld) exceed h_capacity %d", h_row_offset,
+                (long long)h_row_offset + d->chunk_len, h_capacity);
+  if ((int64_t)d->batch * h_capacity * d_model > ((int64_t)1 << 40) ||
+      (int64_t)d_model * d->n_q_heads * d->head_dim > ((int64_t)1 << 40))
+    return fail(CA_ERR_SHAPE, "projection tensors too large");
+  return CA_OK;
+}
+ca::ProjShape proj_shape(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset) {
+  ca::ProjShape s;
+  s.batch = d->batch;
+  s.d_model = d_model;
+  s.hq = d->n_q_heads;
+  s.hkv = d->n_kv_heads;
+  s.head_dim = d->head_dim;
+  s.h_cap = h_capacity;
+  s.h_off = h_row_offset;
+  s.q_cap = d->q_capacity;
+  s.q_off = d->q_row_offset;
+  s.kv_cap = d->kv_capacity;
+  s.start = d->chunk_start;
+  s.len = d->chunk_len;
+  s.dtype = d->dtype;
+  return s;
+}
+}  // namespace
+
 extern "C" {
 
 const char* chunk_attn_strerror(int code) {
@@ -199,6 +232,7 @@ size_t chunk_attn_workspace_size(const chunk_attn_desc* d, int32_t op) {
     case CA_OP_FWD: return 0;
     case CA_OP_BWD:
     case CA_OP_SPARSE_BWD: return delta_bytes(d);
+    case CA_OP_PROJ_BWD: return ca::proj_bwd_ws_bytes(proj_shape(d, 64, d->chunk_len, 0));
     default: return 0;
   }
 }
@@ -244,38 +278,6 @@ int prefix_grad_accumulate(float* acc, const float* src, int32_t batch, int32_t 
   return e == hipSuccess ? CA_OK : hip_fail(e, "prefix_grad_accumulate launch");
 }
 
-namespace {
-static int check_proj(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset) {
-  int rc = check_desc(d, false);
-  if (rc) return rc;
-  if (d_model < 64 || d_model > 65536 || d_model % 64 != 0)
-    return fail(CA_ERR_SHAPE, "d_model %d (a multiple of 64 in [64, 65536])", d_model);
-  if (h_row_offset < 0 || h_capacity < 1 || (int64_t)h_row_offset + d->chunk_len > h_capacity)
-    return fail(CA_ERR_SHAPE, "h rows [%d, %lld) exceed h_capacity %d", h_row_offset,
-                (long long)h_row_offset + d->chunk_len, h_capacity);
-  if ((int64_t)d->batch * h_capacity * d_model > ((int64_t)1 << 40) ||
-      (int64_t)d_model * d->n_q_heads * d->head_dim > ((int64_t)1 << 40))
-    return fail(CA_ERR_SHAPE, "projection tensors too large");
-  return CA_OK;
-}
-static ca::ProjShape proj_shape(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset) {
-  ca::ProjShape s;
-  s.batch = d->batch;
-  s.d_model = d_model;
-  s.hq = d->n_q_heads;
-  s.hkv = d->n_kv_heads;
-  s.head_dim = d->head_dim;
-  s.h_cap = h_capacity;
-  s.h_off = h_row_offset;
-  s.q_cap = d->q_capacity;
-  s.q_off = d->q_row_offset;
-  s.kv_cap = d->kv_capacity;
-  s.start = d->chunk_start;
-  s.len = d->chunk_len;
-  s.dtype = d->dtype;
-  return s;
-}
-}  // namespace
 
 int qkv_proj_fwd(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
                  const void* h, const void* wq, const void* wk, const void* wv, void* q, void* k, void* v,
@@ -291,12 +293,14 @@ int qkv_proj_fwd(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, 
 int qkv_proj_bwd(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
                  const void* h, const void* wq, const void* wk, const void* wv, const float* dq,
                  const float* dk_acc, const float* dv_acc, float* dwq, float* dwk, float* dwv, float* dh,
-                 void* stream) {
+                 void* ws, size_t ws_bytes, void* stream) {
   int rc = check_proj(d, d_model, h_capacity, h_row_offset);
   if (rc) return rc;
   if ((rc = check_ptrs({h, wq, wk, wv, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh}))) return rc;
-  hipError_t e = ca::launch_proj_bwd(proj_shape(d, d_model, h_capacity, h_row_offset), h, wq, wk, wv, dq, dk_acc,
-                                     dv_acc, dwq, dwk, dwv, dh, (hipStream_t)stream);
+  const ca::ProjShape ps = proj_shape(d, d_model, h_capacity, h_row_offset);
+  if ((rc = check_ws(ws, ws_bytes, ca::proj_bwd_ws_bytes(ps)))) return rc;
+  hipError_t e = ca::launch_proj_bwd(ps, h, wq, wk, wv, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh, ws,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? CA_OK : hip_fail(e, "qkv_proj_bwd launch");
 }
 

@@ -52,10 +52,12 @@ struct ProjShape {
 hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
                            void* q, void* k, void* v, hipStream_t st);
 // dW += H^(i)^T G for G = dq, dk, dv rows of the chunk; dh rows of the chunk
-// = dq wq^T + dk wk^T + dv wv^T (float32).
+// = dq wq^T + dk wk^T + dv wv^T (float32). ws: proj_bwd_ws_bytes(s) bytes,
+// 256-byte aligned (bf16 layers hold the chunk's gradients there as bf16).
+size_t proj_bwd_ws_bytes(const ProjShape& s);
 hipError_t launch_proj_bwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
                            const float* dq, const float* dk, const float* dv, float* dwq, float* dwk, float* dwv,
-                           float* dh, hipStream_t st);
+                           float* dh, void* ws, hipStream_t st);
 
 // Fill n floats with zero (a kernel, so it is safe inside captured graphs).
 hipError_t launch_zero(float* p, size_t n, hipStream_t st);

@@ -1,13 +1,30 @@
 // Projection GEMMs around the attention of one chunk for gfx950 (CDNA4): the
-// QKV projections and their weight and input gradients: C = A B, A [M][K], B [K][N], float32
-// accumulation on the matrix cores. Operands and output are read through
-// strided views, so that per-head [heads][rows][d] tensors take part as
-// [rows][heads*d] matrices without copies. A 4-wave workgroup owns a 128x128
-// output tile (2x2 waves of 64x64); 64-deep k slices are staged through
-// registers (converted to the compute type) into double-buffered LDS. An
-// operand whose stored layout has k along its rows ("mn-contiguous") is read
-// through the transposing path, the other with two 8-byte reads per lane, both
-// in the tile slot order.
+// QKV projections and their weight and input gradients, float32 accumulation
+// on the matrix cores.
+//
+// bf16 layers use proj_gemm_kernel: one launch per phase and chunk covers the
+// three projections at once, the weights taken side by side as one matrix
+// W_cat = [W_q | W_k | W_v] of (Hq + 2 Hkv) d columns:
+//   forward  Q|K|V (chunk rows) = H_in^(i) W_cat
+//   weights  dW_cat += H_in^(i)^T G_cat
+//   input    dH_in^(i) = G_cat W_cat^T
+// with G_cat the chunk rows of dQ | dK | dV, first rounded to bf16 in a
+// workspace by gcat_kernel (rows up to a multiple of 64, the tail zero). A
+// workgroup of 8 waves owns a 128x128 output tile: two groups of 4 waves (2x2
+// waves of 64x64) take the even and odd 64-deep k slices of slice pairs, which
+// stream by direct global->LDS loads one pair ahead into two statically named
+// buffers, and add their partial tiles through LDS at the end.
+//
+// float32 layers (the exactness path) use gemm_kernel, which reads every
+// operand through a strided view (so per-head [heads][rows][d] tensors take
+// part as [rows][heads*d] matrices without copies), one launch per projection.
+// A 4-wave workgroup owns a 128x128 output tile (2x2 waves of 64x64); 64-deep
+// k slices are staged through registers into double-buffered padded LDS.
+//
+// Both read an operand whose storage has k along its rows through the
+// transposing LDS path and the other with two 8-byte reads per lane, both in
+// the tile slot order; outputs are computed as C^T tiles so that a lane holds
+// four consecutive columns of one row.
 
 #include "device_common.h"
 
@@ -210,6 +227,294 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 projection GEMM (see the top of the file).
+// ----------------------------------------------------------------------------
+enum { PG_FWD = 0, PG_DW = 1, PG_DH = 2 };
+
+// [128 rows][64 k] bf16 tile with k along the row (k-contiguous operand): the
+// 16-byte chunk c of row r sits at chunk position c ^ ((r >> 1) & 7). Sixteen
+// consecutive rows then put one chunk column on 16 distinct 4-bank groups
+// (even and odd rows alternate between the two halves of the banks), so the
+// two 8-byte fragment reads of a 32-lane half never share a bank.
+struct KLay {
+  static constexpr int COLS = 64;
+  static __device__ __forceinline__ int off(int r, int c) {
+    return r * COLS + ((((c >> 3) ^ (r >> 1)) & 7) << 3) + (c & 7);
+  }
+};
+// [64 k rows][128 m or n] bf16 tile (operand with k along the stored rows).
+using TLay = SwzLay<bf16, 128>;
+constexpr int PG_TILE = 128 * 64;  // elements of one operand tile
+
+struct ProjGemmParams {
+  const bf16* a;             // forward, dW: H_in at the chunk's first row; dH: G_cat
+  long long a_ld, a_bs;      // row stride and batch stride (elements)
+  const bf16* b[3];          // forward, dH: W_q, W_k, W_v; dW: b[0] = G_cat
+  int b_w[3];                // widths of the three weights (dW: b_w[0] = N)
+  long long b_bs;            // dW: batch stride of G_cat
+  void* c[3];                // output segments (three weight/q/k/v blocks, or dH)
+  long long c_rs[3], c_hs[3], c_bs[3];
+  int c_hd[3];               // element (r, col) of segment s at c + b*bs + r*rs + (col/hd)*hs + col%hd
+  int c_w[3];                // segment widths in columns (single segment: c_w[0] = N)
+  int M, N, K;               // K per batch entry, a multiple of 64
+  int a_rows;                // rows of A (forward, dH) or of H_in (dW) that exist: reads clamp to them
+  int batch;                 // forward, dH: batch entries in the grid; dW: summed along k
+};
+
+// Segment of a column given three widths.
+__device__ __forceinline__ int seg3(int x, const int w[3], int& local) {
+  const int s = (x >= w[0]) + (x >= w[0] + w[1]);
+  local = x - (s > 0 ? w[0] : 0) - (s > 1 ? w[1] : 0);
+  return s;
+}
+
+// Geometry of the direct global->LDS loads of one operand tile by 8 waves,
+// two 1 KB instructions each: a tile row holds CH 16-byte chunks (8: the
+// [128][64] k-contiguous tile, 16: the [64][128] tile), instruction i of a
+// wave fills rows rb(i) .. rb(i) + 64/CH - 1, and lane l fetches the logical
+// chunk c(i) of row r(i) that belongs in its LDS slot (the swizzle is applied
+// on the global side).
+template <int CH>
+struct PgGeom {
+  static constexpr int ROWS = CH == 8 ? 128 : 64, RPI = 64 / CH, PER_WAVE = ROWS / 8;
+  static_assert(PER_WAVE == 2 * RPI, "two instructions per wave");
+  __device__ __forceinline__ static int rb(int wave, int i) { return wave * PER_WAVE + i * RPI; }
+  __device__ __forceinline__ static int row(int wave, int i, int lane) { return rb(wave, i) + lane / CH; }
+  __device__ __forceinline__ static int chunk(int wave, int i, int lane) {
+    const int r = row(wave, i, lane), slot = lane % CH;
+    if constexpr (CH == 8) {
+      return (slot ^ (r >> 1)) & 7;
+    } else {
+      return slot ^ TLay::swz(r);
+    }
+  }
+};
+
+template <int CH>
+__device__ __forceinline__ void pg_load(bf16* lds, int wave, int i, const bf16* src) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + PgGeom<CH>::rb(wave, i) * (CH * 8)), 16, 0, 0);
+#endif
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512) void proj_gemm_kernel(ProjGemmParams p) {
+  using E = Elt<bf16>;
+  using frag = E::frag;
+  __shared__ __attribute__((aligned(16))) bf16 As0[2 * PG_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs0[2 * PG_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 As1[2 * PG_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs1[2 * PG_TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wq = wave & 3;
+  const int wm = wq >> 1, wn = wq & 1;
+  const int n = lane & 15, g = lane >> 4;
+  const int mt = (p.M + 127) / 128, ntl = (p.N + 127) / 128;
+  const int id = xcd_order(blockIdx.x, gridDim.x);
+  const int bz = id / (mt * ntl), rem = id % (mt * ntl);
+  const int m0 = (rem % mt) * 128, n0 = (rem / mt) * 128;
+  const int nks = p.K / 64;
+  const int nk = MODE == PG_DW ? nks * p.batch : nks;
+  const int n_pairs = (nk + 1) / 2;
+
+  // Per-lane global sources of the two load instructions of each operand
+  // tile, fixed for the whole k loop; a slice adds its k offset.
+  constexpr int ACH = MODE == PG_DW ? 16 : 8, BCH = MODE == PG_DH ? 8 : 16;
+  using GA = PgGeom<ACH>;
+  using GB = PgGeom<BCH>;
+  const bf16* const w0 = p.b[0];
+  const bf16* const w1 = p.b[1];
+  const bf16* const w2 = p.b[2];
+  const int bw[3] = {p.b_w[0], p.b_w[1], p.b_w[2]};
+  const bf16* asrc[2];
+  const bf16* bsrc[2];
+  long long bld[2];
+  int bcol[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ra = GA::row(wave, i, lane), ca = GA::chunk(wave, i, lane);
+    const int rbb = GB::row(wave, i, lane), cb = GB::chunk(wave, i, lane);
+    if constexpr (MODE == PG_FWD) {
+      asrc[i] = p.a + (long long)bz * p.a_bs + (long long)min(m0 + ra, p.a_rows - 1) * p.a_ld + 8 * ca;
+      int col;
+      const int sg = seg3(min(n0 + 8 * cb, p.N - 8), bw, col);
+      const bf16* w = sg == 0 ? w0 : sg == 1 ? w1 : w2;
+      bld[i] = sg == 0 ? bw[0] : sg == 1 ? bw[1] : bw[2];
+      bsrc[i] = w + (long long)rbb * bld[i] + col;
+    } else if constexpr (MODE == PG_DW) {
+      asrc[i] = p.a + min(m0 + 8 * ca, p.M - 8);
+      bsrc[i] = w0 + (long long)rbb * p.N + min(n0 + 8 * cb, p.N - 8);
+      bld[i] = 0;
+    } else {
+      asrc[i] = p.a + (long long)bz * p.a_bs + (long long)min(m0 + ra, p.a_rows - 1) * p.a_ld + 8 * ca;
+      bsrc[i] = nullptr;                // the slice's weight picks the base
+      bld[i] = min(n0 + rbb, p.N - 1);  // weight row of this lane
+      bcol[i] = 8 * cb;
+    }
+  }
+
+  // Stage slice t (A and B tiles) into LDS.
+  auto stage_slice = [&](bf16* at, bf16* bt, int t) {
+    if constexpr (MODE == PG_FWD) {
+      const int k0 = t * 64;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        pg_load<ACH>(at, wave, i, asrc[i] + k0);
+        pg_load<BCH>(bt, wave, i, bsrc[i] + (long long)k0 * bld[i]);
+      }
+    } else if constexpr (MODE == PG_DW) {
+      const int bb = t / nks, k0 = (t % nks) * 64;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ra = GA::row(wave, i, lane);
+        pg_load<ACH>(at, wave, i, asrc[i] + (long long)bb * p.a_bs + (long long)min(k0 + ra, p.a_rows - 1) * p.a_ld);
+        pg_load<BCH>(bt, wave, i, bsrc[i] + (long long)bb * p.b_bs + (long long)k0 * p.N);
+      }
+    } else {
+      const int k0 = t * 64;
+      int kl;
+      const int sg = seg3(k0, bw, kl);  // uniform: a slice never straddles two weights
+      const bf16* w = sg == 0 ? w0 : sg == 1 ? w1 : w2;
+      const long long wd = sg == 0 ? bw[0] : sg == 1 ? bw[1] : bw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        pg_load<ACH>(at, wave, i, asrc[i] + k0);
+        pg_load<BCH>(bt, wave, i, w + bld[i] * wd + kl + bcol[i]);
+      }
+    }
+  };
+  auto stage_pair = [&](bf16* at, bf16* bt, int pair) {
+    stage_slice(at, bt, 2 * pair);
+    if (2 * pair + 1 < nk) stage_slice(at + PG_TILE, bt + PG_TILE, 2 * pair + 1);
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const bf16* at, const bf16* bt) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      frag af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mr = wm * 64 + i * 16, nr = wn * 64 + i * 16;
+        if constexpr (MODE == PG_DW) {
+          af[i] = ldT8<TLay>(at, ks * 32, mr, lane);
+        } else {
+          af[i] = ld8t<KLay>(at, mr + n, ks * 32, g);
+        }
+        if constexpr (MODE == PG_DH) {
+          bfr[i] = ld8t<KLay>(bt, nr + n, ks * 32, g);
+        } else {
+          bfr[i] = ldT8<TLay>(bt, ks * 32, nr, lane);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) E::mma(acc[i][j], bfr[j], af[i]);
+    }
+  };
+
+  stage_pair(As0, Bs0, 0);
+  wait_loads();
+  __syncthreads();
+  auto pair_step = [&](int i, const bf16* Ac, const bf16* Bc, bf16* An, bf16* Bn) {
+    if (i + 1 < n_pairs) stage_pair(An, Bn, i + 1);
+    if (2 * i + grp < nk) compute(Ac + grp * PG_TILE, Bc + grp * PG_TILE);
+    wait_loads();  // the next pair has landed in LDS
+    __syncthreads();
+  };
+  for (int i = 0; i < n_pairs; i += 2) {
+    pair_step(i, As0, Bs0, As1, Bs1);
+    if (i + 1 < n_pairs) pair_step(i + 1, As1, Bs1, As0, Bs0);
+  }
+
+  // Group 0 finishes rows i = 0, 1 of every wave tile, group 1 rows i = 2, 3;
+  // each hands the other half of its partial sums over through LDS.
+  f32x4* give = (f32x4*)(grp == 0 ? As0 : Bs0);
+  const f32x4* take = (const f32x4*)(grp == 0 ? Bs0 : As0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if ((i >> 1) == grp) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) give[((wq * 8 + (i & 1) * 4 + j) * 64) + lane] = acc[i][j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if ((i >> 1) != grp) continue;
+    const int m = m0 + wm * 64 + i * 16 + n;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nb = n0 + wn * 64 + j * 16 + 4 * g;
+      if (nb >= p.N) continue;
+      const f32x4 v = acc[i][j] + take[((wq * 8 + (i & 1) * 4 + j) * 64) + lane];
+      int col;
+      const int sg = seg3(nb, p.c_w, col);
+      const long long rs = sg == 0 ? p.c_rs[0] : sg == 1 ? p.c_rs[1] : p.c_rs[2];
+      const long long hs = sg == 0 ? p.c_hs[0] : sg == 1 ? p.c_hs[1] : p.c_hs[2];
+      const long long bs = sg == 0 ? p.c_bs[0] : sg == 1 ? p.c_bs[1] : p.c_bs[2];
+      const int hd = sg == 0 ? p.c_hd[0] : sg == 1 ? p.c_hd[1] : p.c_hd[2];
+      void* base = sg == 0 ? p.c[0] : sg == 1 ? p.c[1] : p.c[2];
+      const long long idx = (long long)bz * bs + (long long)m * rs + (long long)(col / hd) * hs + col % hd;
+      if constexpr (MODE == PG_FWD) {
+        store4<bf16>((bf16*)base + idx, v, 1.f);
+      } else if constexpr (MODE == PG_DW) {
+        f32x4* c = (f32x4*)((float*)base + idx);
+        *c = *c + v;
+      } else {
+        *(f32x4*)((float*)base + idx) = v;
+      }
+    }
+  }
+}
+
+// G_cat[b][r][:] = dQ | dK | dV of chunk row r, rounded to bf16, for r < len;
+// zero for len <= r < rows_pad. Eight columns per thread.
+struct GcatParams {
+  const float* g[3];
+  long long g_off[3];  // element offset of the chunk's first row in each head
+  long long g_hs[3];   // head stride (capacity * d)
+  int heads[3];
+  int d, len, rows_pad, ncols, batch;
+  bf16* out;
+};
+__global__ __launch_bounds__(256) void gcat_kernel(GcatParams p) {
+  const int c8 = p.ncols / 8;
+  const long long total = (long long)p.batch * p.rows_pad * c8;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int col = (int)(i % c8) * 8;
+    const long long br = i / c8;
+    const int r = (int)(br % p.rows_pad), b = (int)(br / p.rows_pad);
+    bf16x8 v{};
+    if (r < p.len) {
+      const int w0 = p.heads[0] * p.d, w1 = p.heads[1] * p.d;
+      const int sg = (col >= w0) + (col >= w0 + w1);
+      const int lc = col - (sg > 0 ? w0 : 0) - (sg > 1 ? w1 : 0);
+      const float* src = (sg == 0 ? p.g[0] : sg == 1 ? p.g[1] : p.g[2]) +
+                         ((long long)b * (sg == 0 ? p.heads[0] : sg == 1 ? p.heads[1] : p.heads[2]) + lc / p.d) *
+                             (sg == 0 ? p.g_hs[0] : sg == 1 ? p.g_hs[1] : p.g_hs[2]) +
+                         (sg == 0 ? p.g_off[0] : sg == 1 ? p.g_off[1] : p.g_off[2]) + (long long)r * p.d + lc % p.d;
+      const f32x4 x = *(const f32x4*)src, y = *(const f32x4*)(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = (bf16)x[e];
+        v[4 + e] = (bf16)y[e];
+      }
+    }
+    *(bf16x8*)(p.out + br * p.ncols + col) = v;
+  }
+}
+
 template <typename T, typename SA, typename SB, bool A_MN, bool B_MN, bool OUT_F32>
 hipError_t gemm_launch(const GemmParams& p, int batch, hipStream_t st) {
   prof_begin(CA_KERNEL_PROJ, st);
@@ -275,23 +580,140 @@ hipError_t proj_bwd_impl(const ProjShape& s, const void* h, const void* const w[
   }
   return hipSuccess;
 }
+// bf16: one launch per phase.
+int pg_rows_pad(int len) { return (len + 63) / 64 * 64; }
+
+template <int MODE>
+hipError_t pg_launch(const ProjGemmParams& p, int grid_batch, hipStream_t st) {
+  const int tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * grid_batch;
+  prof_begin(CA_KERNEL_PROJ, st);
+  hipLaunchKernelGGL((proj_gemm_kernel<MODE>), dim3(tiles), dim3(512), 0, st, p);
+  prof_end(CA_KERNEL_PROJ, st);
+  return hipGetLastError();
+}
+
+hipError_t pg_fwd(const ProjShape& s, const void* h, const void* const w[3], void* const out[3], hipStream_t st) {
+  const int d = s.head_dim;
+  const int H[3] = {s.hq, s.hkv, s.hkv};
+  ProjGemmParams p{};
+  p.a = (const bf16*)h + (size_t)s.h_off * s.d_model;
+  p.a_ld = s.d_model;
+  p.a_bs = (long long)s.h_cap * s.d_model;
+  for (int t = 0; t < 3; ++t) {
+    const int cap = t == 0 ? s.q_cap : s.kv_cap, off = t == 0 ? s.q_off : s.start;
+    p.b[t] = (const bf16*)w[t];
+    p.b_w[t] = H[t] * d;
+    p.c[t] = (bf16*)out[t] + (size_t)off * d;
+    p.c_rs[t] = d;
+    p.c_hs[t] = (long long)cap * d;
+    p.c_bs[t] = (long long)H[t] * cap * d;
+    p.c_hd[t] = d;
+    p.c_w[t] = H[t] * d;
+  }
+  p.M = s.len;
+  p.N = (s.hq + 2 * s.hkv) * d;
+  p.K = s.d_model;
+  p.a_rows = s.len;
+  p.batch = s.batch;
+  return pg_launch<PG_FWD>(p, s.batch, st);
+}
+
+hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], const float* const g[3],
+                  float* const dw[3], float* dh, void* ws, hipStream_t st) {
+  const int d = s.head_dim;
+  const int H[3] = {s.hq, s.hkv, s.hkv};
+  const int N = (s.hq + 2 * s.hkv) * d, rows_pad = pg_rows_pad(s.len);
+  bf16* gcat = (bf16*)ws;
+  GcatParams gp{};
+  for (int t = 0; t < 3; ++t) {
+    const int cap = t == 0 ? s.q_cap : s.kv_cap, off = t == 0 ? s.q_off : s.start;
+    gp.g[t] = g[t];
+    gp.g_off[t] = (long long)off * d;
+    gp.g_hs[t] = (long long)cap * d;
+    gp.heads[t] = H[t];
+  }
+  gp.d = d;
+  gp.len = s.len;
+  gp.rows_pad = rows_pad;
+  gp.ncols = N;
+  gp.batch = s.batch;
+  gp.out = gcat;
+  const long long vecs = (long long)s.batch * rows_pad * (N / 8);
+  const int blocks = (int)((vecs + 255) / 256 < 8192 ? (vecs + 255) / 256 : 8192);
+  prof_begin(CA_KERNEL_PROJ_PREP, st);
+  hipLaunchKernelGGL(gcat_kernel, dim3(blocks), dim3(256), 0, st, gp);
+  prof_end(CA_KERNEL_PROJ_PREP, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // dW_cat += H_in^(i)^T G_cat, the batch summed along k.
+  ProjGemmParams p{};
+  p.a = (const bf16*)h + (size_t)s.h_off * s.d_model;
+  p.a_ld = s.d_model;
+  p.a_bs = (long long)s.h_cap * s.d_model;
+  p.b[0] = gcat;
+  p.b_w[0] = N;
+  p.b_bs = (long long)rows_pad * N;
+  for (int t = 0; t < 3; ++t) {
+    p.c[t] = dw[t];
+    p.c_rs[t] = (long long)H[t] * d;
+    p.c_hs[t] = 0;
+    p.c_bs[t] = 0;
+    p.c_hd[t] = 1 << 30;
+    p.c_w[t] = H[t] * d;
+  }
+  p.M = s.d_model;
+  p.N = N;
+  p.K = rows_pad;
+  p.a_rows = s.len;
+  p.batch = s.batch;
+  e = pg_launch<PG_DW>(p, 1, st);
+  if (e != hipSuccess) return e;
+
+  // dH_in^(i) = G_cat W_cat^T.
+  ProjGemmParams q{};
+  q.a = gcat;
+  q.a_ld = N;
+  q.a_bs = (long long)rows_pad * N;
+  for (int t = 0; t < 3; ++t) {
+    q.b[t] = (const bf16*)w[t];
+    q.b_w[t] = H[t] * d;
+  }
+  q.c[0] = dh + (size_t)s.h_off * s.d_model;
+  q.c_rs[0] = s.d_model;
+  q.c_hs[0] = 0;
+  q.c_bs[0] = (long long)s.h_cap * s.d_model;
+  q.c_hd[0] = 1 << 30;
+  q.c_w[0] = s.d_model;
+  q.c_w[1] = q.c_w[2] = 1 << 30;
+  q.M = s.len;
+  q.N = s.d_model;
+  q.K = N;
+  q.a_rows = s.len;
+  q.batch = s.batch;
+  return pg_launch<PG_DH>(q, s.batch, st);
+}
 }  // namespace
+
+size_t proj_bwd_ws_bytes(const ProjShape& s) {
+  if (s.dtype != CA_BF16) return 0;
+  return (size_t)s.batch * pg_rows_pad(s.len) * (s.hq + 2 * s.hkv) * s.head_dim * sizeof(bf16);
+}
 
 hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
                            void* q, void* k, void* v, hipStream_t st) {
   const void* const w[3] = {wq, wk, wv};
   void* const out[3] = {q, k, v};
-  return s.dtype == CA_BF16 ? proj_fwd_impl<bf16>(s, h, w, out, st) : proj_fwd_impl<float>(s, h, w, out, st);
+  return s.dtype == CA_BF16 ? pg_fwd(s, h, w, out, st) : proj_fwd_impl<float>(s, h, w, out, st);
 }
 
 hipError_t launch_proj_bwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
                            const float* dq, const float* dk, const float* dv, float* dwq, float* dwk, float* dwv,
-                           float* dh, hipStream_t st) {
+                           float* dh, void* ws, hipStream_t st) {
   const void* const w[3] = {wq, wk, wv};
   const float* const g[3] = {dq, dk, dv};
   float* const dw[3] = {dwq, dwk, dwv};
-  return s.dtype == CA_BF16 ? proj_bwd_impl<bf16>(s, h, w, g, dw, dh, st)
-                            : proj_bwd_impl<float>(s, h, w, g, dw, dh, st);
+  return s.dtype == CA_BF16 ? pg_bwd(s, h, w, g, dw, dh, ws, st) : proj_bwd_impl<float>(s, h, w, g, dw, dh, st);
 }
 
 }  // namespace ca

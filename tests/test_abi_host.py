@@ -156,3 +156,24 @@ def test_strerror_names():
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.chunk_attn_strerror(code).decode()
     assert lib.chunk_attn_strerror(-99).decode() == "unknown error"
+
+
+def proj_bwd(d, dm=256, hcap=1024, hoff=512, ws=FAKE, ws_bytes=1 << 26, h=FAKE):
+    return lib.qkv_proj_bwd(ctypes.byref(d), dm, hcap, hoff, h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_projection_workspace_and_errors():
+    d = desc()   # bf16, Hq 4, Hkv 2, d 128, chunk 256 rows
+    need = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_PROJ_BWD)
+    assert need == 1 * 256 * (4 + 2 * 2) * 128 * 2
+    ragged = desc(chunk_len=100)  # rows rounded up to 64
+    assert lib.chunk_attn_workspace_size(ctypes.byref(ragged), b.CA_OP_PROJ_BWD) == 128 * 8 * 128 * 2
+    assert lib.chunk_attn_workspace_size(ctypes.byref(desc(dtype=b.CA_F32)), b.CA_OP_PROJ_BWD) == 0
+    assert proj_bwd(d, ws=None) == -5
+    assert proj_bwd(d, ws_bytes=need - 1) == -5
+    assert proj_bwd(d, ws=MISALIGNED, ws_bytes=need) == -4
+    assert proj_bwd(d, dm=96) == -2                  # d_model not a multiple of 64
+    assert proj_bwd(d, hcap=700) == -2               # h rows [512, 768) past the capacity
+    assert proj_bwd(d, h=None) == -1
+    assert proj_bwd(desc(head_dim=96)) == -6

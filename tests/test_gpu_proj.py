@@ -68,6 +68,11 @@ CASES = [
     ("f32_min_dmodel_one_chunk", 1, 100, 100, 64, 2, 1, 64, "f32"),
     ("bf16_batch2_ragged", 2, 640, 250, 256, 4, 2, 128, "bf16"),
     ("bf16_8b_dims_T2048", 1, 2048, 1024, 4096, 32, 8, 128, "bf16"),
+    # Q|K|V widths 192/64/64: output and weight tiles straddle the three
+    # projections; d_model 192 leaves a partial weight-gradient tile
+    ("bf16_d64_one_kv_head", 1, 300, 70, 192, 3, 1, 64, "bf16"),
+    # d_model 64 (one partial tile), 7-row chunks (padded to 64), batch 2
+    ("bf16_min_dmodel_tiny_chunks", 2, 40, 7, 64, 2, 2, 64, "bf16"),
 ]
 
 
@@ -89,3 +94,74 @@ def test_layer_parity(case):
     print(name, {k_: f"{v_:.2e}" for k_, v_ in errs.items()}, flush=True)
     for n_, e in errs.items():
         assert e <= tol, (n_, e)
+
+
+def test_layer_full_size_sampled():
+    """The 8B attention layer at full size (T = 16384, d_model 4096, C = 1024),
+    run exactly as the layer benchmark runs it. Checked on samples the oracle
+    can compute one by one: Q/K/V rows (H_in rows times the weights), and the
+    projection backward from the float32 gradients the GPU's attention
+    backward produced: dH_in rows and single weight-gradient entries
+    (sum over all T positions)."""
+    import torch
+    from sequence_chunked_exact_amd import binding as Bn
+    wl = W.LAYER_WORKLOADS["8b_attn_layer"]
+    print(f"[case] {wl.name} full size", flush=True)
+    inp = W.make_layer_inputs(wl, keep_f64=False)
+    dev = "cuda:0"
+    h, wq, wk, wv, do = (W.to_torch(inp.raw[n], dev) for n in ("h", "wq", "wk", "wv", "do"))
+    B, T, dm = h.shape
+    Hq, Hkv, d, C = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.chunk
+    f32 = torch.float32
+    q = torch.zeros(B, Hq, T, d, dtype=h.dtype, device=dev)
+    k = torch.zeros(B, Hkv, T, d, dtype=h.dtype, device=dev)
+    v = torch.zeros_like(k)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, T, dtype=f32, device=dev)
+    dq = torch.zeros(B, Hq, T, d, dtype=f32, device=dev)
+    dk = torch.zeros(B, Hkv, T, d, dtype=f32, device=dev)
+    dv = torch.zeros_like(dk)
+    dwq = torch.zeros(dm, Hq * d, dtype=f32, device=dev)
+    dwk = torch.zeros(dm, Hkv * d, dtype=f32, device=dev)
+    dwv = torch.zeros_like(dwk)
+    dh = torch.full((B, T, dm), float("nan"), dtype=f32, device=dev)
+    starts = list(range(0, T, C))
+    for s in starts:
+        Bn.qkv_proj_fwd(h, wq, wk, wv, q, k, v, chunk_start=s, chunk_len=min(C, T - s), q_row_offset=s)
+        Bn.chunk_attn_fwd(q, k, v, o, lse, chunk_start=s, chunk_len=min(C, T - s), q_row_offset=s,
+                          softmax_scale=wl.softmax_scale)
+    for s in reversed(starts):
+        c = min(C, T - s)
+        Bn.chunk_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, chunk_start=s, chunk_len=c, q_row_offset=s,
+                          softmax_scale=wl.softmax_scale)
+        Bn.qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, chunk_start=s, chunk_len=c,
+                        q_row_offset=s)
+    torch.cuda.synchronize()
+    hf = W.bf16_bits_to_f64(inp.raw["h"])[0]
+    wf = {n: W.bf16_bits_to_f64(inp.raw[n]) for n in ("wq", "wk", "wv")}
+    g = {"wq": P.heads_to_cols(dq.cpu().double().numpy())[0], "wk": P.heads_to_cols(dk.cpu().double().numpy())[0],
+         "wv": P.heads_to_cols(dv.cpu().double().numpy())[0]}
+    assert all(np.isfinite(x).all() for x in g.values())
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, C - 1, C, T - 1], rng.integers(0, T, 12)]))
+    out = {"wq": P.heads_to_cols(q.float().cpu().double().numpy())[0],
+           "wk": P.heads_to_cols(k.float().cpu().double().numpy())[0],
+           "wv": P.heads_to_cols(v.float().cpu().double().numpy())[0]}
+    for n_ in ("wq", "wk", "wv"):
+        ref = hf[rows] @ wf[n_]
+        e = rel(out[n_][rows], ref)
+        print("proj", n_, f"{e:.2e}", flush=True)
+        assert e <= 2e-2, (n_, e)
+    dh_ref = sum(g[n_][rows] @ wf[n_].T for n_ in ("wq", "wk", "wv"))
+    e = rel(dh.cpu().double().numpy()[0][rows], dh_ref)
+    print("dh", f"{e:.2e}", flush=True)
+    assert e <= 2e-2, e
+    got_w = {"wq": dwq.cpu().double().numpy(), "wk": dwk.cpu().double().numpy(), "wv": dwv.cpu().double().numpy()}
+    for n_ in ("wq", "wk", "wv"):
+        ms = rng.integers(0, dm, 24)
+        ns = rng.integers(0, got_w[n_].shape[1], 24)
+        ref = np.array([hf[:, m] @ g[n_][:, c] for m, c in zip(ms, ns)])
+        scale = max(np.abs(ref).max(), 1e-30)
+        e = float(np.abs(got_w[n_][ms, ns] - ref).max() / scale)
+        print("dW", n_, f"{e:.2e}", flush=True)
+        assert e <= 2e-2, (n_, e)
