@@ -169,7 +169,7 @@ def layer_main(args):
     starts = list(range(0, T, C))
     desc = B.make_desc(q, k, chunk_start=0, chunk_len=C)
     ws = torch.empty(max(B.chunk_attn_workspace_size(desc, B.CA_OP_BWD), 256), dtype=torch.uint8, device=dev)
-    pws = torch.empty(max(B.chunk_attn_workspace_size(desc, B.CA_OP_PROJ_BWD), 256), dtype=torch.uint8, device=dev)
+    pws = torch.empty(max(B.qkv_proj_bwd_workspace_size(desc, dm), 256), dtype=torch.uint8, device=dev)
 
     def step():
         for s in starts:

@@ -60,7 +60,7 @@ enum {
 
 enum { CA_F32 = 0, CA_BF16 = 1 };
 
-enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2, CA_OP_PROJ_BWD = 3 };
+enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2 };
 
 typedef struct {
   int32_t batch;         /* >= 1 */
@@ -79,10 +79,7 @@ typedef struct {
 /* Bytes of workspace the op needs for this descriptor (0 if none; the op then
  * accepts ws == NULL). op is CA_OP_*. For CA_OP_SPARSE_BWD the descriptor is
  * the whole-sequence one that sparse_chunk_bwd takes and chunk_len must be the
- * chunk size. CA_OP_PROJ_BWD sizes qkv_proj_bwd's workspace (bf16 layers:
- * batch * round_up(chunk_len, 64) * (Hq + 2 Hkv) * head_dim bf16 values, the
- * chunk's gradients rounded to bf16; float32 layers: none). Returns 0 for an
- * invalid descriptor. */
+ * chunk size. Returns 0 for an invalid descriptor. */
 size_t chunk_attn_workspace_size(const chunk_attn_desc* desc, int32_t op);
 
 /* Forward of one chunk (the inference-mode pass that fills the caches in SeCO,
@@ -163,10 +160,15 @@ int sparse_chunk_bwd(const chunk_attn_desc* desc, int32_t seq_len, int32_t t, ui
  * chunk_attn_bwd for this chunk; dwq, dwk, dwv are float32 accumulators of the
  * weights' shapes, INCREMENTED (the caller zeroes them before a sweep). The
  * float32 gradients are rounded to dtype before they enter the products
- * (float32 accumulation). ws: chunk_attn_workspace_size(desc, CA_OP_PROJ_BWD)
+ * (float32 accumulation). ws: qkv_proj_bwd_workspace_size(desc, d_model)
  * bytes of device memory, 16-byte aligned, owned by the caller (contents on
  * return unspecified). Errors as for chunk_attn_fwd, plus CA_ERR_SHAPE for
  * d_model or the H_in rows and CA_ERR_WORKSPACE for a missing or short ws. */
+/* Workspace bytes qkv_proj_bwd needs (0 for float32 layers; bf16 layers hold
+ * the chunk's gradients, batch * round_up(chunk_len, 64) rows of
+ * (Hq + 2 Hkv) * head_dim, and the weights' transpose, (Hq + 2 Hkv) * head_dim
+ * rows of d_model, both in bf16). Returns 0 for invalid arguments. */
+size_t qkv_proj_bwd_workspace_size(const chunk_attn_desc* desc, int32_t d_model);
 int qkv_proj_fwd(const chunk_attn_desc* desc, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
                  const void* h, const void* wq, const void* wk, const void* wv, void* q, void* k, void* v,
                  void* stream);

@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libchunk_attn.so")
 
 CA_F32, CA_BF16 = 0, 1
-CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD, CA_OP_PROJ_BWD = 0, 1, 2, 3
+CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD = 0, 1, 2
 KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7}
 ERRORS = {0: "CA_OK", -1: "CA_ERR_NULL", -2: "CA_ERR_SHAPE", -3: "CA_ERR_DTYPE", -4: "CA_ERR_ALIGN",
           -5: "CA_ERR_WORKSPACE", -6: "CA_ERR_UNSUPPORTED", -7: "CA_ERR_HIP"}
@@ -65,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "chunk_select": (ctypes.c_int, [I32, I32, U64, ctypes.POINTER(I32)]),
         "sparse_chunk_bwd": (ctypes.c_int, [D, I32, I32, U64, P, P, P, P, P, P, P, P, P,
                                             ctypes.POINTER(I32), P, SZ, P]),
+        "qkv_proj_bwd_workspace_size": (SZ, [D, I32]),
         "qkv_proj_fwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P]),
         "qkv_proj_bwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "chunk_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -167,6 +168,10 @@ def prefix_grad_accumulate(acc, src, prefix_len: int, scale: float = 1.0):
                                       float(scale), _stream(acc)))
 
 
+def qkv_proj_bwd_workspace_size(desc: Desc, d_model: int) -> int:
+    return int(lib.qkv_proj_bwd_workspace_size(ctypes.byref(desc), int(d_model)))
+
+
 def qkv_proj_fwd(h, wq, wk, wv, q, k, v, *, chunk_start: int, chunk_len: int, q_row_offset: int = 0,
                  h_row_offset: Optional[int] = None):
     """Q/K/V of one chunk from the layer input h [B, T_h, d_model] and weights [d_model, H*d]:
@@ -187,7 +192,11 @@ def qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh, *, 
     desc = make_desc(q, k, chunk_start=chunk_start, chunk_len=chunk_len, q_row_offset=q_row_offset)
     B, Th, dm = h.shape
     hoff = chunk_start if h_row_offset is None else h_row_offset
-    ws, nbytes = _workspace(desc, CA_OP_PROJ_BWD, h, workspace)
+    need = qkv_proj_bwd_workspace_size(desc, dm)
+    if workspace is None and need > 0:
+        import torch
+        workspace = torch.empty(need, dtype=torch.uint8, device=h.device)
+    ws, nbytes = workspace, (0 if workspace is None else workspace.numel() * workspace.element_size())
     _check(lib.qkv_proj_bwd(ctypes.byref(desc), dm, Th, int(hoff), _ptr(h), _ptr(wq), _ptr(wk), _ptr(wv),
                             _ptr(dq), _ptr(dk_acc), _ptr(dv_acc), _ptr(dwq), _ptr(dwk), _ptr(dwv), _ptr(dh),
                             None if ws is None else _ptr(ws), nbytes, _stream(h)))

@@ -232,7 +232,6 @@ size_t chunk_attn_workspace_size(const chunk_attn_desc* d, int32_t op) {
     case CA_OP_FWD: return 0;
     case CA_OP_BWD:
     case CA_OP_SPARSE_BWD: return delta_bytes(d);
-    case CA_OP_PROJ_BWD: return ca::proj_bwd_ws_bytes(proj_shape(d, 64, d->chunk_len, 0));
     default: return 0;
   }
 }
@@ -278,6 +277,11 @@ int prefix_grad_accumulate(float* acc, const float* src, int32_t batch, int32_t 
   return e == hipSuccess ? CA_OK : hip_fail(e, "prefix_grad_accumulate launch");
 }
 
+
+size_t qkv_proj_bwd_workspace_size(const chunk_attn_desc* d, int32_t d_model) {
+  if (check_proj(d, d_model, d ? d->chunk_len : 1, 0) != CA_OK) return 0;
+  return ca::proj_bwd_ws_bytes(proj_shape(d, d_model, d->chunk_len, 0));
+}
 
 int qkv_proj_fwd(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
                  const void* h, const void* wq, const void* wk, const void* wv, void* q, void* k, void* v,

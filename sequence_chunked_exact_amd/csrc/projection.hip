@@ -9,7 +9,9 @@
 //   weights  dW_cat += H_in^(i)^T G_cat
 //   input    dH_in^(i) = G_cat W_cat^T
 // with G_cat the chunk rows of dQ | dK | dV, first rounded to bf16 in a
-// workspace by gcat_kernel (rows up to a multiple of 64, the tail zero). A
+// workspace by gcat_kernel (rows up to a multiple of 64, the tail zero), and
+// W_cat^T written there by wt_kernel: read along its rows in 128-byte pieces,
+// W_cat streamed several times slower than its transpose read along k. A
 // workgroup of 8 waves owns a 128x128 output tile: two groups of 4 waves (2x2
 // waves of 64x64) take the even and odd 64-deep k slices of slice pairs, which
 // stream by direct global->LDS loads one pair ahead into two statically named
@@ -250,8 +252,8 @@ constexpr int PG_TILE = 128 * 64;  // elements of one operand tile
 struct ProjGemmParams {
   const bf16* a;             // forward, dW: H_in at the chunk's first row; dH: G_cat
   long long a_ld, a_bs;      // row stride and batch stride (elements)
-  const bf16* b[3];          // forward, dH: W_q, W_k, W_v; dW: b[0] = G_cat
-  int b_w[3];                // widths of the three weights (dW: b_w[0] = N)
+  const bf16* b[3];          // forward: W_q, W_k, W_v; dW: b[0] = G_cat; dH: b[0] = W_cat^T
+  int b_w[3];                // widths (= row strides) of the B matrices side by side
   long long b_bs;            // dW: batch stride of G_cat
   void* c[3];                // output segments (three weight/q/k/v blocks, or dH)
   long long c_rs[3], c_hs[3], c_bs[3];
@@ -275,10 +277,11 @@ __device__ __forceinline__ int seg3(int x, const int w[3], int& local) {
 // wave fills rows rb(i) .. rb(i) + 64/CH - 1, and lane l fetches the logical
 // chunk c(i) of row r(i) that belongs in its LDS slot (the swizzle is applied
 // on the global side).
-template <int CH>
+template <int CH, int NW>
 struct PgGeom {
-  static constexpr int ROWS = CH == 8 ? 128 : 64, RPI = 64 / CH, PER_WAVE = ROWS / 8;
-  static_assert(PER_WAVE == 2 * RPI, "two instructions per wave");
+  static constexpr int ROWS = CH == 8 ? 128 : 64, RPI = 64 / CH, PER_WAVE = ROWS / NW;
+  static constexpr int NI = PER_WAVE / RPI;  // load instructions per wave and tile
+  static_assert(PER_WAVE % RPI == 0, "whole instructions per wave");
   __device__ __forceinline__ static int rb(int wave, int i) { return wave * PER_WAVE + i * RPI; }
   __device__ __forceinline__ static int row(int wave, int i, int lane) { return rb(wave, i) + lane / CH; }
   __device__ __forceinline__ static int chunk(int wave, int i, int lane) {
@@ -291,25 +294,31 @@ struct PgGeom {
   }
 };
 
-template <int CH>
+template <class G>
 __device__ __forceinline__ void pg_load(bf16* lds, int wave, int i, const bf16* src) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + PgGeom<CH>::rb(wave, i) * (CH * 8)), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + G::rb(wave, i) * (G::ROWS == 128 ? 64 : 128)), 16, 0,
+                                   0);
 #endif
 }
 
-template <int MODE>
-__global__ __launch_bounds__(512) void proj_gemm_kernel(ProjGemmParams p) {
+// NG groups of 4 waves per workgroup (1 or 2): with NG = 2 the groups take
+// alternate k slices of each step and add their partial tiles at the end;
+// with NG = 1 two workgroups share a CU (64 KB of LDS each).
+template <int MODE, int NG>
+__global__ __launch_bounds__(NG * 256) __attribute__((amdgpu_waves_per_eu(2))) void proj_gemm_kernel(
+    ProjGemmParams p) {
   using E = Elt<bf16>;
   using frag = E::frag;
-  __shared__ __attribute__((aligned(16))) bf16 As0[2 * PG_TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Bs0[2 * PG_TILE];
-  __shared__ __attribute__((aligned(16))) bf16 As1[2 * PG_TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Bs1[2 * PG_TILE];
+  constexpr int NW = 4 * NG;
+  __shared__ __attribute__((aligned(16))) bf16 As0[NG * PG_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs0[NG * PG_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 As1[NG * PG_TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Bs1[NG * PG_TILE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, wq = wave & 3;
+  const int grp = NG == 1 ? 0 : wave >> 2, wq = wave & 3;
   const int wm = wq >> 1, wn = wq & 1;
   const int n = lane & 15, g = lane >> 4;
   const int mt = (p.M + 127) / 128, ntl = (p.N + 127) / 128;
@@ -318,77 +327,62 @@ __global__ __launch_bounds__(512) void proj_gemm_kernel(ProjGemmParams p) {
   const int m0 = (rem % mt) * 128, n0 = (rem / mt) * 128;
   const int nks = p.K / 64;
   const int nk = MODE == PG_DW ? nks * p.batch : nks;
-  const int n_pairs = (nk + 1) / 2;
+  const int n_pairs = (nk + NG - 1) / NG;  // steps of NG slices
 
   // Per-lane global sources of the two load instructions of each operand
   // tile, fixed for the whole k loop; a slice adds its k offset.
-  constexpr int ACH = MODE == PG_DW ? 16 : 8, BCH = MODE == PG_DH ? 8 : 16;
-  using GA = PgGeom<ACH>;
-  using GB = PgGeom<BCH>;
+  constexpr int ACH = MODE == PG_DW ? 16 : 8, BCH = 16;
+  using GA = PgGeom<ACH, NW>;
+  using GB = PgGeom<BCH, NW>;
+  constexpr int NI = GA::NI;
+  static_assert(GB::NI == NI, "both tiles take the same number of loads");
   const bf16* const w0 = p.b[0];
   const bf16* const w1 = p.b[1];
   const bf16* const w2 = p.b[2];
   const int bw[3] = {p.b_w[0], p.b_w[1], p.b_w[2]};
-  const bf16* asrc[2];
-  const bf16* bsrc[2];
-  long long bld[2];
-  int bcol[2];
+  const bf16* asrc[NI];
+  const bf16* bsrc[NI];
+  long long bld[NI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int ra = GA::row(wave, i, lane), ca = GA::chunk(wave, i, lane);
     const int rbb = GB::row(wave, i, lane), cb = GB::chunk(wave, i, lane);
-    if constexpr (MODE == PG_FWD) {
+    if constexpr (MODE != PG_DW) {
       asrc[i] = p.a + (long long)bz * p.a_bs + (long long)min(m0 + ra, p.a_rows - 1) * p.a_ld + 8 * ca;
       int col;
       const int sg = seg3(min(n0 + 8 * cb, p.N - 8), bw, col);
       const bf16* w = sg == 0 ? w0 : sg == 1 ? w1 : w2;
       bld[i] = sg == 0 ? bw[0] : sg == 1 ? bw[1] : bw[2];
       bsrc[i] = w + (long long)rbb * bld[i] + col;
-    } else if constexpr (MODE == PG_DW) {
+    } else {
       asrc[i] = p.a + min(m0 + 8 * ca, p.M - 8);
       bsrc[i] = w0 + (long long)rbb * p.N + min(n0 + 8 * cb, p.N - 8);
       bld[i] = 0;
-    } else {
-      asrc[i] = p.a + (long long)bz * p.a_bs + (long long)min(m0 + ra, p.a_rows - 1) * p.a_ld + 8 * ca;
-      bsrc[i] = nullptr;                // the slice's weight picks the base
-      bld[i] = min(n0 + rbb, p.N - 1);  // weight row of this lane
-      bcol[i] = 8 * cb;
     }
   }
 
   // Stage slice t (A and B tiles) into LDS.
   auto stage_slice = [&](bf16* at, bf16* bt, int t) {
-    if constexpr (MODE == PG_FWD) {
+    if constexpr (MODE != PG_DW) {
       const int k0 = t * 64;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        pg_load<ACH>(at, wave, i, asrc[i] + k0);
-        pg_load<BCH>(bt, wave, i, bsrc[i] + (long long)k0 * bld[i]);
-      }
-    } else if constexpr (MODE == PG_DW) {
-      const int bb = t / nks, k0 = (t % nks) * 64;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ra = GA::row(wave, i, lane);
-        pg_load<ACH>(at, wave, i, asrc[i] + (long long)bb * p.a_bs + (long long)min(k0 + ra, p.a_rows - 1) * p.a_ld);
-        pg_load<BCH>(bt, wave, i, bsrc[i] + (long long)bb * p.b_bs + (long long)k0 * p.N);
+      for (int i = 0; i < NI; ++i) {
+        pg_load<GA>(at, wave, i, asrc[i] + k0);
+        pg_load<GB>(bt, wave, i, bsrc[i] + (long long)k0 * bld[i]);
       }
     } else {
-      const int k0 = t * 64;
-      int kl;
-      const int sg = seg3(k0, bw, kl);  // uniform: a slice never straddles two weights
-      const bf16* w = sg == 0 ? w0 : sg == 1 ? w1 : w2;
-      const long long wd = sg == 0 ? bw[0] : sg == 1 ? bw[1] : bw[2];
+      const int bb = t / nks, k0 = (t % nks) * 64;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        pg_load<ACH>(at, wave, i, asrc[i] + k0);
-        pg_load<BCH>(bt, wave, i, w + bld[i] * wd + kl + bcol[i]);
+      for (int i = 0; i < NI; ++i) {
+        const int ra = GA::row(wave, i, lane);
+        pg_load<GA>(at, wave, i, asrc[i] + (long long)bb * p.a_bs + (long long)min(k0 + ra, p.a_rows - 1) * p.a_ld);
+        pg_load<GB>(bt, wave, i, bsrc[i] + (long long)bb * p.b_bs + (long long)k0 * p.N);
       }
     }
   };
   auto stage_pair = [&](bf16* at, bf16* bt, int pair) {
-    stage_slice(at, bt, 2 * pair);
-    if (2 * pair + 1 < nk) stage_slice(at + PG_TILE, bt + PG_TILE, 2 * pair + 1);
+    stage_slice(at, bt, NG * pair);
+    if (NG == 2 && 2 * pair + 1 < nk) stage_slice(at + PG_TILE, bt + PG_TILE, 2 * pair + 1);
   };
 
   f32x4 acc[4][4];
@@ -409,11 +403,7 @@ __global__ __launch_bounds__(512) void proj_gemm_kernel(ProjGemmParams p) {
         } else {
           af[i] = ld8t<KLay>(at, mr + n, ks * 32, g);
         }
-        if constexpr (MODE == PG_DH) {
-          bfr[i] = ld8t<KLay>(bt, nr + n, ks * 32, g);
-        } else {
-          bfr[i] = ldT8<TLay>(bt, ks * 32, nr, lane);
-        }
+        bfr[i] = ldT8<TLay>(bt, ks * 32, nr, lane);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -427,7 +417,7 @@ __global__ __launch_bounds__(512) void proj_gemm_kernel(ProjGemmParams p) {
   __syncthreads();
   auto pair_step = [&](int i, const bf16* Ac, const bf16* Bc, bf16* An, bf16* Bn) {
     if (i + 1 < n_pairs) stage_pair(An, Bn, i + 1);
-    if (2 * i + grp < nk) compute(Ac + grp * PG_TILE, Bc + grp * PG_TILE);
+    if (NG * i + grp < nk) compute(Ac + grp * PG_TILE, Bc + grp * PG_TILE);
     wait_loads();  // the next pair has landed in LDS
     __syncthreads();
   };
@@ -436,27 +426,30 @@ __global__ __launch_bounds__(512) void proj_gemm_kernel(ProjGemmParams p) {
     if (i + 1 < n_pairs) pair_step(i + 1, As1, Bs1, As0, Bs0);
   }
 
-  // Group 0 finishes rows i = 0, 1 of every wave tile, group 1 rows i = 2, 3;
-  // each hands the other half of its partial sums over through LDS.
+  // With two groups, group 0 finishes rows i = 0, 1 of every wave tile and
+  // group 1 rows i = 2, 3; each hands the other half of its partial sums over
+  // through LDS.
   f32x4* give = (f32x4*)(grp == 0 ? As0 : Bs0);
   const f32x4* take = (const f32x4*)(grp == 0 ? Bs0 : As0);
+  if constexpr (NG == 2) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if ((i >> 1) == grp) continue;
+    for (int i = 0; i < 4; ++i) {
+      if ((i >> 1) == grp) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) give[((wq * 8 + (i & 1) * 4 + j) * 64) + lane] = acc[i][j];
+      for (int j = 0; j < 4; ++j) give[((wq * 8 + (i & 1) * 4 + j) * 64) + lane] = acc[i][j];
+    }
+    __syncthreads();
   }
-  __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if ((i >> 1) != grp) continue;
+    if (NG == 2 && (i >> 1) != grp) continue;
     const int m = m0 + wm * 64 + i * 16 + n;
     if (m >= p.M) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int nb = n0 + wn * 64 + j * 16 + 4 * g;
       if (nb >= p.N) continue;
-      const f32x4 v = acc[i][j] + take[((wq * 8 + (i & 1) * 4 + j) * 64) + lane];
+      const f32x4 v = NG == 2 ? acc[i][j] + take[((wq * 8 + (i & 1) * 4 + j) * 64) + lane] : acc[i][j];
       int col;
       const int sg = seg3(nb, p.c_w, col);
       const long long rs = sg == 0 ? p.c_rs[0] : sg == 1 ? p.c_rs[1] : p.c_rs[2];
@@ -512,6 +505,39 @@ __global__ __launch_bounds__(256) void gcat_kernel(GcatParams p) {
       }
     }
     *(bf16x8*)(p.out + br * p.ncols + col) = v;
+  }
+}
+
+// W_cat^T[k][n] = W_s[n][k - begin_s] for the three weights side by side
+// (k < N = (Hq + 2 Hkv) d, n < d_model): 64 x 64 tiles through LDS, 16-byte
+// reads and writes.
+struct WtParams {
+  const bf16* w[3];
+  int w_w[3];
+  int d_model, ncols;
+  bf16* out;
+};
+__global__ __launch_bounds__(256) void wt_kernel(WtParams p) {
+  __shared__ bf16 t[64][64 + 8];
+  const int kt = blockIdx.x % (p.ncols / 64), nt = blockIdx.x / (p.ncols / 64);
+  const int k0 = kt * 64, n0 = nt * 64;
+  int kl;
+  const int sg = seg3(k0, p.w_w, kl);
+  const bf16* w = sg == 0 ? p.w[0] : sg == 1 ? p.w[1] : p.w[2];
+  const int wd = sg == 0 ? p.w_w[0] : sg == 1 ? p.w_w[1] : p.w_w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = threadIdx.x + i * 256, r = idx / 8, c = idx % 8;
+    *(bf16x8*)&t[r][c * 8] = *(const bf16x8*)(w + (long long)(n0 + r) * wd + kl + c * 8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = threadIdx.x + i * 256, r = idx / 8, c = idx % 8;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = t[c * 8 + e][r];
+    *(bf16x8*)(p.out + (long long)(k0 + r) * p.d_model + n0 + c * 8) = v;
   }
 }
 
@@ -582,12 +608,27 @@ hipError_t proj_bwd_impl(const ProjShape& s, const void* h, const void* const w[
 }
 // bf16: one launch per phase.
 int pg_rows_pad(int len) { return (len + 63) / 64 * 64; }
+// Workspace: G_cat [batch][rows_pad][N] then W_cat^T [N][d_model], bf16, each
+// starting on a 256-byte boundary.
+size_t pg_gcat_bytes(const ProjShape& s) {
+  const size_t b = (size_t)s.batch * pg_rows_pad(s.len) * (s.hq + 2 * s.hkv) * s.head_dim * sizeof(bf16);
+  return (b + 255) / 256 * 256;
+}
+
+// Wave groups per workgroup: dH_in has one output tile per CU (chunk rows x
+// d_model), so it splits k over two groups in one workgroup; the forward and
+// dW have enough tiles for two 4-wave workgroups per CU.
+template <int MODE>
+constexpr int pg_groups() {
+  return MODE == PG_DH ? 2 : 1;
+}
 
 template <int MODE>
 hipError_t pg_launch(const ProjGemmParams& p, int grid_batch, hipStream_t st) {
   const int tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * grid_batch;
+  constexpr int NG = pg_groups<MODE>();
   prof_begin(CA_KERNEL_PROJ, st);
-  hipLaunchKernelGGL((proj_gemm_kernel<MODE>), dim3(tiles), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((proj_gemm_kernel<MODE, NG>), dim3(tiles), dim3(NG * 256), 0, st, p);
   prof_end(CA_KERNEL_PROJ, st);
   return hipGetLastError();
 }
@@ -624,6 +665,7 @@ hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], con
   const int H[3] = {s.hq, s.hkv, s.hkv};
   const int N = (s.hq + 2 * s.hkv) * d, rows_pad = pg_rows_pad(s.len);
   bf16* gcat = (bf16*)ws;
+  bf16* wt = (bf16*)((char*)ws + pg_gcat_bytes(s));
   GcatParams gp{};
   for (int t = 0; t < 3; ++t) {
     const int cap = t == 0 ? s.q_cap : s.kv_cap, off = t == 0 ? s.q_off : s.start;
@@ -644,6 +686,20 @@ hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], con
   hipLaunchKernelGGL(gcat_kernel, dim3(blocks), dim3(256), 0, st, gp);
   prof_end(CA_KERNEL_PROJ_PREP, st);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  WtParams tp{};
+  for (int t = 0; t < 3; ++t) {
+    tp.w[t] = (const bf16*)w[t];
+    tp.w_w[t] = H[t] * d;
+  }
+  tp.d_model = s.d_model;
+  tp.ncols = N;
+  tp.out = wt;
+  prof_begin(CA_KERNEL_PROJ_PREP, st);
+  hipLaunchKernelGGL(wt_kernel, dim3((N / 64) * (s.d_model / 64)), dim3(256), 0, st, tp);
+  prof_end(CA_KERNEL_PROJ_PREP, st);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   // dW_cat += H_in^(i)^T G_cat, the batch summed along k.
@@ -675,10 +731,9 @@ hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], con
   q.a = gcat;
   q.a_ld = N;
   q.a_bs = (long long)rows_pad * N;
-  for (int t = 0; t < 3; ++t) {
-    q.b[t] = (const bf16*)w[t];
-    q.b_w[t] = H[t] * d;
-  }
+  q.b[0] = q.b[1] = q.b[2] = wt;
+  q.b_w[0] = s.d_model;
+  q.b_w[1] = q.b_w[2] = 1 << 30;
   q.c[0] = dh + (size_t)s.h_off * s.d_model;
   q.c_rs[0] = s.d_model;
   q.c_hs[0] = 0;
@@ -697,7 +752,7 @@ hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], con
 
 size_t proj_bwd_ws_bytes(const ProjShape& s) {
   if (s.dtype != CA_BF16) return 0;
-  return (size_t)s.batch * pg_rows_pad(s.len) * (s.hq + 2 * s.hkv) * s.head_dim * sizeof(bf16);
+  return pg_gcat_bytes(s) + (size_t)(s.hq + 2 * s.hkv) * s.head_dim * s.d_model * sizeof(bf16);
 }
 
 hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,

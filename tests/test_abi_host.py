@@ -165,11 +165,14 @@ def proj_bwd(d, dm=256, hcap=1024, hoff=512, ws=FAKE, ws_bytes=1 << 26, h=FAKE):
 
 def test_projection_workspace_and_errors():
     d = desc()   # bf16, Hq 4, Hkv 2, d 128, chunk 256 rows
-    need = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_PROJ_BWD)
-    assert need == 1 * 256 * (4 + 2 * 2) * 128 * 2
-    ragged = desc(chunk_len=100)  # rows rounded up to 64
-    assert lib.chunk_attn_workspace_size(ctypes.byref(ragged), b.CA_OP_PROJ_BWD) == 128 * 8 * 128 * 2
-    assert lib.chunk_attn_workspace_size(ctypes.byref(desc(dtype=b.CA_F32)), b.CA_OP_PROJ_BWD) == 0
+    size = lib.qkv_proj_bwd_workspace_size
+    wt = 8 * 128 * 256 * 2                            # (Hq + 2 Hkv) d x d_model, bf16
+    need = size(ctypes.byref(d), 256)
+    assert need == 256 * 8 * 128 * 2 + wt
+    ragged = desc(chunk_len=100)  # gradient rows rounded up to 64
+    assert size(ctypes.byref(ragged), 256) == 128 * 8 * 128 * 2 + wt
+    assert size(ctypes.byref(desc(dtype=b.CA_F32)), 256) == 0
+    assert size(ctypes.byref(d), 96) == 0             # invalid d_model
     assert proj_bwd(d, ws=None) == -5
     assert proj_bwd(d, ws_bytes=need - 1) == -5
     assert proj_bwd(d, ws=MISALIGNED, ws_bytes=need) == -4
