@@ -177,6 +177,64 @@ int qkv_proj_bwd(const chunk_attn_desc* desc, int32_t d_model, int32_t h_capacit
                  const float* dk_acc, const float* dv_acc, float* dwq, float* dwk, float* dwv, float* dh,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* ---- SpaCO over a stack of attention layers ------------------------------
+ *
+ * The relay of SpaCO's Algorithm 2 (SeCO/SpaCO review, Referee Report major
+ * comments on Section 5 / Algorithm 2 and on Section 6.4; "Assumptions"): KV
+ * caches of every layer are filled in one inference-mode pass; then each
+ * drawn chunk j, from the last to the first, has its graph rebuilt from the
+ * caches and is backpropagated from its own loss term together with the
+ * gradient that later drawn chunks accumulated into its cache rows, that
+ * relayed gradient multiplied by relay_factor (line 7, m_j.grad <- (k/t)
+ * m'_j.grad; the deployed method caps the factor at 2). Cache gradients of
+ * chunks that are not drawn are dropped. All chunks drawn with relay_factor 1
+ * is SeCO's exact gradient.
+ *
+ * The stack: layer l maps H_l [batch][h_capacity][d_model] (d_model =
+ * n_q_heads * head_dim) to H_{l+1} = H_l + O_l, O_l the chunked causal
+ * attention of Q, K, V = H_l W_q^l, H_l W_k^l, H_l W_v^l with the heads side
+ * by side; the loss gradient dJ/dH_L = dy is given.
+ *
+ * The descriptor is the whole-sequence one: chunk_len is the chunk size C,
+ * kv_capacity the cache rows (>= seq_len), q_capacity >= C; chunk_start and
+ * q_row_offset are ignored. */
+typedef struct {
+  const void* wq;  /* [d_model][n_q_heads*head_dim], dtype */
+  const void* wk;  /* [d_model][n_kv_heads*head_dim], dtype */
+  const void* wv;
+  void* k_cache;   /* [batch][n_kv_heads][kv_capacity][head_dim], dtype */
+  void* v_cache;
+  float* dk_acc;   /* [batch][n_kv_heads][kv_capacity][head_dim] float32 (m.grad; zeroed by the backward) */
+  float* dv_acc;
+  float* dwq;      /* weight gradients, float32, INCREMENTED */
+  float* dwk;
+  float* dwv;
+} spaco_layer;
+
+/* Workspace bytes for spaco_stack_forward / spaco_stack_backward (chunk-local
+ * activations of every layer, the chunk's gradients, the attention and
+ * projection workspaces). 0 for invalid arguments. */
+size_t spaco_stack_workspace_size(const chunk_attn_desc* desc, int32_t n_layers);
+
+/* Inference-mode pass: every chunk in ascending order through every layer,
+ * writing rows [0, seq_len) of each layer's k_cache and v_cache. h0 is the
+ * stack input [batch][h_capacity][d_model] in dtype. Only wq, wk, wv, k_cache
+ * and v_cache of each layer are used. */
+int spaco_stack_forward(const chunk_attn_desc* desc, int32_t seq_len, int32_t n_layers, const spaco_layer* layers,
+                        const void* h0, int32_t h_capacity, void* ws, size_t ws_bytes, void* stream);
+
+/* SpaCO's relayed backward over the drawn chunks `chunks` (n_chunks distinct
+ * 0-based indices in any order; processed from the last to the first) after
+ * spaco_stack_forward has filled the caches. dy [batch][h_capacity][d_model]
+ * float32 is dJ/dH_L; dh0 (same shape) receives dJ/dH_0 on the drawn chunks'
+ * rows (other rows untouched). Zeroes every layer's dk_acc/dv_acc first;
+ * increments dwq/dwk/dwv. relay_factor: finite. Errors as for sparse_chunk_bwd,
+ * plus CA_ERR_SHAPE for d_model != n_q_heads * head_dim, d_model not a
+ * multiple of 64, or a chunk index out of range or repeated. */
+int spaco_stack_backward(const chunk_attn_desc* desc, int32_t seq_len, int32_t n_layers, const spaco_layer* layers,
+                         const void* h0, const float* dy, float* dh0, int32_t h_capacity, const int32_t* chunks,
+                         int32_t n_chunks, float relay_factor, void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel timing for benchmarks (instrumentation only; results are unchanged).
  * chunk_attn_profile_start() clears the record and, until
  * chunk_attn_profile_stop(), brackets every kernel this library launches with
@@ -193,8 +251,9 @@ enum {
   CA_KERNEL_ACCUMULATE = 4, /* prefix_grad_accumulate */
   CA_KERNEL_ZERO = 5,       /* zero fill used by sparse_chunk_bwd */
   CA_KERNEL_PROJ = 6,       /* projection GEMMs of qkv_proj_fwd / qkv_proj_bwd */
-  CA_KERNEL_PROJ_PREP = 7,  /* qkv_proj_bwd: the chunk's gradients rounded to bf16 */
-  CA_KERNEL_COUNT = 8
+  CA_KERNEL_PROJ_PREP = 7,  /* qkv_proj_bwd: the chunk's gradients rounded to bf16, weights transposed */
+  CA_KERNEL_RESIDUAL = 8,   /* spaco_stack_*: residual connections between layers */
+  CA_KERNEL_COUNT = 9
 };
 int chunk_attn_profile_start(void);
 int chunk_attn_profile_stop(void);

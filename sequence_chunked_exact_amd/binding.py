@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libchunk_attn.so")
 
 CA_F32, CA_BF16 = 0, 1
 CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD = 0, 1, 2
-KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7}
+KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7, "residual": 8}
 ERRORS = {0: "CA_OK", -1: "CA_ERR_NULL", -2: "CA_ERR_SHAPE", -3: "CA_ERR_DTYPE", -4: "CA_ERR_ALIGN",
           -5: "CA_ERR_WORKSPACE", -6: "CA_ERR_UNSUPPORTED", -7: "CA_ERR_HIP"}
 
@@ -42,6 +42,12 @@ class Desc(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class SpacoLayer(ctypes.Structure):
+    """One layer of the stack for spaco_stack_* (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("wq", "wk", "wv", "k_cache", "v_cache", "dk_acc", "dv_acc", "dwq", "dwk", "dwv")]
 
 
 class ChunkAttnError(RuntimeError):
@@ -68,6 +74,10 @@ def _load() -> ctypes.CDLL:
         "qkv_proj_bwd_workspace_size": (SZ, [D, I32]),
         "qkv_proj_fwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P]),
         "qkv_proj_bwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "spaco_stack_workspace_size": (SZ, [D, I32]),
+        "spaco_stack_forward": (ctypes.c_int, [D, I32, I32, ctypes.POINTER(SpacoLayer), P, I32, P, SZ, P]),
+        "spaco_stack_backward": (ctypes.c_int, [D, I32, I32, ctypes.POINTER(SpacoLayer), P, P, P, I32,
+                                                ctypes.POINTER(I32), I32, F, P, SZ, P]),
         "chunk_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "chunk_attn_last_error": (ctypes.c_char_p, []),
         "chunk_attn_profile_start": (ctypes.c_int, []),
@@ -246,6 +256,52 @@ def chunked_backward(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, *, chunk: int,
         chunk_attn_bwd(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, chunk_start=s,
                        chunk_len=min(chunk, T - s), q_row_offset=s, softmax_scale=softmax_scale,
                        workspace=workspace)
+
+
+def _stack_layers(layers):
+    arr = (SpacoLayer * len(layers))()
+    for i, lay in enumerate(layers):
+        for name, _ in SpacoLayer._fields_:
+            t = lay.get(name)
+            setattr(arr[i], name, None if t is None else _ptr(t))
+    return arr
+
+
+def stack_desc(h0, layers, *, chunk: int, softmax_scale: float = 1.0) -> Desc:
+    """Whole-sequence descriptor of a layer stack: h0 [B, T_h, Hq*d], caches [B, Hkv, T_cap, d]."""
+    B, Th, dm = h0.shape
+    _, Hkv, Tcap, d = layers[0]["k_cache"].shape
+    return Desc(B, dm // d, Hkv, d, Tcap, chunk, 0, 0, chunk, float(softmax_scale), _dtype_code(h0))
+
+
+def spaco_stack_workspace(desc: Desc, n_layers: int, like):
+    import torch
+    need = int(lib.spaco_stack_workspace_size(ctypes.byref(desc), int(n_layers)))
+    return torch.empty(max(need, 256), dtype=torch.uint8, device=like.device)
+
+
+def spaco_stack_forward(h0, layers, *, chunk: int, seq_len: Optional[int] = None, softmax_scale: float = 1.0,
+                        workspace=None):
+    """Inference-mode pass of the stack: fills every layer's k_cache / v_cache.
+    layers: list of dicts of tensors (wq, wk, wv, k_cache, v_cache[, dk_acc, dv_acc, dwq, dwk, dwv])."""
+    desc = stack_desc(h0, layers, chunk=chunk, softmax_scale=softmax_scale)
+    T = h0.shape[1] if seq_len is None else seq_len
+    ws = spaco_stack_workspace(desc, len(layers), h0) if workspace is None else workspace
+    _check(lib.spaco_stack_forward(ctypes.byref(desc), int(T), len(layers), _stack_layers(layers), _ptr(h0),
+                                   h0.shape[1], _ptr(ws), ws.numel(), _stream(h0)))
+
+
+def spaco_stack_backward(h0, dy, dh0, layers, *, chunk: int, chunks: Sequence[int], relay_factor: float,
+                         seq_len: Optional[int] = None, softmax_scale: float = 1.0, workspace=None):
+    """SpaCO's relayed backward over the drawn chunks (after spaco_stack_forward)."""
+    _contig(h0, dy, dh0)
+    desc = stack_desc(h0, layers, chunk=chunk, softmax_scale=softmax_scale)
+    T = h0.shape[1] if seq_len is None else seq_len
+    ws = spaco_stack_workspace(desc, len(layers), h0) if workspace is None else workspace
+    sel = (ctypes.c_int32 * len(chunks))(*[int(c) for c in chunks])
+    _check(lib.spaco_stack_backward(ctypes.byref(desc), int(T), len(layers), _stack_layers(layers), _ptr(h0),
+                                    _ptr(dy), _ptr(dh0), h0.shape[1], sel, len(chunks), float(relay_factor),
+                                    _ptr(ws), ws.numel(), _stream(h0)))
 
 
 def profile_start():

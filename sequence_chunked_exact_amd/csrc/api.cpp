@@ -401,3 +401,222 @@ int chunk_attn_profile_read(int32_t kernel, int64_t* launches, double* total_ms)
 }
 
 }  // extern "C"
+
+// ---- SpaCO over a stack of attention layers --------------------------------
+namespace {
+
+// Chunk-local buffers in the stack workspace, each on a 256-byte boundary.
+struct StackWs {
+  size_t hbuf, q, o, lse, dout, dq, dh_a, dh_b, attn_ws, proj_ws, total;
+  size_t h_stride, q_stride, lse_stride;  // per-layer strides (bytes)
+};
+
+StackWs stack_ws(const chunk_attn_desc* d, int32_t L) {
+  const size_t B = d->batch, C = d->chunk_len, Hq = d->n_q_heads, hd = d->head_dim;
+  const size_t dm = Hq * hd, es = d->dtype == CA_BF16 ? 2 : 4;
+  StackWs w{};
+  w.h_stride = round_up(B * C * dm * es);
+  w.q_stride = round_up(B * Hq * C * hd * es);
+  w.lse_stride = round_up(B * Hq * C * 4);
+  size_t at = 0;
+  w.hbuf = at;
+  at += w.h_stride * (size_t)std::max(L - 1, 1);
+  w.q = at;
+  at += w.q_stride * L;
+  w.o = at;
+  at += w.q_stride * L;
+  w.lse = at;
+  at += w.lse_stride * L;
+  w.dout = at;
+  at += w.q_stride;
+  w.dq = at;
+  at += round_up(B * Hq * C * hd * 4);
+  w.dh_a = at;
+  at += round_up(B * C * dm * 4);
+  w.dh_b = at;
+  at += round_up(B * C * dm * 4);
+  w.attn_ws = at;
+  at += delta_bytes(d);
+  w.proj_ws = at;
+  ca::ProjShape ps = proj_shape(d, (int32_t)dm, d->chunk_len, 0);
+  at += round_up(ca::proj_bwd_ws_bytes(ps));
+  w.total = at;
+  return w;
+}
+
+int check_stack(const chunk_attn_desc* d, int32_t seq_len, int32_t L, const spaco_layer* layers, const void* h0,
+                int32_t h_capacity, bool backward) {
+  int rc = check_desc(d, true);
+  if (rc) return rc;
+  if (L < 1 || L > 4096) return fail(CA_ERR_SHAPE, "n_layers %d", L);
+  if (!layers) return fail(CA_ERR_NULL, "layers is NULL");
+  const int64_t dm = (int64_t)d->n_q_heads * d->head_dim;
+  if (dm % 64 != 0 || dm > 65536) return fail(CA_ERR_SHAPE, "d_model = n_q_heads * head_dim = %lld", (long long)dm);
+  if (d->q_capacity < d->chunk_len) return fail(CA_ERR_SHAPE, "q_capacity %d < chunk_len", d->q_capacity);
+  if (seq_len < 1 || seq_len > d->kv_capacity || seq_len > h_capacity)
+    return fail(CA_ERR_SHAPE, "seq_len %d must be in [1, min(kv_capacity, h_capacity)]", seq_len);
+  if ((int64_t)d->batch * h_capacity * dm > ((int64_t)1 << 40)) return fail(CA_ERR_SHAPE, "h too large");
+  if ((rc = check_ptrs({h0}))) return rc;
+  for (int32_t l = 0; l < L; ++l) {
+    const spaco_layer& y = layers[l];
+    if ((rc = check_ptrs({y.wq, y.wk, y.wv, y.k_cache, y.v_cache}))) return rc;
+    if (backward && (rc = check_ptrs({y.dk_acc, y.dv_acc, y.dwq, y.dwk, y.dwv}))) return rc;
+  }
+  return CA_OK;
+}
+
+// Shapes for layer-local launches on chunk j (rows [s, s + len)).
+ca::Shape stack_attn_shape(const chunk_attn_desc* d, int32_t s, int32_t len) {
+  ca::Shape a = shape_of(d);
+  a.q_cap = d->chunk_len;
+  a.q_off = 0;
+  a.start = s;
+  a.len = len;
+  return a;
+}
+ca::ProjShape stack_proj_shape(const chunk_attn_desc* d, int32_t l, int32_t h_capacity, int32_t s, int32_t len) {
+  ca::ProjShape p = proj_shape(d, d->n_q_heads * d->head_dim, l == 0 ? h_capacity : d->chunk_len, l == 0 ? s : 0);
+  p.q_cap = d->chunk_len;
+  p.q_off = 0;
+  p.kv_cap = d->kv_capacity;
+  p.start = s;
+  p.len = len;
+  return p;
+}
+
+// Chunk j through every layer: Q/K/V (K, V into the caches), attention, and
+// the residual sum feeding the next layer. Leaves each layer's Q, O, LSE and
+// input rows in the workspace for a following backward.
+hipError_t stack_chunk_forward(const chunk_attn_desc* d, int32_t L, const spaco_layer* layers, const void* h0,
+                               int32_t h_capacity, int32_t s, int32_t len, char* ws, const StackWs& w,
+                               hipStream_t st) {
+  for (int32_t l = 0; l < L; ++l) {
+    const spaco_layer& y = layers[l];
+    const void* hin = l == 0 ? h0 : (const void*)(ws + w.hbuf + (size_t)(l - 1) * w.h_stride);
+    void* q = ws + w.q + (size_t)l * w.q_stride;
+    void* o = ws + w.o + (size_t)l * w.q_stride;
+    float* lse = (float*)(ws + w.lse + (size_t)l * w.lse_stride);
+    hipError_t e = ca::launch_proj_fwd(stack_proj_shape(d, l, h_capacity, s, len), hin, y.wq, y.wk, y.wv, q,
+                                       y.k_cache, y.v_cache, st);
+    if (e == hipSuccess) e = ca::launch_fwd(stack_attn_shape(d, s, len), q, y.k_cache, y.v_cache, o, lse, st);
+    if (e == hipSuccess && l + 1 < L) {
+      ca::ResidualShape r{d->batch, d->n_q_heads, d->head_dim, len, d->dtype,
+                          l == 0 ? h_capacity : d->chunk_len, l == 0 ? s : 0, d->chunk_len, 0, d->chunk_len, 0};
+      e = ca::launch_residual_fwd(r, hin, o, ws + w.hbuf + (size_t)l * w.h_stride, st);
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spaco_stack_workspace_size(const chunk_attn_desc* d, int32_t n_layers) {
+  if (check_desc(d, true) != CA_OK || n_layers < 1 || n_layers > 4096) return 0;
+  if (((int64_t)d->n_q_heads * d->head_dim) % 64 != 0) return 0;
+  return stack_ws(d, n_layers).total;
+}
+
+int spaco_stack_forward(const chunk_attn_desc* d, int32_t seq_len, int32_t n_layers, const spaco_layer* layers,
+                        const void* h0, int32_t h_capacity, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_stack(d, seq_len, n_layers, layers, h0, h_capacity, false);
+  if (rc) return rc;
+  const StackWs w = stack_ws(d, n_layers);
+  if ((rc = check_ws(ws, ws_bytes, w.total))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int32_t C = d->chunk_len;
+  for (int32_t s = 0; s < seq_len; s += C) {
+    hipError_t e = stack_chunk_forward(d, n_layers, layers, h0, h_capacity, s, std::min(C, seq_len - s),
+                                       (char*)ws, w, st);
+    if (e != hipSuccess) return hip_fail(e, "spaco_stack_forward");
+  }
+  return CA_OK;
+}
+
+int spaco_stack_backward(const chunk_attn_desc* d, int32_t seq_len, int32_t n_layers, const spaco_layer* layers,
+                         const void* h0, const float* dy, float* dh0, int32_t h_capacity, const int32_t* chunks,
+                         int32_t n_chunks, float relay_factor, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_stack(d, seq_len, n_layers, layers, h0, h_capacity, true);
+  if (rc) return rc;
+  if ((rc = check_ptrs({dy, dh0}))) return rc;
+  if (!chunks) return fail(CA_ERR_NULL, "chunks is NULL");
+  if (!(relay_factor == relay_factor) || relay_factor > 3.0e38f || relay_factor < -3.0e38f)
+    return fail(CA_ERR_SHAPE, "relay_factor is not finite");
+  const int32_t C = d->chunk_len;
+  const int32_t kch = (int32_t)(((int64_t)seq_len + C - 1) / C);
+  if (n_chunks < 1 || n_chunks > kch) return fail(CA_ERR_SHAPE, "n_chunks %d not in [1, %d]", n_chunks, kch);
+  std::vector<int32_t> order(chunks, chunks + n_chunks);
+  std::sort(order.begin(), order.end());
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    if (order[i] < 0 || order[i] >= kch) return fail(CA_ERR_SHAPE, "chunk index %d out of [0, %d)", order[i], kch);
+    if (i > 0 && order[i] == order[i - 1]) return fail(CA_ERR_SHAPE, "chunk index %d repeated", order[i]);
+  }
+  const StackWs w = stack_ws(d, n_layers);
+  if ((rc = check_ws(ws, ws_bytes, w.total))) return rc;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const int32_t L = n_layers, B = d->batch, Hq = d->n_q_heads, Hkv = d->n_kv_heads, hd = d->head_dim;
+  const int32_t dm = Hq * hd;
+  const size_t nkv = (size_t)B * Hkv * d->kv_capacity * hd;
+  hipError_t e = hipSuccess;
+  for (int32_t l = 0; l < L && e == hipSuccess; ++l) {
+    e = ca::launch_zero(layers[l].dk_acc, nkv, st);
+    if (e == hipSuccess) e = ca::launch_zero(layers[l].dv_acc, nkv, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "spaco_stack_backward zero");
+
+  void* dout = wsb + w.dout;
+  float* dq = (float*)(wsb + w.dq);
+  float* dh_cur = (float*)(wsb + w.dh_a);
+  float* dh_nxt = (float*)(wsb + w.dh_b);
+  for (int32_t idx = n_chunks - 1; idx >= 0; --idx) {
+    const int32_t s = order[idx] * C, len = std::min(C, seq_len - s);
+    // rebuild the chunk's graph from the caches
+    e = stack_chunk_forward(d, L, layers, h0, h_capacity, s, len, wsb, w, st);
+    if (e != hipSuccess) return hip_fail(e, "spaco_stack_backward rebuild");
+    for (int32_t l = L - 1; l >= 0; --l) {
+      const spaco_layer& y = layers[l];
+      const void* hin = l == 0 ? h0 : (const void*)(wsb + w.hbuf + (size_t)(l - 1) * w.h_stride);
+      const void* q = wsb + w.q + (size_t)l * w.q_stride;
+      const void* o = wsb + w.o + (size_t)l * w.q_stride;
+      const float* lse = (const float*)(wsb + w.lse + (size_t)l * w.lse_stride);
+      // relay: what later drawn chunks accumulated in this chunk's cache rows
+      if (relay_factor != 1.f) {
+        const size_t off = (size_t)s * hd;
+        e = ca::launch_accumulate(y.dk_acc + off, y.dk_acc + off, B, Hkv, d->kv_capacity, d->kv_capacity, hd, len,
+                                  relay_factor - 1.f, st);
+        if (e == hipSuccess)
+          e = ca::launch_accumulate(y.dv_acc + off, y.dv_acc + off, B, Hkv, d->kv_capacity, d->kv_capacity, hd, len,
+                                    relay_factor - 1.f, st);
+      }
+      // dO_l = dH_{l+1} of the chunk's rows (dy at the top)
+      const bool top = l == L - 1;
+      const float* src = top ? dy : dh_cur;
+      const int32_t src_cap = top ? h_capacity : C, src_off = top ? s : 0;
+      if (e == hipSuccess) {
+        ca::ResidualShape r{B, Hq, hd, len, d->dtype, src_cap, src_off, 0, 0, C, 0};
+        e = ca::launch_residual_bwd(r, src, dout, st);
+      }
+      if (e == hipSuccess)
+        e = ca::launch_bwd(stack_attn_shape(d, s, len), q, y.k_cache, y.v_cache, o, lse, dout, 1.f, dq, y.dk_acc,
+                           y.dv_acc, (float*)(wsb + w.attn_ws), st);
+      // dH_l = dH_{l+1} + (dQ W_q^T + dK W_k^T + dV W_v^T) over the chunk's rows
+      float* dst = l == 0 ? dh0 : dh_nxt;
+      const int32_t dst_cap = l == 0 ? h_capacity : C, dst_off = l == 0 ? s : 0;
+      if (e == hipSuccess)
+        e = ca::launch_proj_bwd(stack_proj_shape(d, l, h_capacity, s, len), hin, y.wq, y.wk, y.wv, dq, y.dk_acc,
+                                y.dv_acc, y.dwq, y.dwk, y.dwv, dst, wsb + w.proj_ws, st);
+      if (e == hipSuccess)
+        e = ca::launch_accumulate(dst + (size_t)dst_off * dm, src + (size_t)src_off * dm, B, 1, dst_cap, src_cap, dm,
+                                  len, 1.f, st);
+      if (e != hipSuccess) return hip_fail(e, "spaco_stack_backward layer");
+      if (l > 0) std::swap(dh_cur, dh_nxt);
+    }
+  }
+  return CA_OK;
+}
+
+}  // extern "C"

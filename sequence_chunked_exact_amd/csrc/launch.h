@@ -59,6 +59,21 @@ hipError_t launch_proj_bwd(const ProjShape& s, const void* h, const void* wq, co
                            const float* dq, const float* dk, const float* dv, float* dwq, float* dwk, float* dwv,
                            float* dh, void* ws, hipStream_t st);
 
+// Residual connections of a layer stack over one chunk's rows (d_model =
+// hq * head_dim). Row-major operands are [batch][cap][d_model] with the chunk
+// at row `off`; the per-head operand is [batch][hq][o_cap][head_dim] at row
+// o_off.
+struct ResidualShape {
+  int batch, hq, head_dim, len, dtype;
+  int a_cap, a_off;  // h_in (forward) or dh (backward, float32)
+  int c_cap, c_off;  // h_out (forward)
+  int o_cap, o_off;  // o (forward) or dout (backward)
+};
+// h_out = h_in + o (heads side by side), in dtype.
+hipError_t launch_residual_fwd(const ResidualShape& s, const void* h_in, const void* o, void* h_out, hipStream_t st);
+// dout = dh (float32, row-major) in the per-head layout, in dtype.
+hipError_t launch_residual_bwd(const ResidualShape& s, const float* dh, void* dout, hipStream_t st);
+
 // Fill n floats with zero (a kernel, so it is safe inside captured graphs).
 hipError_t launch_zero(float* p, size_t n, hipStream_t st);
 

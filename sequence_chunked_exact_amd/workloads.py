@@ -197,3 +197,77 @@ def to_torch(raw: np.ndarray, device="cpu"):
     else:
         t = torch.from_numpy(raw)
     return t.to(device)
+
+
+@dataclasses.dataclass(frozen=True)
+class StackWorkload:
+    """A stack of attention layers with residual connections (d_model = Hq * d) for
+    SpaCO's relayed backward: input H_0 [B, T, d_model], per-layer W_q/W_k/W_v, and
+    the loss gradient dy = dJ/dH_L. t of the k chunks are drawn per step; the
+    relayed cache gradient is multiplied by min(k/t, relay_cap)."""
+    name: str
+    batch: int
+    seq_len: int
+    chunk: int
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str
+    t: int
+    relay_cap: Optional[float]
+    seed: int
+
+    @property
+    def d_model(self) -> int:
+        return self.n_q_heads * self.head_dim
+
+    @property
+    def n_chunks(self) -> int:
+        return -(-self.seq_len // self.chunk)
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def relay_factor(self) -> float:
+        g = self.n_chunks / self.t
+        return g if self.relay_cap is None else min(g, self.relay_cap)
+
+
+STACK_WORKLOADS = {
+    # four LLaMA3-8B-shaped attention layers at 16K tokens, t = 4 of k = 16
+    # chunks, the relay factor k/t = 4 capped at 2 as the deployed method does
+    "8b_stack4_spaco": StackWorkload("8b_stack4_spaco", 1, 16384, 1024, 4, 32, 8, 128, "bf16", 4, 2.0, 11),
+}
+
+
+def make_stack_inputs(wl: StackWorkload, seq_len: Optional[int] = None, keep_f64: bool = True) -> Inputs:
+    """Draw H_0 ~ N(0, 1), weights ~ N(0, 1/d_model) per layer, dy ~ N(0, 1), rounded to
+    the storage type like make_inputs (dy stays float32)."""
+    T = wl.seq_len if seq_len is None else seq_len
+    B, Hq, Hkv, d, dm = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.d_model
+    rng = np.random.default_rng(wl.seed)
+    ws = 1.0 / math.sqrt(dm)
+    arrays = {"h0": _draw(rng, (B, T, dm), 1.0)}
+    for l in range(wl.n_layers):
+        arrays[f"wq{l}"] = _draw(rng, (dm, Hq * d), ws)
+        arrays[f"wk{l}"] = _draw(rng, (dm, Hkv * d), ws)
+        arrays[f"wv{l}"] = _draw(rng, (dm, Hkv * d), ws)
+    arrays["dy"] = _draw(rng, (B, T, dm), 1.0)
+    raw, f64 = {}, {}
+    for name in list(arrays):
+        a = arrays[name]
+        if wl.dtype == "bf16" and name != "dy":
+            bits = round_to_bf16_bits(a)
+            raw[name] = bits
+            if keep_f64:
+                f64[name] = bf16_bits_to_f64(bits)
+        else:
+            f32 = a.astype(np.float32)
+            raw[name] = f32
+            if keep_f64:
+                f64[name] = f32.astype(np.float64)
+        arrays[name] = None
+    return Inputs(wl, f64, raw)

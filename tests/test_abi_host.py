@@ -180,3 +180,34 @@ def test_projection_workspace_and_errors():
     assert proj_bwd(d, hcap=700) == -2               # h rows [512, 768) past the capacity
     assert proj_bwd(d, h=None) == -1
     assert proj_bwd(desc(head_dim=96)) == -6
+
+
+def test_stack_errors():
+    d = desc(chunk_start=0, chunk_len=128, q_capacity=128, n_q_heads=2, n_kv_heads=1, kv_capacity=1024)
+    lay = (b.SpacoLayer * 2)()
+    for i in range(2):
+        for name, _ in b.SpacoLayer._fields_:
+            setattr(lay[i], name, FAKE)
+    sel = (ctypes.c_int32 * 3)(0, 3, 5)
+    need = lib.spaco_stack_workspace_size(ctypes.byref(d), 2)
+    assert need > 0
+    assert lib.spaco_stack_workspace_size(ctypes.byref(d), 0) == 0
+
+    def bwd_(seq_len=1024, L=2, layers=lay, chunks=sel, n=3, factor=2.0, ws_bytes=need, dy=FAKE, dd=d):
+        return lib.spaco_stack_backward(ctypes.byref(dd), seq_len, L, layers, FAKE, dy, FAKE, 1024, chunks, n,
+                                        factor, FAKE, ws_bytes, None)
+
+    assert bwd_(L=0) == -2
+    assert bwd_(layers=None) == -1
+    assert bwd_(dy=None) == -1
+    assert bwd_(ws_bytes=need - 1) == -5
+    assert bwd_(factor=float("nan")) == -2
+    assert bwd_(n=9) == -2                                    # more chunks than k = 8
+    assert bwd_(chunks=(ctypes.c_int32 * 3)(0, 8, 5)) == -2   # index out of range
+    assert bwd_(chunks=(ctypes.c_int32 * 3)(1, 3, 1)) == -2   # repeated
+    assert bwd_(seq_len=2048) == -2                           # past the caches
+    assert bwd_(dd=desc(chunk_len=128, q_capacity=64, n_q_heads=2, n_kv_heads=1, kv_capacity=1024)) == -2  # q_capacity < C
+    lay[1].dwk = None
+    assert bwd_() == -1
+    assert lib.spaco_stack_forward(ctypes.byref(d), 1024, 2, lay, FAKE, 1024, FAKE, need - 1, None) == -5
+
