@@ -244,6 +244,163 @@ def layer_main(args):
     print(json.dumps(out), flush=True)
 
 
+def stack_flops(wl, T, drawn):
+    """FLOPs of one SpaCO step on a layer stack, by kernel: the inference-mode pass
+    over every chunk and layer, then per drawn chunk the rebuild (projections and
+    attention forward) and the backward (attention and projections)."""
+    Hq, Hkv, d, dm, C, L = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.d_model, wl.chunk, wl.n_layers
+    proj_row = 2 * dm * (Hq + 2 * Hkv) * d          # one row of Q|K|V
+    f = {"proj": 0, "fwd": 0, "dkdv": 0, "dq": 0}
+    for s in range(0, T, C):
+        c = min(C, T - s)
+        f["proj"] += L * c * proj_row
+        f["fwd"] += L * 4 * d * causal_pairs(s, c) * Hq
+    for j in drawn:
+        s = j * C
+        c = min(C, T - s)
+        pairs = causal_pairs(s, c)
+        f["proj"] += L * c * proj_row * 3           # rebuild, dW, dH
+        f["fwd"] += L * 4 * d * pairs * Hq          # rebuild
+        f["dkdv"] += L * 8 * d * pairs * Hq
+        f["dq"] += L * 2 * d * pairs * Hq
+    return f
+
+
+def stack_cpu_baseline(wl, raw, sample_len=4096):
+    """The float64 stack oracle (oracle.stack.spaco_estimate) on the workload cut to its
+    first `sample_len` positions with the last chunk drawn, its rate in the GPU path's
+    FLOP accounting extrapolated to the full step."""
+    import numpy as np
+    from oracle import stack as S
+    from sequence_chunked_exact_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+
+    def f64(a):
+        return W.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+    Ts = min(sample_len, wl.seq_len)
+    h0 = f64(raw["h0"][:, :Ts])
+    dy = f64(raw["dy"][:, :Ts])
+    weights = [(f64(raw[f"wq{l}"]), f64(raw[f"wk{l}"]), f64(raw[f"wv{l}"])) for l in range(wl.n_layers)]
+    last = (Ts - 1) // wl.chunk
+    t0 = time.perf_counter()
+    S.spaco_estimate(h0, weights, dy, wl.n_q_heads, wl.n_kv_heads, wl.softmax_scale, wl.chunk, [last],
+                     wl.relay_factor)
+    dt = time.perf_counter() - t0
+    rate = sum(stack_flops(wl, Ts, [last]).values()) / dt
+    return rate, dt, threads
+
+
+def stack_main(args):
+    import numpy as np
+    import torch
+    from sequence_chunked_exact_amd import binding as B
+    from sequence_chunked_exact_amd import workloads as W
+
+    wl = W.STACK_WORKLOADS["8b_stack4_spaco"]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {wl.name} inputs")
+    inp = W.make_stack_inputs(wl, keep_f64=False)
+    r = inp.raw
+    h0, dy = W.to_torch(r["h0"], dev), W.to_torch(r["dy"], dev)
+    Bt, T, dm = h0.shape
+    Hq, Hkv, d, C, L = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.chunk, wl.n_layers
+    f32 = torch.float32
+    layers = []
+    for l in range(L):
+        layers.append({"wq": W.to_torch(r[f"wq{l}"], dev), "wk": W.to_torch(r[f"wk{l}"], dev),
+                       "wv": W.to_torch(r[f"wv{l}"], dev),
+                       "k_cache": torch.zeros(Bt, Hkv, T, d, dtype=h0.dtype, device=dev),
+                       "v_cache": torch.zeros(Bt, Hkv, T, d, dtype=h0.dtype, device=dev),
+                       "dk_acc": torch.empty(Bt, Hkv, T, d, dtype=f32, device=dev),
+                       "dv_acc": torch.empty(Bt, Hkv, T, d, dtype=f32, device=dev),
+                       "dwq": torch.zeros(dm, Hq * d, dtype=f32, device=dev),
+                       "dwk": torch.zeros(dm, Hkv * d, dtype=f32, device=dev),
+                       "dwv": torch.zeros(dm, Hkv * d, dtype=f32, device=dev)})
+    dh0 = torch.zeros(Bt, T, dm, dtype=f32, device=dev)
+    desc = B.stack_desc(h0, layers, chunk=C, softmax_scale=wl.softmax_scale)
+    ws = B.spaco_stack_workspace(desc, L, h0)
+    k = wl.n_chunks
+    drawn = B.chunk_select(k, wl.t, args.seed)
+    gamma = wl.relay_factor
+
+    def step():
+        for lay in layers:
+            for n_ in ("dwq", "dwk", "dwv"):
+                lay[n_].zero_()
+        B.spaco_stack_forward(h0, layers, chunk=C, softmax_scale=wl.softmax_scale, workspace=ws)
+        B.spaco_stack_backward(h0, dy, dh0, layers, chunk=C, chunks=drawn, relay_factor=gamma,
+                               softmax_scale=wl.softmax_scale, workspace=ws)
+
+    log(f"[bench] stack warmup {args.warmup}; drawn chunks {drawn}, relay factor {gamma}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} stack steps")
+    B.profile_start()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    B.profile_stop()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = B.profile_read()
+    kflops = stack_flops(wl, T, drawn)
+    total = sum(kflops.values())
+    kernels = {n_: {"launches_per_step": c_ / args.steps, "ms_per_step": t_ / args.steps, "avg_us": t_ / c_ * 1e3}
+               for n_, (c_, t_) in prof.items() if c_}
+    log(f"[bench] {ms:.3f} ms/stack step; kernels " + json.dumps(kernels))
+    dom = max((n_ for n_ in kernels if n_ in kflops), key=lambda n_: kernels[n_]["ms_per_step"])
+    n_l, t_l = prof[dom]
+    per_launch = kflops[dom] / (n_l / args.steps)
+    achieved = per_launch / (t_l / n_l * 1e-3) / 1e12
+    from sequence_chunked_exact_amd.profile_summary import read_traffic
+    out = {
+        "metric": "SpaCO step on an attention-layer stack (inference pass + relayed backward of t drawn chunks) "
+                  "tokens/s, 1 GPU",
+        "value": Bt * T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "tflops": total / (ms * 1e-3) / 1e12,
+        "pct_bf16_peak": 100.0 * total / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "config": {"workload": wl.name, "batch": Bt, "seq_len": T, "chunk": C, "n_layers": L, "d_model": dm,
+                   "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "t": wl.t, "k": k, "drawn": drawn,
+                   "relay_factor": gamma, "flops_per_step": total, "flops_by_kernel": kflops},
+        "kernels": kernels,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{wl.name}.md"), dom),
+                     "avg_launch_us": t_l / n_l * 1e3, "flops_per_launch": per_launch},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        rate, dt, threads = stack_cpu_baseline(wl, r)
+        out["cpu_baseline"] = {"value": Bt * T / (total / rate), "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"float64 stack oracle on the first 4096 positions with the last chunk "
+                                         f"drawn ({dt:.1f} s, {rate / 1e9:.1f} GFLOP/s in this step's FLOP "
+                                         f"accounting), extrapolated to the full step by FLOPs",
+                               "seconds": dt}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,6 +410,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layer", action="store_true",
                     help="measure the whole attention layer step (QKV projections + attention)")
+    ap.add_argument("--stack", action="store_true",
+                    help="measure SpaCO's step on a stack of attention layers (relayed cache gradients)")
+    ap.add_argument("--seed", type=int, default=0, help="chunk draw seed for --stack")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -261,6 +421,8 @@ def main():
 
     if args.layer:
         return layer_main(args)
+    if args.stack:
+        return stack_main(args)
 
     import numpy as np
     import torch
