@@ -34,7 +34,9 @@ COPY_BYTES = 1 << 30
 N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
 SHORT = {"fwd_kernel": "fwd", "dkdv_kernel": "dkdv", "dq_kernel": "dq", "delta_kernel": "delta",
-         "zero_kernel": "zero", "accumulate_kernel": "accumulate", "gemm_kernel": "proj"}
+         "zero_kernel": "zero", "accumulate_kernel": "accumulate", "gemm_kernel": "proj",
+         "residual_fwd_kernel": "residual_fwd", "residual_bwd_kernel": "residual_bwd", "wt_kernel": "proj_prep",
+         "gcat_kernel": "proj_prep"}
 
 
 def kernel_sources(kernel: str) -> list:
@@ -52,7 +54,7 @@ def kernel_source_sha256(kernel: str) -> str:
 
 
 def short_name(full: str) -> str:
-    for key, val in SHORT.items():
+    for key, val in sorted(SHORT.items(), key=lambda kv: -len(kv[0])):  # most specific first
         if key in full:
             return val
     return full[:40]
@@ -63,8 +65,7 @@ def per_dispatch(path: str, counter: str, name_filter=None):
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        if name_filter and name_filter not in short_name(r["Kernel_Name"]) and \
-                name_filter not in r["Kernel_Name"]:
+        if name_filter and short_name(r["Kernel_Name"]) != name_filter:
             continue
         vals.append(float(r["Counter_Value"]))
     return vals
