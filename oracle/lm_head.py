@@ -1,0 +1,93 @@
+"""Oracle: the language-model head's supervised fine-tuning loss and its
+gradients, dense and streamed over sequence partitions, in float64.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this module;
+only the tests and the benchmark's CPU-baseline leg use it. It shares no code
+with the HIP library.
+
+What it computes. StreamBP streams the language-modeling head by partitioning
+the logits along the sequence, ps_head = 100 positions at a time, the SFT loss
+being separable over positions (StreamBP review, "Core claim"; "Assumptions":
+Eq. (3), ps_head = 100). The page does not print Eq. (3); the reading here is
+the standard next-token objective: with logits z_t = W h_t (W [vocab][d_model])
+and target labels y_t (-1: not a target),
+
+    L = scale * sum_{t: y_t >= 0} (logsumexp(z_t) - z_t[y_t]),  scale = 1 / #targets
+
+    dz_t = scale * (softmax(z_t) - onehot(y_t))   (0 where y_t < 0)
+    dh_t = W^T dz_t,      dW = sum_t dz_t h_t^T
+
+Streaming over partitions of the positions gives the same sums (Eq. (1) of the
+page: a weight gradient is a sum over output chunks); the loss is the sum of the
+partitions' terms. Matrix products are numpy's float64 matmul.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _lse(z):
+    m = z.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(z - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
+def target_scale(labels):
+    """1 / number of target positions (0 if there are none)."""
+    n = int((np.asarray(labels) >= 0).sum())
+    return 1.0 / n if n else 0.0
+
+
+def sft_partition(h, w, labels, rows, scale):
+    """Loss terms and gradients of the positions ``rows`` (a range of the
+    sequence) for every batch entry: (loss, dh over those rows [B, len, d_model],
+    dW contribution [vocab, d_model])."""
+    h = np.asarray(h, dtype=np.float64)[:, rows]
+    w = np.asarray(w, dtype=np.float64)
+    y = np.asarray(labels)[:, rows]
+    z = h @ w.T                                     # [B, len, V]
+    lse = _lse(z)
+    tgt = y >= 0
+    yc = np.where(tgt, y, 0)
+    z_y = np.take_along_axis(z, yc[..., None], axis=-1)[..., 0]
+    loss = scale * float(np.where(tgt, lse - z_y, 0.0).sum())
+    p = np.exp(z - lse[..., None])
+    onehot = np.zeros_like(p)
+    np.put_along_axis(onehot, yc[..., None], 1.0, axis=-1)
+    dz = scale * (p - onehot) * tgt[..., None]
+    dh = dz @ w
+    dw = sum(dz[b].T @ h[b] for b in range(h.shape[0]))
+    return loss, dh, dw
+
+
+def sft_dense(h, w, labels, scale=None):
+    """(loss, dh [B, T, d_model], dW [vocab, d_model]) over the whole sequence."""
+    T = np.asarray(h).shape[1]
+    scale = target_scale(labels) if scale is None else scale
+    return sft_partition(h, w, labels, slice(0, T), scale)
+
+
+def sft_streamed(h, w, labels, ps, scale=None):
+    """The same quantities accumulated partition by partition (ps positions each)."""
+    h = np.asarray(h, dtype=np.float64)
+    B, T, dm = h.shape
+    scale = target_scale(labels) if scale is None else scale
+    loss = 0.0
+    dh = np.zeros((B, T, dm))
+    dw = np.zeros(np.asarray(w).shape)
+    for s in range(0, T, ps):
+        rows = slice(s, min(T, s + ps))
+        l_i, dh_i, dw_i = sft_partition(h, w, labels, rows, scale)
+        loss += l_i
+        dh[:, rows] = dh_i
+        dw += dw_i
+    return loss, dh, dw
+
+
+def row_losses(h, w, labels):
+    """Unscaled per-position loss terms [B, T] (0 where the label is -1)."""
+    h = np.asarray(h, dtype=np.float64)
+    z = h @ np.asarray(w, dtype=np.float64).T
+    y = np.asarray(labels)
+    tgt = y >= 0
+    z_y = np.take_along_axis(z, np.where(tgt, y, 0)[..., None], axis=-1)[..., 0]
+    return np.where(tgt, _lse(z) - z_y, 0.0)
