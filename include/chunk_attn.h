@@ -235,6 +235,49 @@ int spaco_stack_backward(const chunk_attn_desc* desc, int32_t seq_len, int32_t n
                          const void* h0, const float* dy, float* dh0, int32_t h_capacity, const int32_t* chunks,
                          int32_t n_chunks, float relay_factor, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Streamed language-model head, supervised fine-tuning ----------------
+ *
+ * StreamBP streams the LM head by partitioning the logits along the sequence
+ * (ps_head = 100 positions at a time), the SFT loss being separable over
+ * positions (StreamBP review, "Core claim"; "Assumptions": Eq. (3), ps_head).
+ * With logits z_t = W h_t and labels y_t (-1: not a target), the loss is
+ * loss_scale * sum_t (logsumexp(z_t) - z_t[y_t]) over target positions, and
+ *   dz_t = loss_scale * (softmax(z_t) - onehot(y_t)),  dh_t = W^T dz_t,
+ *   dW += sum_t dz_t h_t^T.
+ * Only the partition's logits exist at a time (in the workspace). */
+typedef struct {
+  int32_t batch;         /* >= 1 */
+  int32_t seq_capacity;  /* rows per batch entry in h, labels, row_loss and dh */
+  int32_t d_model;       /* multiple of 64, <= 65536 */
+  int32_t vocab;         /* multiple of 64 */
+  int32_t dtype;         /* CA_BF16 (the only supported storage type; else CA_ERR_UNSUPPORTED) */
+} lm_head_desc;
+
+/* wt [d_model][vocab] = w^T for w [vocab][d_model] (bf16, device). The
+ * partition call reads the logits product's weight operand from wt; call once
+ * per weight update. */
+int lm_head_transpose(const lm_head_desc* desc, const void* w, void* wt, void* stream);
+
+/* Workspace bytes of lm_head_sft_partition for partitions of up to `rows`
+ * positions: the partition's float32 logits and bf16 logit gradients (0 for
+ * invalid arguments). */
+size_t lm_head_sft_workspace_size(const lm_head_desc* desc, int32_t rows);
+
+/* One partition, positions [row_start, row_start + rows) of every batch entry:
+ * h [batch][seq_capacity][d_model] bf16; w [vocab][d_model] bf16 and its
+ * transpose wt; labels [batch][seq_capacity] int32 (a position is a target iff
+ * 0 <= label < vocab; other values, e.g. -1, mark prompt or padding positions);
+ * loss_scale multiplies the gradients
+ * (1 / number of targets for a mean). Writes row_loss [batch][seq_capacity]
+ * float32 (the unscaled loss of each position of the partition, 0 for
+ * non-targets) and dh rows of the partition (float32, OVERWRITTEN); adds into
+ * dw [vocab][d_model] float32. Errors: CA_ERR_NULL / CA_ERR_ALIGN for
+ * pointers, CA_ERR_SHAPE for sizes or rows outside the capacity,
+ * CA_ERR_UNSUPPORTED for a dtype other than bf16, CA_ERR_WORKSPACE. */
+int lm_head_sft_partition(const lm_head_desc* desc, int32_t row_start, int32_t rows, const void* h, const void* w,
+                          const void* wt, const int32_t* labels, float loss_scale, float* row_loss, float* dh,
+                          float* dw, void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel timing for benchmarks (instrumentation only; results are unchanged).
  * chunk_attn_profile_start() clears the record and, until
  * chunk_attn_profile_stop(), brackets every kernel this library launches with
@@ -253,7 +296,9 @@ enum {
   CA_KERNEL_PROJ = 6,       /* projection GEMMs of qkv_proj_fwd / qkv_proj_bwd */
   CA_KERNEL_PROJ_PREP = 7,  /* qkv_proj_bwd: the chunk's gradients rounded to bf16, weights transposed */
   CA_KERNEL_RESIDUAL = 8,   /* spaco_stack_*: residual connections between layers */
-  CA_KERNEL_COUNT = 9
+  CA_KERNEL_HEAD = 9,       /* lm_head_sft_partition: logits, dH and dW products */
+  CA_KERNEL_HEAD_AUX = 10,  /* lm_head_*: softmax/cross-entropy rows, weight transpose */
+  CA_KERNEL_COUNT = 11
 };
 int chunk_attn_profile_start(void);
 int chunk_attn_profile_stop(void);

@@ -37,10 +37,10 @@ def target_scale(labels):
     return 1.0 / n if n else 0.0
 
 
-def sft_partition(h, w, labels, rows, scale):
+def sft_partition(h, w, labels, rows, scale, with_dw=True):
     """Loss terms and gradients of the positions ``rows`` (a range of the
     sequence) for every batch entry: (loss, dh over those rows [B, len, d_model],
-    dW contribution [vocab, d_model])."""
+    dW contribution [vocab, d_model], or None without ``with_dw``)."""
     h = np.asarray(h, dtype=np.float64)[:, rows]
     w = np.asarray(w, dtype=np.float64)
     y = np.asarray(labels)[:, rows]
@@ -55,7 +55,7 @@ def sft_partition(h, w, labels, rows, scale):
     np.put_along_axis(onehot, yc[..., None], 1.0, axis=-1)
     dz = scale * (p - onehot) * tgt[..., None]
     dh = dz @ w
-    dw = sum(dz[b].T @ h[b] for b in range(h.shape[0]))
+    dw = sum(dz[b].T @ h[b] for b in range(h.shape[0])) if with_dw else None
     return loss, dh, dw
 
 

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libchunk_attn.so")
 
 CA_F32, CA_BF16 = 0, 1
 CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD = 0, 1, 2
-KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7, "residual": 8}
+KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7, "residual": 8, "head": 9, "head_aux": 10}
 ERRORS = {0: "CA_OK", -1: "CA_ERR_NULL", -2: "CA_ERR_SHAPE", -3: "CA_ERR_DTYPE", -4: "CA_ERR_ALIGN",
           -5: "CA_ERR_WORKSPACE", -6: "CA_ERR_UNSUPPORTED", -7: "CA_ERR_HIP"}
 
@@ -48,6 +48,12 @@ class SpacoLayer(ctypes.Structure):
     """One layer of the stack for spaco_stack_* (device pointers)."""
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("wq", "wk", "wv", "k_cache", "v_cache", "dk_acc", "dv_acc", "dwq", "dwk", "dwv")]
+
+
+class HeadDesc(ctypes.Structure):
+    """lm_head_desc of include/chunk_attn.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("seq_capacity", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class ChunkAttnError(RuntimeError):
@@ -78,6 +84,10 @@ def _load() -> ctypes.CDLL:
         "spaco_stack_forward": (ctypes.c_int, [D, I32, I32, ctypes.POINTER(SpacoLayer), P, I32, P, SZ, P]),
         "spaco_stack_backward": (ctypes.c_int, [D, I32, I32, ctypes.POINTER(SpacoLayer), P, P, P, I32,
                                                 ctypes.POINTER(I32), I32, F, P, SZ, P]),
+        "lm_head_transpose": (ctypes.c_int, [ctypes.POINTER(HeadDesc), P, P, P]),
+        "lm_head_sft_workspace_size": (SZ, [ctypes.POINTER(HeadDesc), I32]),
+        "lm_head_sft_partition": (ctypes.c_int, [ctypes.POINTER(HeadDesc), I32, I32, P, P, P, P, F, P, P, P, P, SZ,
+                                                 P]),
         "chunk_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "chunk_attn_last_error": (ctypes.c_char_p, []),
         "chunk_attn_profile_start": (ctypes.c_int, []),
@@ -302,6 +312,47 @@ def spaco_stack_backward(h0, dy, dh0, layers, *, chunk: int, chunks: Sequence[in
     _check(lib.spaco_stack_backward(ctypes.byref(desc), int(T), len(layers), _stack_layers(layers), _ptr(h0),
                                     _ptr(dy), _ptr(dh0), h0.shape[1], sel, len(chunks), float(relay_factor),
                                     _ptr(ws), ws.numel(), _stream(h0)))
+
+
+def head_desc(h, w) -> HeadDesc:
+    """Descriptor from h [B, T, d_model] and w [vocab, d_model]."""
+    B, T, dm = h.shape
+    return HeadDesc(B, T, dm, w.shape[0], _dtype_code(h))
+
+
+def lm_head_transpose(w, wt):
+    """wt [d_model, vocab] = w^T (bf16)."""
+    _contig(w, wt)
+    d = HeadDesc(1, 1, w.shape[1], w.shape[0], _dtype_code(w))
+    _check(lib.lm_head_transpose(ctypes.byref(d), _ptr(w), _ptr(wt), _stream(w)))
+
+
+def lm_head_sft_workspace(h, w, rows: int):
+    import torch
+    d = head_desc(h, w)
+    need = int(lib.lm_head_sft_workspace_size(ctypes.byref(d), int(rows)))
+    return torch.empty(max(need, 256), dtype=torch.uint8, device=h.device)
+
+
+def lm_head_sft_partition(h, w, wt, labels, row_loss, dh, dw, *, row_start: int, rows: int, loss_scale: float,
+                          workspace=None):
+    """One partition of the streamed SFT head (see lm_head_sft_partition in chunk_attn.h)."""
+    _contig(h, w, wt, labels, row_loss, dh, dw)
+    d = head_desc(h, w)
+    ws = lm_head_sft_workspace(h, w, rows) if workspace is None else workspace
+    _check(lib.lm_head_sft_partition(ctypes.byref(d), int(row_start), int(rows), _ptr(h), _ptr(w), _ptr(wt),
+                                     _ptr(labels), float(loss_scale), _ptr(row_loss), _ptr(dh), _ptr(dw), _ptr(ws),
+                                     ws.numel(), _stream(h)))
+
+
+def lm_head_sft(h, w, wt, labels, row_loss, dh, dw, *, loss_scale: float, ps: int = 100,
+                seq_len: Optional[int] = None, workspace=None):
+    """StreamBP's streamed SFT head: every partition of ps positions in order."""
+    T = h.shape[1] if seq_len is None else seq_len
+    ws = lm_head_sft_workspace(h, w, ps) if workspace is None else workspace
+    for s in range(0, T, ps):
+        lm_head_sft_partition(h, w, wt, labels, row_loss, dh, dw, row_start=s, rows=min(ps, T - s),
+                              loss_scale=loss_scale, workspace=ws)
 
 
 def profile_start():

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libchunk_attn.so")
-SOURCES = ["api.cpp", "attention.hip", "projection.hip", "stack.hip"]
+SOURCES = ["api.cpp", "attention.hip", "projection.hip", "stack.hip", "lm_head.hip"]
 ARCH = os.environ.get("CHUNK_ATTN_ARCH", "gfx950")
 
 

@@ -620,3 +620,71 @@ int spaco_stack_backward(const chunk_attn_desc* d, int32_t seq_len, int32_t n_la
 }
 
 }  // extern "C"
+
+// ---- Streamed language-model head ------------------------------------------
+namespace {
+
+int check_head(const lm_head_desc* d) {
+  if (!d) return fail(CA_ERR_NULL, "lm_head descriptor is NULL");
+  if (d->dtype != CA_BF16) {
+    if (d->dtype != CA_F32) return fail(CA_ERR_DTYPE, "dtype %d", d->dtype);
+    return fail(CA_ERR_UNSUPPORTED, "lm_head: only bf16 storage is supported");
+  }
+  if (d->batch < 1 || d->batch > 65535 || d->seq_capacity < 1) return fail(CA_ERR_SHAPE, "batch/seq_capacity");
+  if (d->d_model < 64 || d->d_model > 65536 || d->d_model % 64 != 0)
+    return fail(CA_ERR_SHAPE, "d_model %d (a multiple of 64 in [64, 65536])", d->d_model);
+  if (d->vocab < 64 || d->vocab % 64 != 0 || d->vocab > (1 << 24))
+    return fail(CA_ERR_SHAPE, "vocab %d (a multiple of 64 up to 2^24)", d->vocab);
+  if ((int64_t)d->batch * d->seq_capacity * d->d_model > ((int64_t)1 << 40) ||
+      (int64_t)d->vocab * d->d_model > ((int64_t)1 << 40))
+    return fail(CA_ERR_SHAPE, "lm_head tensors too large");
+  return CA_OK;
+}
+
+ca::HeadShape head_shape(const lm_head_desc* d, int32_t row_start, int32_t rows) {
+  ca::HeadShape s;
+  s.batch = d->batch;
+  s.capacity = d->seq_capacity;
+  s.d_model = d->d_model;
+  s.vocab = d->vocab;
+  s.row_start = row_start;
+  s.rows = rows;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lm_head_transpose(const lm_head_desc* d, const void* w, void* wt, void* stream) {
+  int rc = check_head(d);
+  if (rc) return rc;
+  if ((rc = check_ptrs({w, wt}))) return rc;
+  hipError_t e = ca::launch_head_transpose(head_shape(d, 0, 1), w, wt, (hipStream_t)stream);
+  return e == hipSuccess ? CA_OK : hip_fail(e, "lm_head_transpose launch");
+}
+
+size_t lm_head_sft_workspace_size(const lm_head_desc* d, int32_t rows) {
+  if (check_head(d) != CA_OK || rows < 1 || (int64_t)d->batch * rows > 65535 * 64) return 0;
+  return ca::head_ws_bytes(head_shape(d, 0, rows));
+}
+
+int lm_head_sft_partition(const lm_head_desc* d, int32_t row_start, int32_t rows, const void* h, const void* w,
+                          const void* wt, const int32_t* labels, float loss_scale, float* row_loss, float* dh,
+                          float* dw, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_head(d);
+  if (rc) return rc;
+  if ((rc = check_ptrs({h, w, wt, labels, row_loss, dh, dw}))) return rc;
+  if (rows < 1 || row_start < 0 || (int64_t)row_start + rows > d->seq_capacity ||
+      (int64_t)d->batch * rows > 65535 * 64)
+    return fail(CA_ERR_SHAPE, "partition rows [%d, %lld) outside seq_capacity %d", row_start,
+                (long long)row_start + rows, d->seq_capacity);
+  if (!(loss_scale == loss_scale) || loss_scale > 3.0e38f || loss_scale < -3.0e38f)
+    return fail(CA_ERR_SHAPE, "loss_scale is not finite");
+  const ca::HeadShape s = head_shape(d, row_start, rows);
+  if ((rc = check_ws(ws, ws_bytes, ca::head_ws_bytes(s)))) return rc;
+  hipError_t e = ca::launch_head_sft(s, h, w, wt, labels, loss_scale, row_loss, dh, dw, ws, (hipStream_t)stream);
+  return e == hipSuccess ? CA_OK : hip_fail(e, "lm_head_sft_partition launch");
+}
+
+}  // extern "C"

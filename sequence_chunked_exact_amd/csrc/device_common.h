@@ -151,6 +151,20 @@ __device__ __forceinline__ f32x8 ldT8(const float* t, int kbase, int c0, int lan
   return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Fragment of row r, columns kbase + tile-order slots (4g + s, 16 + 4g + s - 4).
+template <class Lt>
+__device__ __forceinline__ bf16x8 ld8t(const bf16* t, int r, int kbase, int g) {
+  const bf16x4 a = *(const bf16x4*)(t + Lt::off(r, kbase + 4 * g));
+  const bf16x4 b = *(const bf16x4*)(t + Lt::off(r, kbase + 16 + 4 * g));
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <class Lt>
+__device__ __forceinline__ f32x8 ld8t(const float* t, int r, int kbase, int g) {
+  const f32x4 a = *(const f32x4*)(t + Lt::off(r, kbase + 4 * g));
+  const f32x4 b = *(const f32x4*)(t + Lt::off(r, kbase + 16 + 4 * g));
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // 8 consecutive elements from global memory.
 __device__ __forceinline__ bf16x8 ldg8(const bf16* p) { return *(const bf16x8*)p; }
 __device__ __forceinline__ f32x8 ldg8(const float* p) {

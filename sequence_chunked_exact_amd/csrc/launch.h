@@ -74,6 +74,16 @@ hipError_t launch_residual_fwd(const ResidualShape& s, const void* h_in, const v
 // dout = dh (float32, row-major) in the per-head layout, in dtype.
 hipError_t launch_residual_bwd(const ResidualShape& s, const float* dh, void* dout, hipStream_t st);
 
+// Language-model head over one partition of positions [row_start, +rows) of
+// h [batch][capacity][d_model] (bf16); w [vocab][d_model], wt = w^T.
+struct HeadShape {
+  int batch, capacity, d_model, vocab, row_start, rows;
+};
+size_t head_ws_bytes(const HeadShape& s);
+hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hipStream_t st);
+hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, const void* wt, const int* labels,
+                           float scale, float* row_loss, float* dh, float* dw, void* ws, hipStream_t st);
+
 // Fill n floats with zero (a kernel, so it is safe inside captured graphs).
 hipError_t launch_zero(float* p, size_t n, hipStream_t st);
 

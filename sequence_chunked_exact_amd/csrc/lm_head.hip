@@ -1,0 +1,261 @@
+// Language-model head streamed over sequence partitions, supervised
+// fine-tuning loss (gfx950). StreamBP streams the head by partitioning the
+// logits along the sequence, ps_head positions at a time, the SFT loss being
+// separable over positions (StreamBP review, "Core claim"; "Assumptions":
+// Eq. (3), ps_head = 100). Per partition of `rows` positions:
+//
+//   Z  = H W^T                       [rows][vocab] float32     (PG_DH GEMM over W^T)
+//   per row: lse = logsumexp(Z), loss = lse - Z[y]; dZ = scale (softmax(Z) - onehot(y))
+//                                    [rows_pad][vocab] bf16     (ce_kernel)
+//   dH = dZ W                        float32, overwritten      (PG_DH GEMM over W)
+//   dW += dZ^T H                     float32, incremented      (PG_DW GEMM)
+//
+// Only one partition's logits exist at a time. W^T [d_model][vocab] is written
+// once per step by wt_head_kernel: the logits product reads it along k.
+#include "gemm_bf16.h"
+
+namespace ca {
+namespace {
+
+struct CeParams {
+  const float* z;        // [batch][rows][vocab]
+  const int* labels;     // partition's first label of batch entry b at labels + b * lab_bs
+  long long lab_bs;
+  bf16* dz;              // [batch][rows_pad][vocab]
+  float* row_loss;       // partition's first row of batch entry b at row_loss + b * lab_bs
+  float scale;
+  int rows, rows_pad, vocab, batch;
+};
+
+// One workgroup per (batch entry, row of rows_pad): a pass for the row's max
+// and exponential sum (each thread over a strided quarter-vector set, then a
+// workgroup reduction), then a pass writing dZ. Padding rows write zeros.
+__global__ __launch_bounds__(256) void ce_kernel(CeParams p) {
+  __shared__ float red_m[4], red_s[4];
+  const int r = blockIdx.x % p.rows_pad, b = blockIdx.x / p.rows_pad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bf16* dz = p.dz + ((long long)b * p.rows_pad + r) * p.vocab;
+  const int nv = p.vocab / 4;
+  int y = r < p.rows ? p.labels[b * p.lab_bs + r] : -1;
+  if (y >= p.vocab) y = -1;  // not a target
+  if (y < 0) {
+    for (int i = tid; i < nv; i += 256) *(bf16x4*)(dz + 4 * i) = bf16x4{};
+    if (r < p.rows && tid == 0) p.row_loss[b * p.lab_bs + r] = 0.f;
+    return;
+  }
+  const float* z = p.z + ((long long)b * p.rows + r) * p.vocab;
+  float m = -kInf, s = 0.f;
+  for (int i = tid; i < nv; i += 256) {
+    const f32x4 v = *(const f32x4*)(z + 4 * i);
+    const float mv = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+    if (mv > m) {
+      s *= fexp2((m - mv) * kLog2e);
+      m = mv;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += fexp2((v[e] - m) * kLog2e);
+  }
+  // reduce (m, s) over the wave, then over the 4 waves
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    const float mm = fmaxf(m, m2);
+    s = (m == -kInf ? 0.f : s * fexp2((m - mm) * kLog2e)) + (m2 == -kInf ? 0.f : s2 * fexp2((m2 - mm) * kLog2e));
+    m = mm;
+  }
+  if (lane == 0) {
+    red_m[wave] = m;
+    red_s[wave] = s;
+  }
+  __syncthreads();
+  float M = red_m[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w]);
+  float S = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) S += red_s[w] * fexp2((red_m[w] - M) * kLog2e);
+  const float lse = M + __logf(S);
+  if (tid == 0) p.row_loss[b * p.lab_bs + r] = lse - z[y];
+  for (int i = tid; i < nv; i += 256) {
+    const f32x4 v = *(const f32x4*)(z + 4 * i);
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float g = fexp2((v[e] - lse) * kLog2e);
+      if (4 * i + e == y) g -= 1.f;
+      o[e] = (bf16)(p.scale * g);
+    }
+    *(bf16x4*)(dz + 4 * i) = o;
+  }
+}
+
+// W^T: out[c][v] = w[v][c], 64 x 64 tiles through LDS, 16-byte accesses.
+__global__ __launch_bounds__(256) void wt_head_kernel(const bf16* w, bf16* out, int vocab, int d_model) {
+  __shared__ bf16 t[64][64 + 8];
+  const int vt = blockIdx.x % (vocab / 64), ct = blockIdx.x / (vocab / 64);
+  const int v0 = vt * 64, c0 = ct * 64;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = threadIdx.x + i * 256, r = idx / 8, c = idx % 8;
+    *(bf16x8*)&t[r][c * 8] = *(const bf16x8*)(w + (long long)(v0 + r) * d_model + c0 + c * 8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = threadIdx.x + i * 256, r = idx / 8, c = idx % 8;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = t[c * 8 + e][r];
+    *(bf16x8*)(out + (long long)(c0 + r) * vocab + v0 + c * 8) = v;
+  }
+}
+
+// dh rows = sum over the split-k partials [splits][rows][d_model].
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float* part, float* dh, int splits, int rows, int dm) {
+  const long long n4 = (long long)rows * dm / 4;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (long long)gridDim.x * blockDim.x) {
+    f32x4 acc = ((const f32x4*)part)[i];
+    for (int s = 1; s < splits; ++s) acc += ((const f32x4*)part)[(long long)s * n4 + i];
+    ((f32x4*)dh)[i] = acc;
+  }
+}
+
+constexpr int kWide = 1 << 30;
+
+// Split of the dH product's k range (the vocabulary) into a divisor of its
+// 64-wide slices, so that its few output tiles (rows x d_model) fill the GPU.
+int head_splits(int vocab) {
+  const int slices = vocab / 64;
+  for (int s = 16; s > 1; --s)
+    if (slices % s == 0) return s;
+  return 1;
+}
+
+}  // namespace
+
+// Workspace: logits [batch][rows][vocab] float32, dZ [batch][rows_pad][vocab]
+// bf16, split-k partials of dH [splits][rows][d_model] float32, each on a
+// 256-byte boundary.
+size_t head_z_bytes(const HeadShape& s) { return ((size_t)s.batch * s.rows * s.vocab * sizeof(float) + 255) / 256 * 256; }
+size_t head_dz_bytes(const HeadShape& s) {
+  return ((size_t)s.batch * pg_rows_pad(s.rows) * s.vocab * sizeof(bf16) + 255) / 256 * 256;
+}
+
+size_t head_ws_bytes(const HeadShape& s) {
+  return head_z_bytes(s) + head_dz_bytes(s) + (size_t)head_splits(s.vocab) * s.rows * s.d_model * sizeof(float);
+}
+
+hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hipStream_t st) {
+  prof_begin(CA_KERNEL_HEAD_AUX, st);
+  hipLaunchKernelGGL(wt_head_kernel, dim3((s.vocab / 64) * (s.d_model / 64)), dim3(256), 0, st, (const bf16*)w,
+                     (bf16*)wt, s.vocab, s.d_model);
+  prof_end(CA_KERNEL_HEAD_AUX, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, const void* wt, const int* labels,
+                           float scale, float* row_loss, float* dh, float* dw, void* ws, hipStream_t st) {
+  const int dm = s.d_model, V = s.vocab, rows_pad = pg_rows_pad(s.rows);
+  float* z = (float*)ws;
+  bf16* dz = (bf16*)((char*)ws + head_z_bytes(s));
+  float* part = (float*)((char*)ws + head_z_bytes(s) + head_dz_bytes(s));
+  const int S = head_splits(V), kpart = V / S;
+  const bf16* hp = (const bf16*)h + (size_t)s.row_start * dm;
+
+  // Z = H W^T
+  ProjGemmParams zp{};
+  zp.a = hp;
+  zp.a_ld = dm;
+  zp.a_bs = (long long)s.capacity * dm;
+  zp.b[0] = zp.b[1] = zp.b[2] = (const bf16*)wt;
+  zp.b_w[0] = V;
+  zp.b_w[1] = zp.b_w[2] = kWide;
+  zp.c[0] = z;
+  zp.c_rs[0] = V;
+  zp.c_bs[0] = (long long)s.rows * V;
+  zp.c_hd[0] = kWide;
+  zp.c_w[0] = V;
+  zp.c_w[1] = zp.c_w[2] = kWide;
+  zp.M = s.rows;
+  zp.N = V;
+  zp.K = dm;
+  zp.a_rows = s.rows;
+  zp.batch = s.batch;
+  hipError_t e = pg_launch<PG_DH>(zp, s.batch, CA_KERNEL_HEAD, st);
+  if (e != hipSuccess) return e;
+
+  // per-row loss and dZ
+  CeParams cp{};
+  cp.z = z;
+  cp.labels = labels + s.row_start;
+  cp.lab_bs = s.capacity;
+  cp.dz = dz;
+  cp.row_loss = row_loss + s.row_start;
+  cp.scale = scale;
+  cp.rows = s.rows;
+  cp.rows_pad = rows_pad;
+  cp.vocab = V;
+  cp.batch = s.batch;
+  prof_begin(CA_KERNEL_HEAD_AUX, st);
+  hipLaunchKernelGGL(ce_kernel, dim3(s.batch * rows_pad), dim3(256), 0, st, cp);
+  prof_end(CA_KERNEL_HEAD_AUX, st);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // dH = dZ W, the vocabulary split S ways into partials, then summed
+  for (int b = 0; b < s.batch; ++b) {
+    ProjGemmParams hq{};
+    hq.a = dz + (size_t)b * rows_pad * V;
+    hq.a_ld = V;
+    hq.a_bs = kpart;  // split j reads dZ columns [j kpart, (j + 1) kpart)
+    hq.b[0] = hq.b[1] = hq.b[2] = (const bf16*)w;
+    hq.b_w[0] = dm;
+    hq.b_w[1] = hq.b_w[2] = kWide;
+    hq.b_bs = (long long)kpart * dm;  // and W rows of the same range
+    hq.c[0] = part;
+    hq.c_rs[0] = dm;
+    hq.c_bs[0] = (long long)s.rows * dm;
+    hq.c_hd[0] = kWide;
+    hq.c_w[0] = dm;
+    hq.c_w[1] = hq.c_w[2] = kWide;
+    hq.M = s.rows;
+    hq.N = dm;
+    hq.K = kpart;
+    hq.a_rows = s.rows;
+    hq.batch = S;
+    e = pg_launch<PG_DH>(hq, S, CA_KERNEL_HEAD, st);
+    if (e != hipSuccess) return e;
+    const long long n4 = (long long)s.rows * dm / 4;
+    const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
+    prof_begin(CA_KERNEL_HEAD_AUX, st);
+    hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, st, part,
+                       dh + ((size_t)b * s.capacity + s.row_start) * dm, S, s.rows, dm);
+    prof_end(CA_KERNEL_HEAD_AUX, st);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+
+  // dW += dZ^T H, the batch summed along k
+  ProjGemmParams wp{};
+  wp.a = dz;
+  wp.a_ld = V;
+  wp.a_bs = (long long)rows_pad * V;
+  wp.b[0] = wp.b[1] = wp.b[2] = hp;
+  wp.b_w[0] = dm;
+  wp.b_w[1] = wp.b_w[2] = kWide;
+  wp.b_bs = (long long)s.capacity * dm;
+  wp.c[0] = dw;
+  wp.c_rs[0] = dm;
+  wp.c_hd[0] = kWide;
+  wp.c_w[0] = dm;
+  wp.c_w[1] = wp.c_w[2] = kWide;
+  wp.M = V;
+  wp.N = dm;
+  wp.K = rows_pad;
+  wp.a_rows = rows_pad;  // dZ's padding rows are zero
+  wp.b_rows = s.rows;    // H rows past the partition are not read
+  wp.batch = s.batch;
+  return pg_launch<PG_DW>(wp, 1, CA_KERNEL_HEAD, st);
+}
+
+}  // namespace ca

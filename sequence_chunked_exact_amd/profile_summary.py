@@ -41,8 +41,9 @@ SHORT = {"fwd_kernel": "fwd", "dkdv_kernel": "dkdv", "dq_kernel": "dq", "delta_k
 
 def kernel_sources(kernel: str) -> list:
     """The source files a kernel is built from (the shared device header and its own file)."""
-    own = "projection.hip" if kernel == "proj" else "attention.hip"
-    return [os.path.join(CSRC, "device_common.h"), os.path.join(CSRC, own)]
+    own = {"proj": ["gemm_bf16.h", "projection.hip"], "head": ["gemm_bf16.h", "lm_head.hip"],
+           "head_ce": ["lm_head.hip"]}.get(kernel, ["attention.hip"])
+    return [os.path.join(CSRC, f) for f in ["device_common.h"] + own]
 
 
 def kernel_source_sha256(kernel: str) -> str:

@@ -271,3 +271,51 @@ def make_stack_inputs(wl: StackWorkload, seq_len: Optional[int] = None, keep_f64
                 f64[name] = f32.astype(np.float64)
         arrays[name] = None
     return Inputs(wl, f64, raw)
+
+
+@dataclasses.dataclass(frozen=True)
+class HeadWorkload:
+    """The language-model head under SFT: final hidden states H [B, T, d_model], the
+    head W [vocab, d_model], target labels (-1 on the first `prompt` positions, the
+    prompt, which carries no loss), streamed in partitions of ps positions."""
+    name: str
+    batch: int
+    seq_len: int
+    d_model: int
+    vocab: int
+    ps: int
+    prompt: int
+    dtype: str
+    seed: int
+
+
+HEAD_WORKLOADS = {
+    # LLaMA3-8B head (vocab 128256) on 16K positions, ps_head = 100
+    "8b_head_sft": HeadWorkload("8b_head_sft", 1, 16384, 4096, 128256, 100, 1024, "bf16", 19),
+}
+
+
+def make_head_inputs(wl: HeadWorkload, seq_len: Optional[int] = None, keep_f64: bool = True) -> Inputs:
+    """Draw H ~ N(0, 1), W ~ N(0, 1/d_model) (logits ~N(0, 1)), labels uniform over
+    the vocabulary, -1 on the prompt positions; H and W rounded like make_inputs."""
+    T = wl.seq_len if seq_len is None else seq_len
+    rng = np.random.default_rng(wl.seed)
+    arrays = {"h": _draw(rng, (wl.batch, T, wl.d_model), 1.0),
+              "w": _draw(rng, (wl.vocab, wl.d_model), 1.0 / math.sqrt(wl.d_model))}
+    labels = rng.integers(0, wl.vocab, size=(wl.batch, T)).astype(np.int32)
+    labels[:, :min(wl.prompt, T)] = -1
+    raw, f64 = {"labels": labels}, {"labels": labels}
+    for name in list(arrays):
+        a = arrays[name]
+        if wl.dtype == "bf16":
+            bits = round_to_bf16_bits(a)
+            raw[name] = bits
+            if keep_f64:
+                f64[name] = bf16_bits_to_f64(bits)
+        else:
+            f32 = a.astype(np.float32)
+            raw[name] = f32
+            if keep_f64:
+                f64[name] = f32.astype(np.float64)
+        arrays[name] = None
+    return Inputs(wl, f64, raw)

@@ -211,3 +211,29 @@ def test_stack_errors():
     assert bwd_() == -1
     assert lib.spaco_stack_forward(ctypes.byref(d), 1024, 2, lay, FAKE, 1024, FAKE, need - 1, None) == -5
 
+
+def test_lm_head_errors():
+    HD = b.HeadDesc
+    d = HD(1, 1024, 256, 1024, b.CA_BF16)
+    size = lib.lm_head_sft_workspace_size
+    need = size(ctypes.byref(d), 100)
+    # logits (float32) + dZ (bf16, rows padded to 64) + 16 split-k partials of dH
+    assert need == (100 * 1024 * 4 + 255) // 256 * 256 + 128 * 1024 * 2 + 16 * 100 * 256 * 4
+    assert size(ctypes.byref(HD(1, 1024, 256, 1000, b.CA_BF16)), 100) == 0   # vocab % 64
+    assert size(ctypes.byref(d), 0) == 0
+
+    def part(dd=d, row_start=0, rows=100, ws_bytes=need, labels=FAKE, scale=1.0):
+        return lib.lm_head_sft_partition(ctypes.byref(dd), row_start, rows, FAKE, FAKE, FAKE, labels, scale, FAKE,
+                                         FAKE, FAKE, FAKE, ws_bytes, None)
+
+    assert part(dd=HD(1, 1024, 256, 1024, b.CA_F32)) == -6
+    assert part(dd=HD(1, 1024, 96, 1024, b.CA_BF16)) == -2
+    assert part(row_start=1000) == -2
+    assert part(rows=0) == -2
+    assert part(labels=None) == -1
+    assert part(labels=MISALIGNED) == -4
+    assert part(ws_bytes=need - 1) == -5
+    assert part(scale=float("inf")) == -2
+    assert lib.lm_head_transpose(ctypes.byref(HD(1, 1, 256, 1000, b.CA_BF16)), FAKE, FAKE, None) == -2
+    assert lib.lm_head_transpose(None, FAKE, FAKE, None) == -1
+

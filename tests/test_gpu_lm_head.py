@@ -1,0 +1,161 @@
+"""GPU parity of the streamed LM head under SFT (lm_head_transpose /
+lm_head_sft_partition through the C ABI) against the float64 oracle
+(oracle.lm_head). bf16 storage only; bar 2e-2 per tensor (max error over max
+reference magnitude), loss to 1e-3 relative.
+"""
+import numpy as np
+import pytest
+
+from oracle import lm_head as O
+from sequence_chunked_exact_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def rel(a, b):
+    return float(np.abs(np.asarray(a, np.float64) - b).max() / max(np.abs(b).max(), 1e-30))
+
+
+def run_head(inp, ps, scale, labels_override=None):
+    import torch
+    from sequence_chunked_exact_amd import binding as Bn
+    dev = "cuda:0"
+    h = W.to_torch(inp.raw["h"], dev)
+    w = W.to_torch(inp.raw["w"], dev)
+    lab = inp.raw["labels"] if labels_override is None else labels_override
+    labels = torch.from_numpy(np.ascontiguousarray(lab)).to(dev)
+    B, T, dm = h.shape
+    V = w.shape[0]
+    wt = torch.empty(dm, V, dtype=h.dtype, device=dev)
+    row_loss = torch.full((B, T), float("nan"), device=dev)
+    dh = torch.full((B, T, dm), float("nan"), device=dev)
+    dw = torch.zeros(V, dm, device=dev)
+    Bn.lm_head_transpose(w, wt)
+    Bn.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=scale, ps=ps)
+    torch.cuda.synchronize()
+    return row_loss.cpu().double().numpy(), dh.cpu().double().numpy(), dw.cpu().double().numpy()
+
+
+CASES = [
+    # name, B, T, d_model, vocab, ps, prompt
+    ("ragged_partitions", 1, 250, 256, 1024, 100, 20),
+    ("batch2_ps64", 2, 128, 128, 2048, 64, 0),
+    ("ps1_tiny_vocab", 1, 9, 64, 64, 1, 3),
+    ("one_partition_all_rows", 2, 70, 192, 448, 100, 5),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_head_parity(case):
+    name, B, T, dm, V, ps, prompt = case
+    print(f"[case] {name}", flush=True)
+    wl = W.HeadWorkload(name, B, T, dm, V, ps, prompt, "bf16", seed=29)
+    inp = W.make_head_inputs(wl)
+    f = inp.f64
+    scale = O.target_scale(f["labels"])
+    rl, dh, dw = run_head(inp, ps, scale)
+    loss_ref, dh_ref, dw_ref = O.sft_streamed(f["h"], f["w"], f["labels"], ps, scale)
+    rl_ref = O.row_losses(f["h"], f["w"], f["labels"])
+    loss = scale * rl.sum()
+    errs = {"loss": abs(loss - loss_ref) / abs(loss_ref), "row_loss": rel(rl, rl_ref), "dh": rel(dh, dh_ref),
+            "dw": rel(dw, dw_ref)}
+    print(name, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs["loss"] <= 1e-3
+    for k in ("row_loss", "dh", "dw"):
+        assert errs[k] <= 2e-2, (k, errs[k])
+    assert np.all(rl[:, :prompt] == 0.0)
+
+
+def test_labels_outside_the_vocabulary_are_not_targets():
+    wl = W.HeadWorkload("oob_labels", 1, 64, 128, 256, 32, 0, "bf16", seed=31)
+    inp = W.make_head_inputs(wl)
+    lab = inp.raw["labels"].copy()
+    lab[0, 5] = 256          # == vocab
+    lab[0, 9] = 1 << 30
+    lab[0, 12] = -7
+    ref_lab = lab.copy()
+    ref_lab[(ref_lab < 0) | (ref_lab >= 256)] = -1
+    f = inp.f64
+    scale = O.target_scale(ref_lab)
+    rl, dh, dw = run_head(inp, 32, scale, labels_override=lab)
+    _, dh_ref, dw_ref = O.sft_streamed(f["h"], f["w"], ref_lab, 32, scale)
+    assert rl[0, 5] == 0.0 and rl[0, 9] == 0.0 and rl[0, 12] == 0.0
+    assert np.abs(dh[0, [5, 9, 12]]).max() == 0.0
+    assert rel(dh, dh_ref) <= 2e-2 and rel(dw, dw_ref) <= 2e-2
+
+
+def test_llama3_head_one_partition():
+    """The LLaMA3-8B head (d_model 4096, vocab 128256) on one ps_head = 100
+    partition: every row loss, every dH row, and sampled dW rows."""
+    base = W.HEAD_WORKLOADS["8b_head_sft"]
+    wl = W.HeadWorkload(base.name, 1, 100, base.d_model, base.vocab, 100, 10, "bf16", base.seed)
+    print(f"[case] {wl.name} one partition", flush=True)
+    inp = W.make_head_inputs(wl)
+    f = inp.f64
+    scale = O.target_scale(f["labels"])
+    rl, dh, dw = run_head(inp, 100, scale)
+    _, dh_ref, dw_ref = O.sft_streamed(f["h"], f["w"], f["labels"], 100, scale)
+    rl_ref = O.row_losses(f["h"], f["w"], f["labels"])
+    rows = np.random.default_rng(0).integers(0, base.vocab, 64)
+    errs = {"row_loss": rel(rl, rl_ref), "dh": rel(dh, dh_ref),
+            "dw_rows": float(np.abs(dw[rows] - dw_ref[rows]).max() / np.abs(dw_ref).max())}
+    print(errs, flush=True)
+    for k, e in errs.items():
+        assert e <= 2e-2, (k, e)
+
+
+def test_full_size_sampled():
+    """The benchmark's workload at full size (T = 16384, ps_head = 100), run as
+    the benchmark runs it, partition by partition: sampled row losses and dH
+    rows against the oracle computed row by row, and the last (ragged, 84-row)
+    partition's weight-gradient increment (dW after it minus dW before it)
+    against the oracle's dW of that partition, on sampled vocabulary rows
+    including every label of the partition."""
+    import torch
+    from sequence_chunked_exact_amd import binding as Bn
+    wl = W.HEAD_WORKLOADS["8b_head_sft"]
+    print(f"[case] {wl.name} full size", flush=True)
+    inp = W.make_head_inputs(wl, keep_f64=False)
+    lab = inp.raw["labels"]
+    scale = 1.0 / float((lab >= 0).sum())
+    dev = "cuda:0"
+    h_d = W.to_torch(inp.raw["h"], dev)
+    w_d = W.to_torch(inp.raw["w"], dev)
+    labels = torch.from_numpy(np.ascontiguousarray(lab)).to(dev)
+    B, T, dm = h_d.shape
+    V = w_d.shape[0]
+    wt = torch.empty(dm, V, dtype=h_d.dtype, device=dev)
+    row_loss = torch.full((B, T), float("nan"), device=dev)
+    dh_d = torch.full((B, T, dm), float("nan"), device=dev)
+    dw_d = torch.zeros(V, dm, device=dev)
+    ws = Bn.lm_head_sft_workspace(h_d, w_d, wl.ps)
+    Bn.lm_head_transpose(w_d, wt)
+    starts = list(range(0, T, wl.ps))
+    last = starts[-1]
+    for s0 in starts:
+        if s0 == last:
+            torch.cuda.synchronize()
+            before = dw_d.cpu()
+        Bn.lm_head_sft_partition(h_d, w_d, wt, labels, row_loss, dh_d, dw_d, row_start=s0, rows=min(wl.ps, T - s0),
+                                 loss_scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    inc = (dw_d.cpu() - before).double().numpy()
+    rl = row_loss.cpu().double().numpy()
+    dh = dh_d.cpu().double().numpy()
+    assert np.isfinite(rl).all() and np.isfinite(dh).all()
+    h = W.bf16_bits_to_f64(inp.raw["h"])
+    w = W.bf16_bits_to_f64(inp.raw["w"])
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, wl.prompt - 1, wl.prompt, T - 1], rng.integers(0, T, 8)]))
+    for t in rows:
+        _, dh_t, _ = O.sft_partition(h, w, lab, slice(t, t + 1), scale, with_dw=False)
+        rl_t = O.row_losses(h[:, t:t + 1], w, lab[:, t:t + 1])
+        e_l = abs(rl[0, t] - rl_t[0, 0]) / max(abs(rl_t[0, 0]), 1e-30)
+        e_h = rel(dh[0, t], dh_t[0, 0]) if lab[0, t] >= 0 else float(np.abs(dh[0, t]).max())
+        print("row", t, f"{e_l:.2e} {e_h:.2e}", flush=True)
+        assert e_l <= 2e-2 and e_h <= 2e-2
+    _, _, dw_last = O.sft_partition(h, w, lab, slice(last, T), scale)
+    vs = np.union1d(lab[0, last:][lab[0, last:] >= 0], rng.integers(0, V, 64))
+    e = float(np.abs(inc[vs] - dw_last[vs]).max() / np.abs(dw_last).max())
+    print("last partition dW increment", f"{e:.2e}", flush=True)
+    assert e <= 2e-2
