@@ -401,6 +401,110 @@ def stack_main(args):
     print(json.dumps(out), flush=True)
 
 
+def head_main(args):
+    import numpy as np
+    import torch
+    from sequence_chunked_exact_amd import binding as B
+    from sequence_chunked_exact_amd import workloads as W
+
+    wl = W.HEAD_WORKLOADS["8b_head_sft"]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {wl.name} inputs")
+    inp = W.make_head_inputs(wl, keep_f64=False)
+    h = W.to_torch(inp.raw["h"], dev)
+    w = W.to_torch(inp.raw["w"], dev)
+    lab_np = inp.raw["labels"]
+    labels = torch.from_numpy(np.ascontiguousarray(lab_np)).to(dev)
+    Bt, T, dm = h.shape
+    V = w.shape[0]
+    scale = 1.0 / float((lab_np >= 0).sum())
+    wt = torch.empty(dm, V, dtype=h.dtype, device=dev)
+    row_loss = torch.empty(Bt, T, device=dev)
+    dh = torch.empty(Bt, T, dm, device=dev)
+    dw = torch.zeros(V, dm, device=dev)
+    ws = B.lm_head_sft_workspace(h, w, wl.ps)
+
+    def step():
+        dw.zero_()
+        B.lm_head_transpose(w, wt)
+        B.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=scale, ps=wl.ps, workspace=ws)
+
+    log(f"[bench] head warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} head steps")
+    B.profile_start()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    B.profile_stop()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = B.profile_read()
+    flops = 3 * 2 * Bt * T * V * dm                     # logits, dH, dW
+    kernels = {n_: {"launches_per_step": c_ / args.steps, "ms_per_step": t_ / args.steps, "avg_us": t_ / c_ * 1e3}
+               for n_, (c_, t_) in prof.items() if c_}
+    log(f"[bench] {ms:.3f} ms/head step; kernels " + json.dumps(kernels))
+    n_h, t_h = prof["head"]
+    per_launch = flops / (n_h / args.steps)
+    achieved = per_launch / (t_h / n_h * 1e-3) / 1e12
+    loss = scale * float(row_loss.sum().item())
+    from sequence_chunked_exact_amd.profile_summary import read_traffic
+    out = {
+        "metric": "streamed LM head SFT loss + gradients (ps_head partitions) tokens/s, 1 GPU",
+        "value": Bt * T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "pct_bf16_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "config": {"workload": wl.name, "batch": Bt, "seq_len": T, "d_model": dm, "vocab": V, "ps_head": wl.ps,
+                   "prompt": wl.prompt, "flops_per_step": flops, "loss": loss},
+        "kernels": kernels,
+        "roofline": {"kernel": "head", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": read_traffic(os.path.join(ROOT, "profiles", f"head_{wl.name}.md"), "head"),
+                     "avg_launch_us": t_h / n_h * 1e3, "flops_per_launch": per_launch},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        from oracle import lm_head as O
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        hf = W.bf16_bits_to_f64(inp.raw["h"])
+        wf = W.bf16_bits_to_f64(inp.raw["w"])
+        n_part = 3
+        t0 = time.perf_counter()
+        for i in range(n_part):
+            s0 = wl.prompt + i * wl.ps
+            O.sft_partition(hf, wf, lab_np, slice(s0, s0 + wl.ps), scale)
+        dt = time.perf_counter() - t0
+        rate = 3 * 2 * n_part * wl.ps * V * dm / dt
+        out["cpu_baseline"] = {"value": Bt * T / (flops / rate), "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"float64 oracle on {n_part} partitions of {wl.ps} positions at the full "
+                                         f"vocabulary ({dt:.1f} s, {rate / 1e9:.1f} GFLOP/s), extrapolated to all "
+                                         f"{T} positions by FLOPs", "seconds": dt}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,6 +517,7 @@ def main():
     ap.add_argument("--stack", action="store_true",
                     help="measure SpaCO's step on a stack of attention layers (relayed cache gradients)")
     ap.add_argument("--seed", type=int, default=0, help="chunk draw seed for --stack")
+    ap.add_argument("--head", action="store_true", help="measure the streamed LM head (SFT) step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -423,6 +528,8 @@ def main():
         return layer_main(args)
     if args.stack:
         return stack_main(args)
+    if args.head:
+        return head_main(args)
 
     import numpy as np
     import torch
