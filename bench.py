@@ -423,12 +423,13 @@ def head_main(args):
     row_loss = torch.empty(Bt, T, device=dev)
     dh = torch.empty(Bt, T, dm, device=dev)
     dw = torch.zeros(V, dm, device=dev)
-    ws = B.lm_head_sft_workspace(h, w, wl.ps)
+    ws = B.lm_head_sweep_workspace(h, w, wl.ps, wl.dw_group)
 
     def step():
         dw.zero_()
         B.lm_head_transpose(w, wt)
-        B.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=scale, ps=wl.ps, workspace=ws)
+        B.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=scale, ps=wl.ps, dw_group=wl.dw_group,
+                      workspace=ws)
 
     log(f"[bench] head warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -471,7 +472,7 @@ def head_main(args):
         "tflops": flops / (ms * 1e-3) / 1e12,
         "pct_bf16_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "config": {"workload": wl.name, "batch": Bt, "seq_len": T, "d_model": dm, "vocab": V, "ps_head": wl.ps,
-                   "prompt": wl.prompt, "flops_per_step": flops, "loss": loss},
+                   "dw_group": wl.dw_group, "prompt": wl.prompt, "flops_per_step": flops, "loss": loss},
         "kernels": kernels,
         "roofline": {"kernel": "head", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,

@@ -278,6 +278,18 @@ int lm_head_sft_partition(const lm_head_desc* desc, int32_t row_start, int32_t r
                           const void* wt, const int32_t* labels, float loss_scale, float* row_loss, float* dh,
                           float* dw, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole streamed sweep over positions [0, seq_len): partitions of ps
+ * positions in order, each as lm_head_sft_partition, except that the weight
+ * gradient is added once per dw_group consecutive partitions, from their
+ * logit gradients (bf16) kept in the workspace; logits still exist for one
+ * partition at a time. dw_group = 1 adds it after every partition. Arguments,
+ * outputs and errors as for lm_head_sft_partition; ws:
+ * lm_head_sft_sweep_workspace_size(desc, ps, dw_group) bytes. */
+size_t lm_head_sft_sweep_workspace_size(const lm_head_desc* desc, int32_t ps, int32_t dw_group);
+int lm_head_sft_sweep(const lm_head_desc* desc, int32_t seq_len, int32_t ps, int32_t dw_group, const void* h,
+                      const void* w, const void* wt, const int32_t* labels, float loss_scale, float* row_loss,
+                      float* dh, float* dw, void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel timing for benchmarks (instrumentation only; results are unchanged).
  * chunk_attn_profile_start() clears the record and, until
  * chunk_attn_profile_stop(), brackets every kernel this library launches with

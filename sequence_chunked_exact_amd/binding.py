@@ -88,6 +88,9 @@ def _load() -> ctypes.CDLL:
         "lm_head_sft_workspace_size": (SZ, [ctypes.POINTER(HeadDesc), I32]),
         "lm_head_sft_partition": (ctypes.c_int, [ctypes.POINTER(HeadDesc), I32, I32, P, P, P, P, F, P, P, P, P, SZ,
                                                  P]),
+        "lm_head_sft_sweep_workspace_size": (SZ, [ctypes.POINTER(HeadDesc), I32, I32]),
+        "lm_head_sft_sweep": (ctypes.c_int, [ctypes.POINTER(HeadDesc), I32, I32, I32, P, P, P, P, F, P, P, P, P,
+                                             SZ, P]),
         "chunk_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "chunk_attn_last_error": (ctypes.c_char_p, []),
         "chunk_attn_profile_start": (ctypes.c_int, []),
@@ -345,14 +348,23 @@ def lm_head_sft_partition(h, w, wt, labels, row_loss, dh, dw, *, row_start: int,
                                      ws.numel(), _stream(h)))
 
 
-def lm_head_sft(h, w, wt, labels, row_loss, dh, dw, *, loss_scale: float, ps: int = 100,
+def lm_head_sweep_workspace(h, w, ps: int, dw_group: int):
+    import torch
+    d = head_desc(h, w)
+    need = int(lib.lm_head_sft_sweep_workspace_size(ctypes.byref(d), int(ps), int(dw_group)))
+    return torch.empty(max(need, 256), dtype=torch.uint8, device=h.device)
+
+
+def lm_head_sft(h, w, wt, labels, row_loss, dh, dw, *, loss_scale: float, ps: int = 100, dw_group: int = 1,
                 seq_len: Optional[int] = None, workspace=None):
-    """StreamBP's streamed SFT head: every partition of ps positions in order."""
+    """StreamBP's streamed SFT head over every partition of ps positions (lm_head_sft_sweep)."""
+    _contig(h, w, wt, labels, row_loss, dh, dw)
+    d = head_desc(h, w)
     T = h.shape[1] if seq_len is None else seq_len
-    ws = lm_head_sft_workspace(h, w, ps) if workspace is None else workspace
-    for s in range(0, T, ps):
-        lm_head_sft_partition(h, w, wt, labels, row_loss, dh, dw, row_start=s, rows=min(ps, T - s),
-                              loss_scale=loss_scale, workspace=ws)
+    ws = lm_head_sweep_workspace(h, w, ps, dw_group) if workspace is None else workspace
+    _check(lib.lm_head_sft_sweep(ctypes.byref(d), int(T), int(ps), int(dw_group), _ptr(h), _ptr(w), _ptr(wt),
+                                 _ptr(labels), float(loss_scale), _ptr(row_loss), _ptr(dh), _ptr(dw), _ptr(ws),
+                                 ws.numel(), _stream(h)))
 
 
 def profile_start():

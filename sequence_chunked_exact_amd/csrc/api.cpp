@@ -641,8 +641,10 @@ int check_head(const lm_head_desc* d) {
   return CA_OK;
 }
 
-ca::HeadShape head_shape(const lm_head_desc* d, int32_t row_start, int32_t rows) {
+ca::HeadShape head_shape(const lm_head_desc* d, int32_t row_start, int32_t rows, int32_t ps, int32_t group) {
   ca::HeadShape s;
+  s.ps = ps;
+  s.group = group;
   s.batch = d->batch;
   s.capacity = d->seq_capacity;
   s.d_model = d->d_model;
@@ -660,13 +662,13 @@ int lm_head_transpose(const lm_head_desc* d, const void* w, void* wt, void* stre
   int rc = check_head(d);
   if (rc) return rc;
   if ((rc = check_ptrs({w, wt}))) return rc;
-  hipError_t e = ca::launch_head_transpose(head_shape(d, 0, 1), w, wt, (hipStream_t)stream);
+  hipError_t e = ca::launch_head_transpose(head_shape(d, 0, 1, 1, 1), w, wt, (hipStream_t)stream);
   return e == hipSuccess ? CA_OK : hip_fail(e, "lm_head_transpose launch");
 }
 
 size_t lm_head_sft_workspace_size(const lm_head_desc* d, int32_t rows) {
   if (check_head(d) != CA_OK || rows < 1 || (int64_t)d->batch * rows > 65535 * 64) return 0;
-  return ca::head_ws_bytes(head_shape(d, 0, rows));
+  return ca::head_ws_bytes(head_shape(d, 0, rows, rows, 1));
 }
 
 int lm_head_sft_partition(const lm_head_desc* d, int32_t row_start, int32_t rows, const void* h, const void* w,
@@ -681,10 +683,36 @@ int lm_head_sft_partition(const lm_head_desc* d, int32_t row_start, int32_t rows
                 (long long)row_start + rows, d->seq_capacity);
   if (!(loss_scale == loss_scale) || loss_scale > 3.0e38f || loss_scale < -3.0e38f)
     return fail(CA_ERR_SHAPE, "loss_scale is not finite");
-  const ca::HeadShape s = head_shape(d, row_start, rows);
+  const ca::HeadShape s = head_shape(d, row_start, rows, rows, 1);
   if ((rc = check_ws(ws, ws_bytes, ca::head_ws_bytes(s)))) return rc;
   hipError_t e = ca::launch_head_sft(s, h, w, wt, labels, loss_scale, row_loss, dh, dw, ws, (hipStream_t)stream);
   return e == hipSuccess ? CA_OK : hip_fail(e, "lm_head_sft_partition launch");
+}
+
+size_t lm_head_sft_sweep_workspace_size(const lm_head_desc* d, int32_t ps, int32_t dw_group) {
+  if (check_head(d) != CA_OK || ps < 1 || dw_group < 1 || (int64_t)ps * dw_group > (1 << 20) ||
+      (int64_t)d->batch * ps * dw_group > (int64_t)1 << 26)
+    return 0;
+  return ca::head_ws_bytes(head_shape(d, 0, ps, ps, dw_group));
+}
+
+int lm_head_sft_sweep(const lm_head_desc* d, int32_t seq_len, int32_t ps, int32_t dw_group, const void* h,
+                      const void* w, const void* wt, const int32_t* labels, float loss_scale, float* row_loss,
+                      float* dh, float* dw, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_head(d);
+  if (rc) return rc;
+  if ((rc = check_ptrs({h, w, wt, labels, row_loss, dh, dw}))) return rc;
+  if (seq_len < 1 || seq_len > d->seq_capacity) return fail(CA_ERR_SHAPE, "seq_len %d outside [1, %d]", seq_len,
+                                                          d->seq_capacity);
+  if (ps < 1 || dw_group < 1 || (int64_t)ps * dw_group > (1 << 20) ||
+      (int64_t)d->batch * ps * dw_group > (int64_t)1 << 26)
+    return fail(CA_ERR_SHAPE, "ps %d, dw_group %d", ps, dw_group);
+  if (!(loss_scale == loss_scale) || loss_scale > 3.0e38f || loss_scale < -3.0e38f)
+    return fail(CA_ERR_SHAPE, "loss_scale is not finite");
+  const ca::HeadShape s = head_shape(d, 0, seq_len, ps, dw_group);
+  if ((rc = check_ws(ws, ws_bytes, ca::head_ws_bytes(s)))) return rc;
+  hipError_t e = ca::launch_head_sft(s, h, w, wt, labels, loss_scale, row_loss, dh, dw, ws, (hipStream_t)stream);
+  return e == hipSuccess ? CA_OK : hip_fail(e, "lm_head_sft_sweep launch");
 }
 
 }  // extern "C"

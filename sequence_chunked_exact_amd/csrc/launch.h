@@ -77,7 +77,9 @@ hipError_t launch_residual_bwd(const ResidualShape& s, const float* dh, void* do
 // Language-model head over one partition of positions [row_start, +rows) of
 // h [batch][capacity][d_model] (bf16); w [vocab][d_model], wt = w^T.
 struct HeadShape {
-  int batch, capacity, d_model, vocab, row_start, rows;
+  int batch, capacity, d_model, vocab;
+  int row_start, rows;  // positions covered: [row_start, row_start + rows)
+  int ps, group;        // partition size; partitions per weight-gradient update
 };
 size_t head_ws_bytes(const HeadShape& s);
 hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hipStream_t st);

@@ -10,8 +10,11 @@
 //   dH = dZ W                        float32, overwritten      (PG_DH GEMM over W)
 //   dW += dZ^T H                     float32, incremented      (PG_DW GEMM)
 //
-// Only one partition's logits exist at a time. W^T [d_model][vocab] is written
-// once per step by wt_head_kernel: the logits product reads it along k.
+// Only one partition's logits exist at a time. The weight gradient is added
+// once per group of consecutive partitions from their dZ rows (bf16, kept in
+// the workspace): added per partition, its float32 read-modify-write (8 bytes
+// per weight) dominates the step. W^T [d_model][vocab] is written once per
+// step by wt_head_kernel: the logits product reads it along k.
 #include "gemm_bf16.h"
 
 namespace ca {
@@ -21,10 +24,11 @@ struct CeParams {
   const float* z;        // [batch][rows][vocab]
   const int* labels;     // partition's first label of batch entry b at labels + b * lab_bs
   long long lab_bs;
-  bf16* dz;              // [batch][rows_pad][vocab]
+  bf16* dz;              // partition's first dZ row of batch entry b at dz + b * dz_bs
+  long long dz_bs;
   float* row_loss;       // partition's first row of batch entry b at row_loss + b * lab_bs
   float scale;
-  int rows, rows_pad, vocab, batch;
+  int rows, rows_pad, vocab, batch;  // rows [rows, rows_pad) of dZ are zeroed
 };
 
 // One workgroup per (batch entry, row of rows_pad): a pass for the row's max
@@ -34,7 +38,7 @@ __global__ __launch_bounds__(256) void ce_kernel(CeParams p) {
   __shared__ float red_m[4], red_s[4];
   const int r = blockIdx.x % p.rows_pad, b = blockIdx.x / p.rows_pad;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  bf16* dz = p.dz + ((long long)b * p.rows_pad + r) * p.vocab;
+  bf16* dz = p.dz + b * p.dz_bs + (long long)r * p.vocab;
   const int nv = p.vocab / 4;
   int y = r < p.rows ? p.labels[b * p.lab_bs + r] : -1;
   if (y >= p.vocab) y = -1;  // not a target
@@ -133,16 +137,17 @@ int head_splits(int vocab) {
 
 }  // namespace
 
-// Workspace: logits [batch][rows][vocab] float32, dZ [batch][rows_pad][vocab]
-// bf16, split-k partials of dH [splits][rows][d_model] float32, each on a
-// 256-byte boundary.
-size_t head_z_bytes(const HeadShape& s) { return ((size_t)s.batch * s.rows * s.vocab * sizeof(float) + 255) / 256 * 256; }
+// Workspace: logits [batch][ps][vocab] float32; dZ of a group of partitions
+// [batch][pad64(group * ps)][vocab] bf16; split-k partials of dH
+// [splits][ps][d_model] float32; each on a 256-byte boundary.
+size_t head_z_bytes(const HeadShape& s) { return ((size_t)s.batch * s.ps * s.vocab * sizeof(float) + 255) / 256 * 256; }
+int head_group_rows(const HeadShape& s) { return pg_rows_pad(s.ps * s.group); }
 size_t head_dz_bytes(const HeadShape& s) {
-  return ((size_t)s.batch * pg_rows_pad(s.rows) * s.vocab * sizeof(bf16) + 255) / 256 * 256;
+  return ((size_t)s.batch * head_group_rows(s) * s.vocab * sizeof(bf16) + 255) / 256 * 256;
 }
 
 size_t head_ws_bytes(const HeadShape& s) {
-  return head_z_bytes(s) + head_dz_bytes(s) + (size_t)head_splits(s.vocab) * s.rows * s.d_model * sizeof(float);
+  return head_z_bytes(s) + head_dz_bytes(s) + (size_t)head_splits(s.vocab) * s.ps * s.d_model * sizeof(float);
 }
 
 hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hipStream_t st) {
@@ -153,14 +158,19 @@ hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hi
   return hipGetLastError();
 }
 
-hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, const void* wt, const int* labels,
-                           float scale, float* row_loss, float* dh, float* dw, void* ws, hipStream_t st) {
-  const int dm = s.d_model, V = s.vocab, rows_pad = pg_rows_pad(s.rows);
+namespace {
+
+// One partition [s0, s0 + rows): logits, loss rows and dZ (at row `off` of the
+// group's dZ buffer, with `zero_to` - rows padding rows zeroed after it), dH.
+hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zero_to, const void* h,
+                          const void* w, const void* wt, const int* labels, float scale, float* row_loss,
+                          float* dh, char* ws, hipStream_t st) {
+  const int dm = s.d_model, V = s.vocab, grows = head_group_rows(s);
   float* z = (float*)ws;
-  bf16* dz = (bf16*)((char*)ws + head_z_bytes(s));
-  float* part = (float*)((char*)ws + head_z_bytes(s) + head_dz_bytes(s));
+  bf16* dzg = (bf16*)(ws + head_z_bytes(s));
+  float* part = (float*)(ws + head_z_bytes(s) + head_dz_bytes(s));
   const int S = head_splits(V), kpart = V / S;
-  const bf16* hp = (const bf16*)h + (size_t)s.row_start * dm;
+  const bf16* hp = (const bf16*)h + (size_t)s0 * dm;
 
   // Z = H W^T
   ProjGemmParams zp{};
@@ -172,14 +182,14 @@ hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, con
   zp.b_w[1] = zp.b_w[2] = kWide;
   zp.c[0] = z;
   zp.c_rs[0] = V;
-  zp.c_bs[0] = (long long)s.rows * V;
+  zp.c_bs[0] = (long long)rows * V;
   zp.c_hd[0] = kWide;
   zp.c_w[0] = V;
   zp.c_w[1] = zp.c_w[2] = kWide;
-  zp.M = s.rows;
+  zp.M = rows;
   zp.N = V;
   zp.K = dm;
-  zp.a_rows = s.rows;
+  zp.a_rows = rows;
   zp.batch = s.batch;
   hipError_t e = pg_launch<PG_DH>(zp, s.batch, CA_KERNEL_HEAD, st);
   if (e != hipSuccess) return e;
@@ -187,17 +197,18 @@ hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, con
   // per-row loss and dZ
   CeParams cp{};
   cp.z = z;
-  cp.labels = labels + s.row_start;
+  cp.labels = labels + s0;
   cp.lab_bs = s.capacity;
-  cp.dz = dz;
-  cp.row_loss = row_loss + s.row_start;
+  cp.dz = dzg + (size_t)off * V;
+  cp.dz_bs = (long long)grows * V;
+  cp.row_loss = row_loss + s0;
   cp.scale = scale;
-  cp.rows = s.rows;
-  cp.rows_pad = rows_pad;
+  cp.rows = rows;
+  cp.rows_pad = zero_to;
   cp.vocab = V;
   cp.batch = s.batch;
   prof_begin(CA_KERNEL_HEAD_AUX, st);
-  hipLaunchKernelGGL(ce_kernel, dim3(s.batch * rows_pad), dim3(256), 0, st, cp);
+  hipLaunchKernelGGL(ce_kernel, dim3(s.batch * zero_to), dim3(256), 0, st, cp);
   prof_end(CA_KERNEL_HEAD_AUX, st);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -205,7 +216,7 @@ hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, con
   // dH = dZ W, the vocabulary split S ways into partials, then summed
   for (int b = 0; b < s.batch; ++b) {
     ProjGemmParams hq{};
-    hq.a = dz + (size_t)b * rows_pad * V;
+    hq.a = dzg + ((size_t)b * grows + off) * V;
     hq.a_ld = V;
     hq.a_bs = kpart;  // split j reads dZ columns [j kpart, (j + 1) kpart)
     hq.b[0] = hq.b[1] = hq.b[2] = (const bf16*)w;
@@ -214,48 +225,69 @@ hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, con
     hq.b_bs = (long long)kpart * dm;  // and W rows of the same range
     hq.c[0] = part;
     hq.c_rs[0] = dm;
-    hq.c_bs[0] = (long long)s.rows * dm;
+    hq.c_bs[0] = (long long)rows * dm;
     hq.c_hd[0] = kWide;
     hq.c_w[0] = dm;
     hq.c_w[1] = hq.c_w[2] = kWide;
-    hq.M = s.rows;
+    hq.M = rows;
     hq.N = dm;
     hq.K = kpart;
-    hq.a_rows = s.rows;
+    hq.a_rows = rows;
     hq.batch = S;
     e = pg_launch<PG_DH>(hq, S, CA_KERNEL_HEAD, st);
     if (e != hipSuccess) return e;
-    const long long n4 = (long long)s.rows * dm / 4;
+    const long long n4 = (long long)rows * dm / 4;
     const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
     prof_begin(CA_KERNEL_HEAD_AUX, st);
     hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, st, part,
-                       dh + ((size_t)b * s.capacity + s.row_start) * dm, S, s.rows, dm);
+                       dh + ((size_t)b * s.capacity + s0) * dm, S, rows, dm);
     prof_end(CA_KERNEL_HEAD_AUX, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  return hipSuccess;
+}
 
-  // dW += dZ^T H, the batch summed along k
-  ProjGemmParams wp{};
-  wp.a = dz;
-  wp.a_ld = V;
-  wp.a_bs = (long long)rows_pad * V;
-  wp.b[0] = wp.b[1] = wp.b[2] = hp;
-  wp.b_w[0] = dm;
-  wp.b_w[1] = wp.b_w[2] = kWide;
-  wp.b_bs = (long long)s.capacity * dm;
-  wp.c[0] = dw;
-  wp.c_rs[0] = dm;
-  wp.c_hd[0] = kWide;
-  wp.c_w[0] = dm;
-  wp.c_w[1] = wp.c_w[2] = kWide;
-  wp.M = V;
-  wp.N = dm;
-  wp.K = rows_pad;
-  wp.a_rows = rows_pad;  // dZ's padding rows are zero
-  wp.b_rows = s.rows;    // H rows past the partition are not read
-  wp.batch = s.batch;
-  return pg_launch<PG_DW>(wp, 1, CA_KERNEL_HEAD, st);
+}  // namespace
+
+hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, const void* wt, const int* labels,
+                           float scale, float* row_loss, float* dh, float* dw, void* ws, hipStream_t st) {
+  const int dm = s.d_model, V = s.vocab, grows = head_group_rows(s);
+  const bf16* dzg = (const bf16*)((const char*)ws + head_z_bytes(s));
+  const int end = s.row_start + s.rows, span = s.ps * s.group;
+  for (int gs = s.row_start; gs < end; gs += span) {
+    const int ge = gs + span < end ? gs + span : end;
+    for (int s0 = gs; s0 < ge; s0 += s.ps) {
+      const int rows = s0 + s.ps < ge ? s.ps : ge - s0;
+      const bool last = s0 + rows == ge;
+      hipError_t e = head_partition(s, s0, rows, s0 - gs, last ? grows - (s0 - gs) : rows, h, w, wt, labels, scale,
+                                    row_loss, dh, (char*)ws, st);
+      if (e != hipSuccess) return e;
+    }
+    // dW += dZ^T H over the group's rows, the batch summed along k
+    ProjGemmParams wp{};
+    wp.a = dzg;
+    wp.a_ld = V;
+    wp.a_bs = (long long)grows * V;
+    wp.b[0] = wp.b[1] = wp.b[2] = (const bf16*)h + (size_t)gs * dm;
+    wp.b_w[0] = dm;
+    wp.b_w[1] = wp.b_w[2] = kWide;
+    wp.b_bs = (long long)s.capacity * dm;
+    wp.c[0] = dw;
+    wp.c_rs[0] = dm;
+    wp.c_hd[0] = kWide;
+    wp.c_w[0] = dm;
+    wp.c_w[1] = wp.c_w[2] = kWide;
+    wp.M = V;
+    wp.N = dm;
+    wp.K = grows;
+    wp.a_rows = grows;    // dZ rows past the group are zero
+    wp.b_rows = ge - gs;  // H rows past the group are not read
+    wp.batch = s.batch;
+    hipError_t e = pg_launch<PG_DW>(wp, 1, CA_KERNEL_HEAD, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ca

@@ -287,11 +287,13 @@ class HeadWorkload:
     prompt: int
     dtype: str
     seed: int
+    dw_group: int = 1
 
 
 HEAD_WORKLOADS = {
-    # LLaMA3-8B head (vocab 128256) on 16K positions, ps_head = 100
-    "8b_head_sft": HeadWorkload("8b_head_sft", 1, 16384, 4096, 128256, 100, 1024, "bf16", 19),
+    # LLaMA3-8B head (vocab 128256) on 16K positions, ps_head = 100; the weight
+    # gradient is added once per 16 partitions (1600 positions)
+    "8b_head_sft": HeadWorkload("8b_head_sft", 1, 16384, 4096, 128256, 100, 1024, "bf16", 19, 16),
 }
 
 

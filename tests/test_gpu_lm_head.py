@@ -16,7 +16,7 @@ def rel(a, b):
     return float(np.abs(np.asarray(a, np.float64) - b).max() / max(np.abs(b).max(), 1e-30))
 
 
-def run_head(inp, ps, scale, labels_override=None):
+def run_head(inp, ps, scale, labels_override=None, dw_group=1):
     import torch
     from sequence_chunked_exact_amd import binding as Bn
     dev = "cuda:0"
@@ -31,29 +31,31 @@ def run_head(inp, ps, scale, labels_override=None):
     dh = torch.full((B, T, dm), float("nan"), device=dev)
     dw = torch.zeros(V, dm, device=dev)
     Bn.lm_head_transpose(w, wt)
-    Bn.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=scale, ps=ps)
+    Bn.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=scale, ps=ps, dw_group=dw_group)
     torch.cuda.synchronize()
     return row_loss.cpu().double().numpy(), dh.cpu().double().numpy(), dw.cpu().double().numpy()
 
 
 CASES = [
-    # name, B, T, d_model, vocab, ps, prompt
-    ("ragged_partitions", 1, 250, 256, 1024, 100, 20),
-    ("batch2_ps64", 2, 128, 128, 2048, 64, 0),
-    ("ps1_tiny_vocab", 1, 9, 64, 64, 1, 3),
-    ("one_partition_all_rows", 2, 70, 192, 448, 100, 5),
+    # name, B, T, d_model, vocab, ps, prompt, dw_group (partitions per weight-gradient update)
+    ("ragged_partitions", 1, 250, 256, 1024, 100, 20, 1),
+    ("batch2_ps64", 2, 128, 128, 2048, 64, 0, 1),
+    ("ps1_tiny_vocab", 1, 9, 64, 64, 1, 3, 1),
+    ("one_partition_all_rows", 2, 70, 192, 448, 100, 5, 1),
+    ("grouped_dw_short_last_group", 1, 250, 256, 1024, 40, 10, 3),
+    ("grouped_dw_batch2_group_exceeds_sequence", 2, 130, 128, 512, 32, 0, 8),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_head_parity(case):
-    name, B, T, dm, V, ps, prompt = case
+    name, B, T, dm, V, ps, prompt, group = case
     print(f"[case] {name}", flush=True)
     wl = W.HeadWorkload(name, B, T, dm, V, ps, prompt, "bf16", seed=29)
     inp = W.make_head_inputs(wl)
     f = inp.f64
     scale = O.target_scale(f["labels"])
-    rl, dh, dw = run_head(inp, ps, scale)
+    rl, dh, dw = run_head(inp, ps, scale, dw_group=group)
     loss_ref, dh_ref, dw_ref = O.sft_streamed(f["h"], f["w"], f["labels"], ps, scale)
     rl_ref = O.row_losses(f["h"], f["w"], f["labels"])
     loss = scale * rl.sum()
