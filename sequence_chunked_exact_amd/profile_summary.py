@@ -96,8 +96,9 @@ def summarize_main(args):
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
     out = {}
     if args.fetch and args.write and args.cal_fetch and args.cal_write:
-        f = per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
-        w = per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+        match = args.match or args.kernel
+        f = per_dispatch(args.fetch, "FETCH_SIZE", match)
+        w = per_dispatch(args.write, "WRITE_SIZE", match)
         cf = max(per_dispatch(args.cal_fetch, "FETCH_SIZE"))
         cw = max(per_dispatch(args.cal_write, "WRITE_SIZE"))
         kf, kw = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
@@ -152,7 +153,7 @@ def main(argv=None):
     sub.add_parser("copy")
     s = sub.add_parser("summarize")
     for opt in ("--stats", "--fetch", "--write", "--cal-fetch", "--cal-write", "--kernel", "--workload",
-                "--out", "--commands", "--mfma"):
+                "--out", "--commands", "--mfma", "--match"):
         s.add_argument(opt, default=None)
     args = ap.parse_args(argv)
     if args.cmd == "copy":
