@@ -91,3 +91,62 @@ def row_losses(h, w, labels):
     tgt = y >= 0
     z_y = np.take_along_axis(z, np.where(tgt, y, 0)[..., None], axis=-1)[..., 0]
     return np.where(tgt, _lse(z) - z_y, 0.0)
+
+
+def _logp_rows(h, w, labels):
+    """log p(y_t) per position [B, T] (0 where the label is not a target) and the
+    softmax P [B, T, V]."""
+    h = np.asarray(h, dtype=np.float64)
+    z = h @ np.asarray(w, dtype=np.float64).T
+    y = np.asarray(labels)
+    tgt = y >= 0
+    lse = _lse(z)
+    z_y = np.take_along_axis(z, np.where(tgt, y, 0)[..., None], axis=-1)[..., 0]
+    return np.where(tgt, z_y - lse, 0.0), np.exp(z - lse[..., None]), tgt
+
+
+def weighted_grads(h, w, labels, weight):
+    """dh, dW of sum_t weight_t * (-log p(y_t)) over target positions:
+    dz_t = weight_t (softmax(z_t) - onehot(y_t))."""
+    h = np.asarray(h, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    _, p, tgt = _logp_rows(h, w, labels)
+    y = np.where(tgt, np.asarray(labels), 0)
+    onehot = np.zeros_like(p)
+    np.put_along_axis(onehot, y[..., None], 1.0, axis=-1)
+    dz = np.asarray(weight, dtype=np.float64)[..., None] * (p - onehot) * tgt[..., None]
+    return dz @ w, sum(dz[b].T @ h[b] for b in range(h.shape[0]))
+
+
+def grpo_dense(h, w, labels, advantages):
+    """GRPO's policy-gradient objective on one group of B sampled responses to a
+    prompt (StreamBP review, "Assumptions": Eq. (6), separable over positions).
+    The page does not print Eq. (6); the reading is the on-policy form (ratio 1,
+    no clipping or KL term): L = -(1/B) sum_i (1/|o_i|) sum_{t in o_i} A_i log p(y_t),
+    with o_i the target positions of batch entry i. Returns (L, dh, dW)."""
+    logp, _, tgt = _logp_rows(h, w, labels)
+    n = np.maximum(tgt.sum(axis=1), 1)
+    B = logp.shape[0]
+    wt = (np.asarray(advantages, dtype=np.float64) / (B * n))[:, None] * np.ones_like(logp)
+    loss = float(-(wt * logp).sum())
+    dh, dw = weighted_grads(h, w, labels, wt)
+    return loss, dh, dw
+
+
+def dpo_dense(h, w, labels, ref_logp, beta):
+    """DPO on one preference pair, batch entry 0 the chosen response and 1 the
+    rejected one (StreamBP review, "Assumptions": Eqs. (8)-(10); the loss is not
+    separable but its gradient factorizes with a final scalar). Reading:
+    L = -log sigmoid(beta * ((lp_c - ref_c) - (lp_r - ref_r))), lp = sum over the
+    response's target positions of log p(y_t). dL/dtheta = c * (grad(-lp_c) -
+    grad(-lp_r)), c = beta * sigmoid(-beta * margin): the sum of the per-position
+    gradients with weights +1 / -1, multiplied by c once every position is done.
+    Returns (L, dh, dW, c)."""
+    logp, _, _ = _logp_rows(h, w, labels)
+    lp = logp.sum(axis=1)
+    margin = (lp[0] - ref_logp[0]) - (lp[1] - ref_logp[1])
+    loss = float(np.logaddexp(0.0, -beta * margin))          # -log sigmoid(beta * margin)
+    c = beta / (1.0 + np.exp(beta * margin))                 # beta * sigmoid(-beta * margin)
+    sign = np.array([1.0, -1.0])[:, None] * np.ones_like(logp)
+    dh, dw = weighted_grads(h, w, labels, sign)
+    return loss, c * dh, c * dw, c

@@ -101,3 +101,65 @@ def test_no_targets_gives_zero():
     y[:] = -1
     l, dh, dw = H.sft_dense(h, w, y)
     assert l == 0.0 and not dh.any() and not dw.any()
+
+
+def test_grpo_matches_torch_autograd():
+    h, w, y = case(B=3, T=8, seed=8, ignore=(0, 1))
+    y[2, :3] = -1
+    adv = np.array([0.7, -1.2, 0.4])
+    th = torch.tensor(h, requires_grad=True)
+    tw = torch.tensor(w, requires_grad=True)
+    logp = torch.log_softmax(th @ tw.T, dim=-1)
+    ty = torch.tensor(y)
+    tgt = ty >= 0
+    lp = torch.gather(logp, -1, ty.clamp(min=0)[..., None])[..., 0] * tgt
+    loss = -(torch.tensor(adv)[:, None] * lp / tgt.sum(dim=1, keepdim=True)).sum() / 3
+    loss.backward()
+    l, dh, dw = H.grpo_dense(h, w, y, adv)
+    assert abs(l - loss.item()) <= 1e-12 * abs(loss.item())
+    np.testing.assert_allclose(dh, th.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dw, tw.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_grpo_with_equal_advantages_and_lengths_is_scaled_sft():
+    h, w, y = case(B=2, T=6, seed=9, ignore=())
+    l, dh, dw = H.grpo_dense(h, w, y, np.array([1.0, 1.0]))
+    ls, dhs, dws = H.sft_dense(h, w, y)
+    assert abs(l - ls) < 1e-12
+    np.testing.assert_allclose(dh, dhs, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(dw, dws, rtol=1e-12, atol=1e-15)
+
+
+def test_dpo_matches_torch_autograd_and_finite_differences():
+    h, w, y = case(B=2, T=7, seed=10, ignore=(0,))
+    y[1, :2] = -1
+    ref = np.array([-20.0, -21.5])
+    beta = 0.3
+    th = torch.tensor(h, requires_grad=True)
+    tw = torch.tensor(w, requires_grad=True)
+    logp = torch.log_softmax(th @ tw.T, dim=-1)
+    ty = torch.tensor(y)
+    lp = (torch.gather(logp, -1, ty.clamp(min=0)[..., None])[..., 0] * (ty >= 0)).sum(dim=1)
+    margin = (lp[0] - ref[0]) - (lp[1] - ref[1])
+    loss = -torch.nn.functional.logsigmoid(beta * margin)
+    loss.backward()
+    l, dh, dw, c = H.dpo_dense(h, w, y, ref, beta)
+    assert abs(l - loss.item()) <= 1e-12 * abs(loss.item())
+    np.testing.assert_allclose(dh, th.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(dw, tw.grad.numpy(), rtol=1e-10, atol=1e-13)
+    eps = 1e-6
+    idx = (1, 3)
+    wp, wm = w.copy(), w.copy()
+    wp[idx] += eps
+    wm[idx] -= eps
+    fd = (H.dpo_dense(h, wp, y, ref, beta)[0] - H.dpo_dense(h, wm, y, ref, beta)[0]) / (2 * eps)
+    assert abs(fd - dw[idx]) <= 1e-7 * max(1.0, abs(fd))
+
+
+def test_dpo_at_zero_margin():
+    # margin 0: loss ln 2 and c = beta / 2
+    h, w, y = case(B=2, T=5, seed=11, ignore=())
+    logp = -H.row_losses(h, w, y)
+    ref = logp.sum(axis=1)
+    l, _, _, c = H.dpo_dense(h, w, y, ref, 0.5)
+    assert abs(l - np.log(2.0)) < 1e-12 and abs(c - 0.25) < 1e-15
