@@ -267,7 +267,11 @@ size_t lm_head_sft_workspace_size(const lm_head_desc* desc, int32_t rows);
  * h [batch][seq_capacity][d_model] bf16; w [vocab][d_model] bf16 and its
  * transpose wt; labels [batch][seq_capacity] int32 (a position is a target iff
  * 0 <= label < vocab; other values, e.g. -1, mark prompt or padding positions);
- * loss_scale multiplies the gradients
+ * row_weight [batch][seq_capacity] float32 or NULL: a per-position weight of
+ * the gradient (dz_t = loss_scale * row_weight_t * (softmax - onehot)); NULL is
+ * 1 everywhere (SFT). GRPO takes A_i / (G |o_i|) on the positions of response i
+ * (the on-policy policy gradient of Eq. (6)); DPO takes +1 on the chosen and -1
+ * on the rejected response, then lm_head_dpo_finish. loss_scale multiplies the gradients
  * (1 / number of targets for a mean). Writes row_loss [batch][seq_capacity]
  * float32 (the unscaled loss of each position of the partition, 0 for
  * non-targets) and dh rows of the partition (float32, OVERWRITTEN); adds into
@@ -275,8 +279,8 @@ size_t lm_head_sft_workspace_size(const lm_head_desc* desc, int32_t rows);
  * pointers, CA_ERR_SHAPE for sizes or rows outside the capacity,
  * CA_ERR_UNSUPPORTED for a dtype other than bf16, CA_ERR_WORKSPACE. */
 int lm_head_sft_partition(const lm_head_desc* desc, int32_t row_start, int32_t rows, const void* h, const void* w,
-                          const void* wt, const int32_t* labels, float loss_scale, float* row_loss, float* dh,
-                          float* dw, void* ws, size_t ws_bytes, void* stream);
+                          const void* wt, const int32_t* labels, const float* row_weight, float loss_scale,
+                          float* row_loss, float* dh, float* dw, void* ws, size_t ws_bytes, void* stream);
 
 /* The whole streamed sweep over positions [0, seq_len): partitions of ps
  * positions in order, each as lm_head_sft_partition, except that the weight
@@ -287,8 +291,22 @@ int lm_head_sft_partition(const lm_head_desc* desc, int32_t row_start, int32_t r
  * lm_head_sft_sweep_workspace_size(desc, ps, dw_group) bytes. */
 size_t lm_head_sft_sweep_workspace_size(const lm_head_desc* desc, int32_t ps, int32_t dw_group);
 int lm_head_sft_sweep(const lm_head_desc* desc, int32_t seq_len, int32_t ps, int32_t dw_group, const void* h,
-                      const void* w, const void* wt, const int32_t* labels, float loss_scale, float* row_loss,
-                      float* dh, float* dw, void* ws, size_t ws_bytes, void* stream);
+                      const void* w, const void* wt, const int32_t* labels, const float* row_weight,
+                      float loss_scale, float* row_loss, float* dh, float* dw, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* DPO's final scalar (StreamBP review, "Assumptions": Eqs. (8)-(10), the loss is
+ * not separable but its gradient factorizes with a scalar known only at the
+ * end). For one preference pair, batch entry 0 chosen and 1 rejected, after a
+ * sweep over positions [0, seq_len) with row weights +1 / -1 and loss_scale 1:
+ * lp_b = -(sum of entry b's row losses), margin = (lp_0 - ref_logp_chosen) -
+ * (lp_1 - ref_logp_rejected), loss = -log sigmoid(beta * margin), and dh (rows
+ * [0, seq_len) of both entries) and dw are multiplied by c = beta *
+ * sigmoid(-beta * margin). Copies the row losses to the host (synchronizes the
+ * stream). Writes *loss_out and *c_out. CA_ERR_SHAPE unless batch == 2. */
+int lm_head_dpo_finish(const lm_head_desc* desc, int32_t seq_len, const float* row_loss, float ref_logp_chosen,
+                       float ref_logp_rejected, float beta, float* dh, float* dw, float* loss_out, float* c_out,
+                       void* stream);
 
 /* Kernel timing for benchmarks (instrumentation only; results are unchanged).
  * chunk_attn_profile_start() clears the record and, until

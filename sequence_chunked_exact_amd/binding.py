@@ -86,11 +86,13 @@ def _load() -> ctypes.CDLL:
                                                 ctypes.POINTER(I32), I32, F, P, SZ, P]),
         "lm_head_transpose": (ctypes.c_int, [ctypes.POINTER(HeadDesc), P, P, P]),
         "lm_head_sft_workspace_size": (SZ, [ctypes.POINTER(HeadDesc), I32]),
-        "lm_head_sft_partition": (ctypes.c_int, [ctypes.POINTER(HeadDesc), I32, I32, P, P, P, P, F, P, P, P, P, SZ,
-                                                 P]),
+        "lm_head_sft_partition": (ctypes.c_int, [ctypes.POINTER(HeadDesc), I32, I32, P, P, P, P, P, F, P, P, P, P,
+                                                 SZ, P]),
+        "lm_head_dpo_finish": (ctypes.c_int, [ctypes.POINTER(HeadDesc), I32, P, F, F, F, P, P,
+                                              ctypes.POINTER(F), ctypes.POINTER(F), P]),
         "lm_head_sft_sweep_workspace_size": (SZ, [ctypes.POINTER(HeadDesc), I32, I32]),
-        "lm_head_sft_sweep": (ctypes.c_int, [ctypes.POINTER(HeadDesc), I32, I32, I32, P, P, P, P, F, P, P, P, P,
-                                             SZ, P]),
+        "lm_head_sft_sweep": (ctypes.c_int, [ctypes.POINTER(HeadDesc), I32, I32, I32, P, P, P, P, P, F, P, P, P,
+                                             P, SZ, P]),
         "chunk_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "chunk_attn_last_error": (ctypes.c_char_p, []),
         "chunk_attn_profile_start": (ctypes.c_int, []),
@@ -338,14 +340,15 @@ def lm_head_sft_workspace(h, w, rows: int):
 
 
 def lm_head_sft_partition(h, w, wt, labels, row_loss, dh, dw, *, row_start: int, rows: int, loss_scale: float,
-                          workspace=None):
+                          row_weight=None, workspace=None):
     """One partition of the streamed SFT head (see lm_head_sft_partition in chunk_attn.h)."""
     _contig(h, w, wt, labels, row_loss, dh, dw)
     d = head_desc(h, w)
     ws = lm_head_sft_workspace(h, w, rows) if workspace is None else workspace
     _check(lib.lm_head_sft_partition(ctypes.byref(d), int(row_start), int(rows), _ptr(h), _ptr(w), _ptr(wt),
-                                     _ptr(labels), float(loss_scale), _ptr(row_loss), _ptr(dh), _ptr(dw), _ptr(ws),
-                                     ws.numel(), _stream(h)))
+                                     _ptr(labels), None if row_weight is None else _ptr(row_weight),
+                                     float(loss_scale), _ptr(row_loss), _ptr(dh), _ptr(dw), _ptr(ws), ws.numel(),
+                                     _stream(h)))
 
 
 def lm_head_sweep_workspace(h, w, ps: int, dw_group: int):
@@ -356,15 +359,28 @@ def lm_head_sweep_workspace(h, w, ps: int, dw_group: int):
 
 
 def lm_head_sft(h, w, wt, labels, row_loss, dh, dw, *, loss_scale: float, ps: int = 100, dw_group: int = 1,
-                seq_len: Optional[int] = None, workspace=None):
+                seq_len: Optional[int] = None, row_weight=None, workspace=None):
     """StreamBP's streamed SFT head over every partition of ps positions (lm_head_sft_sweep)."""
     _contig(h, w, wt, labels, row_loss, dh, dw)
     d = head_desc(h, w)
     T = h.shape[1] if seq_len is None else seq_len
     ws = lm_head_sweep_workspace(h, w, ps, dw_group) if workspace is None else workspace
     _check(lib.lm_head_sft_sweep(ctypes.byref(d), int(T), int(ps), int(dw_group), _ptr(h), _ptr(w), _ptr(wt),
-                                 _ptr(labels), float(loss_scale), _ptr(row_loss), _ptr(dh), _ptr(dw), _ptr(ws),
-                                 ws.numel(), _stream(h)))
+                                 _ptr(labels), None if row_weight is None else _ptr(row_weight),
+                                 float(loss_scale), _ptr(row_loss), _ptr(dh), _ptr(dw), _ptr(ws), ws.numel(),
+                                 _stream(h)))
+
+
+def lm_head_dpo_finish(row_loss, dh, dw, w, *, ref_logp, beta: float, seq_len: Optional[int] = None):
+    """DPO's final scalar on one preference pair (see lm_head_dpo_finish); returns (loss, c)."""
+    _contig(row_loss, dh, dw)
+    B, T = row_loss.shape
+    d = HeadDesc(B, T, dh.shape[2], w.shape[0], _dtype_code(w))
+    loss, c = ctypes.c_float(), ctypes.c_float()
+    _check(lib.lm_head_dpo_finish(ctypes.byref(d), int(T if seq_len is None else seq_len), _ptr(row_loss),
+                                  float(ref_logp[0]), float(ref_logp[1]), float(beta), _ptr(dh), _ptr(dw),
+                                  ctypes.byref(loss), ctypes.byref(c), _stream(dh)))
+    return float(loss.value), float(c.value)
 
 
 def profile_start():

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -672,8 +673,8 @@ size_t lm_head_sft_workspace_size(const lm_head_desc* d, int32_t rows) {
 }
 
 int lm_head_sft_partition(const lm_head_desc* d, int32_t row_start, int32_t rows, const void* h, const void* w,
-                          const void* wt, const int32_t* labels, float loss_scale, float* row_loss, float* dh,
-                          float* dw, void* ws, size_t ws_bytes, void* stream) {
+                          const void* wt, const int32_t* labels, const float* row_weight, float loss_scale,
+                          float* row_loss, float* dh, float* dw, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_head(d);
   if (rc) return rc;
   if ((rc = check_ptrs({h, w, wt, labels, row_loss, dh, dw}))) return rc;
@@ -685,7 +686,9 @@ int lm_head_sft_partition(const lm_head_desc* d, int32_t row_start, int32_t rows
     return fail(CA_ERR_SHAPE, "loss_scale is not finite");
   const ca::HeadShape s = head_shape(d, row_start, rows, rows, 1);
   if ((rc = check_ws(ws, ws_bytes, ca::head_ws_bytes(s)))) return rc;
-  hipError_t e = ca::launch_head_sft(s, h, w, wt, labels, loss_scale, row_loss, dh, dw, ws, (hipStream_t)stream);
+  if (row_weight && (rc = check_ptrs({row_weight}))) return rc;
+  hipError_t e = ca::launch_head_sft(s, h, w, wt, labels, row_weight, loss_scale, row_loss, dh, dw, ws,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? CA_OK : hip_fail(e, "lm_head_sft_partition launch");
 }
 
@@ -697,8 +700,9 @@ size_t lm_head_sft_sweep_workspace_size(const lm_head_desc* d, int32_t ps, int32
 }
 
 int lm_head_sft_sweep(const lm_head_desc* d, int32_t seq_len, int32_t ps, int32_t dw_group, const void* h,
-                      const void* w, const void* wt, const int32_t* labels, float loss_scale, float* row_loss,
-                      float* dh, float* dw, void* ws, size_t ws_bytes, void* stream) {
+                      const void* w, const void* wt, const int32_t* labels, const float* row_weight,
+                      float loss_scale, float* row_loss, float* dh, float* dw, void* ws, size_t ws_bytes,
+                      void* stream) {
   int rc = check_head(d);
   if (rc) return rc;
   if ((rc = check_ptrs({h, w, wt, labels, row_loss, dh, dw}))) return rc;
@@ -711,8 +715,41 @@ int lm_head_sft_sweep(const lm_head_desc* d, int32_t seq_len, int32_t ps, int32_
     return fail(CA_ERR_SHAPE, "loss_scale is not finite");
   const ca::HeadShape s = head_shape(d, 0, seq_len, ps, dw_group);
   if ((rc = check_ws(ws, ws_bytes, ca::head_ws_bytes(s)))) return rc;
-  hipError_t e = ca::launch_head_sft(s, h, w, wt, labels, loss_scale, row_loss, dh, dw, ws, (hipStream_t)stream);
+  if (row_weight && (rc = check_ptrs({row_weight}))) return rc;
+  hipError_t e = ca::launch_head_sft(s, h, w, wt, labels, row_weight, loss_scale, row_loss, dh, dw, ws,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? CA_OK : hip_fail(e, "lm_head_sft_sweep launch");
+}
+
+int lm_head_dpo_finish(const lm_head_desc* d, int32_t seq_len, const float* row_loss, float ref_logp_chosen,
+                       float ref_logp_rejected, float beta, float* dh, float* dw, float* loss_out, float* c_out,
+                       void* stream) {
+  int rc = check_head(d);
+  if (rc) return rc;
+  if ((rc = check_ptrs({row_loss, dh, dw}))) return rc;
+  if (!loss_out || !c_out) return fail(CA_ERR_NULL, "lm_head_dpo_finish: NULL output");
+  if (d->batch != 2) return fail(CA_ERR_SHAPE, "DPO needs batch 2 (chosen, rejected), got %d", d->batch);
+  if (seq_len < 1 || seq_len > d->seq_capacity) return fail(CA_ERR_SHAPE, "seq_len %d", seq_len);
+  if (!(beta == beta) || !(ref_logp_chosen == ref_logp_chosen) || !(ref_logp_rejected == ref_logp_rejected))
+    return fail(CA_ERR_SHAPE, "beta / reference log-probabilities must be numbers");
+  hipStream_t st = (hipStream_t)stream;
+  std::vector<float> rl((size_t)2 * d->seq_capacity);
+  hipError_t e = hipMemcpyAsync(rl.data(), row_loss, rl.size() * sizeof(float), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "lm_head_dpo_finish copy");
+  double lp[2] = {0.0, 0.0};
+  for (int b = 0; b < 2; ++b)
+    for (int32_t t = 0; t < seq_len; ++t) lp[b] -= rl[(size_t)b * d->seq_capacity + t];
+  const double margin = (lp[0] - ref_logp_chosen) - (lp[1] - ref_logp_rejected);
+  const double x = -beta * margin;  // loss = log(1 + e^x), c = beta * sigmoid(x)
+  *loss_out = (float)(x > 0 ? x + std::log1p(std::exp(-x)) : std::log1p(std::exp(x)));
+  const double c = beta / (1.0 + std::exp(-x));
+  *c_out = (float)c;
+  // scale in place: acc += (c - 1) * acc
+  e = ca::launch_accumulate(dh, dh, 2, 1, d->seq_capacity, d->seq_capacity, d->d_model, seq_len, (float)(c - 1.0), st);
+  if (e == hipSuccess)
+    e = ca::launch_accumulate(dw, dw, 1, 1, d->vocab, d->vocab, d->d_model, d->vocab, (float)(c - 1.0), st);
+  return e == hipSuccess ? CA_OK : hip_fail(e, "lm_head_dpo_finish scale");
 }
 
 }  // extern "C"

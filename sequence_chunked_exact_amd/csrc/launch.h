@@ -84,7 +84,8 @@ struct HeadShape {
 size_t head_ws_bytes(const HeadShape& s);
 hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hipStream_t st);
 hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, const void* wt, const int* labels,
-                           float scale, float* row_loss, float* dh, float* dw, void* ws, hipStream_t st);
+                           const float* weight, float scale, float* row_loss, float* dh, float* dw, void* ws,
+                           hipStream_t st);
 
 // Fill n floats with zero (a kernel, so it is safe inside captured graphs).
 hipError_t launch_zero(float* p, size_t n, hipStream_t st);

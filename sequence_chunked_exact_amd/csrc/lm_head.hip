@@ -23,6 +23,7 @@ namespace {
 struct CeParams {
   const float* z;        // [batch][rows][vocab]
   const int* labels;     // partition's first label of batch entry b at labels + b * lab_bs
+  const float* weight;   // per-position gradient weights, same layout (NULL: 1)
   long long lab_bs;
   bf16* dz;              // partition's first dZ row of batch entry b at dz + b * dz_bs
   long long dz_bs;
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(256) void ce_kernel(CeParams p) {
   for (int w = 0; w < 4; ++w) S += red_s[w] * fexp2((red_m[w] - M) * kLog2e);
   const float lse = M + __logf(S);
   if (tid == 0) p.row_loss[b * p.lab_bs + r] = lse - z[y];
+  const float scale = p.weight ? p.scale * p.weight[b * p.lab_bs + r] : p.scale;
   for (int i = tid; i < nv; i += 256) {
     const f32x4 v = *(const f32x4*)(z + 4 * i);
     bf16x4 o;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void ce_kernel(CeParams p) {
     for (int e = 0; e < 4; ++e) {
       float g = fexp2((v[e] - lse) * kLog2e);
       if (4 * i + e == y) g -= 1.f;
-      o[e] = (bf16)(p.scale * g);
+      o[e] = (bf16)(scale * g);
     }
     *(bf16x4*)(dz + 4 * i) = o;
   }
@@ -163,8 +165,8 @@ namespace {
 // One partition [s0, s0 + rows): logits, loss rows and dZ (at row `off` of the
 // group's dZ buffer, with `zero_to` - rows padding rows zeroed after it), dH.
 hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zero_to, const void* h,
-                          const void* w, const void* wt, const int* labels, float scale, float* row_loss,
-                          float* dh, char* ws, hipStream_t st) {
+                          const void* w, const void* wt, const int* labels, const float* weight, float scale,
+                          float* row_loss, float* dh, char* ws, hipStream_t st) {
   const int dm = s.d_model, V = s.vocab, grows = head_group_rows(s);
   float* z = (float*)ws;
   bf16* dzg = (bf16*)(ws + head_z_bytes(s));
@@ -198,6 +200,7 @@ hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zer
   CeParams cp{};
   cp.z = z;
   cp.labels = labels + s0;
+  cp.weight = weight ? weight + s0 : nullptr;
   cp.lab_bs = s.capacity;
   cp.dz = dzg + (size_t)off * V;
   cp.dz_bs = (long long)grows * V;
@@ -251,7 +254,8 @@ hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zer
 }  // namespace
 
 hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, const void* wt, const int* labels,
-                           float scale, float* row_loss, float* dh, float* dw, void* ws, hipStream_t st) {
+                           const float* weight, float scale, float* row_loss, float* dh, float* dw, void* ws,
+                           hipStream_t st) {
   const int dm = s.d_model, V = s.vocab, grows = head_group_rows(s);
   const bf16* dzg = (const bf16*)((const char*)ws + head_z_bytes(s));
   const int end = s.row_start + s.rows, span = s.ps * s.group;
@@ -260,8 +264,8 @@ hipError_t launch_head_sft(const HeadShape& s, const void* h, const void* w, con
     for (int s0 = gs; s0 < ge; s0 += s.ps) {
       const int rows = s0 + s.ps < ge ? s.ps : ge - s0;
       const bool last = s0 + rows == ge;
-      hipError_t e = head_partition(s, s0, rows, s0 - gs, last ? grows - (s0 - gs) : rows, h, w, wt, labels, scale,
-                                    row_loss, dh, (char*)ws, st);
+      hipError_t e = head_partition(s, s0, rows, s0 - gs, last ? grows - (s0 - gs) : rows, h, w, wt, labels,
+                                    weight, scale, row_loss, dh, (char*)ws, st);
       if (e != hipSuccess) return e;
     }
     // dW += dZ^T H over the group's rows, the batch summed along k

@@ -223,8 +223,8 @@ def test_lm_head_errors():
     assert size(ctypes.byref(d), 0) == 0
 
     def part(dd=d, row_start=0, rows=100, ws_bytes=need, labels=FAKE, scale=1.0):
-        return lib.lm_head_sft_partition(ctypes.byref(dd), row_start, rows, FAKE, FAKE, FAKE, labels, scale, FAKE,
-                                         FAKE, FAKE, FAKE, ws_bytes, None)
+        return lib.lm_head_sft_partition(ctypes.byref(dd), row_start, rows, FAKE, FAKE, FAKE, labels, None, scale,
+                                         FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
 
     assert part(dd=HD(1, 1024, 256, 1024, b.CA_F32)) == -6
     assert part(dd=HD(1, 1024, 96, 1024, b.CA_BF16)) == -2
@@ -236,4 +236,9 @@ def test_lm_head_errors():
     assert part(scale=float("inf")) == -2
     assert lib.lm_head_transpose(ctypes.byref(HD(1, 1, 256, 1000, b.CA_BF16)), FAKE, FAKE, None) == -2
     assert lib.lm_head_transpose(None, FAKE, FAKE, None) == -1
+    loss, c = ctypes.c_float(), ctypes.c_float()
+    assert lib.lm_head_dpo_finish(ctypes.byref(d), 100, FAKE, 0.0, 0.0, 0.1, FAKE, FAKE, ctypes.byref(loss),
+                                  ctypes.byref(c), None) == -2                     # batch must be 2
+    assert lib.lm_head_dpo_finish(ctypes.byref(HD(2, 1024, 256, 1024, b.CA_BF16)), 100, FAKE, 0.0, 0.0, 0.1, FAKE,
+                                  FAKE, None, ctypes.byref(c), None) == -1
 

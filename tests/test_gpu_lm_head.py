@@ -161,3 +161,63 @@ def test_full_size_sampled():
     e = float(np.abs(inc[vs] - dw_last[vs]).max() / np.abs(dw_last).max())
     print("last partition dW increment", f"{e:.2e}", flush=True)
     assert e <= 2e-2
+
+
+def _device_head(inp, dev="cuda:0"):
+    import torch
+    from sequence_chunked_exact_amd import binding as Bn
+    h = W.to_torch(inp.raw["h"], dev)
+    w = W.to_torch(inp.raw["w"], dev)
+    labels = torch.from_numpy(np.ascontiguousarray(inp.raw["labels"])).to(dev)
+    B, T, dm = h.shape
+    V = w.shape[0]
+    wt = torch.empty(dm, V, dtype=h.dtype, device=dev)
+    Bn.lm_head_transpose(w, wt)
+    return Bn, torch, h, w, wt, labels, torch.zeros(B, T, device=dev), torch.zeros(B, T, dm, device=dev), \
+        torch.zeros(V, dm, device=dev)
+
+
+def test_grpo_weighted_rows():
+    """GRPO's on-policy objective through per-position weights A_i / (G |o_i|)."""
+    wl = W.HeadWorkload("grpo", 3, 96, 128, 512, 40, 12, "bf16", seed=37)
+    inp = W.make_head_inputs(wl)
+    lab = inp.raw["labels"]
+    lab[2, 80:] = -1                                   # a shorter response
+    adv = np.array([0.8, -1.1, 0.3])
+    n = (lab >= 0).sum(axis=1)
+    weight = np.where(lab >= 0, (adv / (3 * n))[:, None], 0.0).astype(np.float32)
+    Bn, torch, h, w, wt, labels, row_loss, dh, dw = _device_head(inp)
+    labels.copy_(torch.from_numpy(lab))
+    wd = torch.from_numpy(weight).to(h.device)
+    Bn.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=1.0, ps=wl.ps, dw_group=2, row_weight=wd)
+    torch.cuda.synchronize()
+    f = inp.f64
+    loss_ref, dh_ref, dw_ref = O.grpo_dense(f["h"], f["w"], lab, adv)
+    loss = float((weight.astype(np.float64) * row_loss.cpu().double().numpy()).sum())
+    errs = {"loss": abs(loss - loss_ref) / abs(loss_ref), "dh": rel(dh.cpu().double().numpy(), dh_ref),
+            "dw": rel(dw.cpu().double().numpy(), dw_ref)}
+    print("grpo", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs["loss"] <= 1e-3 and errs["dh"] <= 2e-2 and errs["dw"] <= 2e-2
+
+
+@pytest.mark.parametrize("offset", [0.0, 3.0])
+def test_dpo_scalar_correction(offset):
+    """DPO on one preference pair: a sweep with weights +1 / -1, then the final
+    scalar c = beta sigmoid(-beta margin) from the accumulated log-probabilities."""
+    wl = W.HeadWorkload("dpo", 2, 80, 128, 448, 32, 16, "bf16", seed=41)
+    inp = W.make_head_inputs(wl)
+    lab = inp.raw["labels"]
+    f = inp.f64
+    lp = -O.row_losses(f["h"], f["w"], lab).sum(axis=1)
+    ref = np.array([lp[0] - offset, lp[1] + offset])      # margin 2 * offset
+    beta = 0.2
+    Bn, torch, h, w, wt, labels, row_loss, dh, dw = _device_head(inp)
+    weight = torch.tensor([[1.0], [-1.0]], device=h.device).expand(2, lab.shape[1]).contiguous()
+    Bn.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=1.0, ps=wl.ps, dw_group=2, row_weight=weight)
+    loss, c = Bn.lm_head_dpo_finish(row_loss, dh, dw, w, ref_logp=ref, beta=beta)
+    torch.cuda.synchronize()
+    loss_ref, dh_ref, dw_ref, c_ref = O.dpo_dense(f["h"], f["w"], lab, ref, beta)
+    errs = {"loss": abs(loss - loss_ref) / abs(loss_ref), "c": abs(c - c_ref) / c_ref,
+            "dh": rel(dh.cpu().double().numpy(), dh_ref), "dw": rel(dw.cpu().double().numpy(), dw_ref)}
+    print("dpo", offset, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert errs["loss"] <= 2e-3 and errs["c"] <= 2e-3 and errs["dh"] <= 2e-2 and errs["dw"] <= 2e-2
