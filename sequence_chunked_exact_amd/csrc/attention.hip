@@ -12,13 +12,16 @@
 // Matrix products and their fragment slot orders follow the conventions in
 // device_common.h; products accumulate in float32.
 //
-// LDS holds every streamed tile once, row-major, with its 16-byte chunks
-// XOR-swizzled by row so that both access patterns are free of bank
-// conflicts: 16 lanes reading one chunk column of 16 rows (operands contracted
-// over head_dim), and ds_read_b64_tr_b16 transposing reads (operands
-// contracted over rows: V in P V, K in dS K, Q and dO in dS^T Q and P^T dO).
-// Tiles are double-buffered: the next tile's global loads are in flight while
-// the current one is consumed, with one barrier per tile.
+// LDS holds every streamed tile once, row-major. Tiles filled by direct
+// global->LDS loads (K/V in the forward and dQ) have their 16-byte chunks
+// XOR-swizzled by row (the loads write each wave's kilobyte contiguously);
+// tiles written from registers (Q/dO in dK/dV) have each row padded by 32
+// bytes. Either way both access patterns are free of bank conflicts: 16 lanes
+// reading one chunk column of 16 rows (operands contracted over head_dim), and
+// ds_read_b64_tr_b16 transposing reads (operands contracted over rows: V in
+// P V, K in dS K, Q and dO in dS^T Q and P^T dO). Tiles are double-buffered:
+// the next tile's loads are in flight while the current one is consumed, with
+// one barrier per tile (per pair of tiles in the forward and dQ).
 //
 // Layout choices:
 //  * forward / dQ: S^T = K Q^T per key tile, so each lane owns one query column
