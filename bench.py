@@ -521,7 +521,7 @@ def main():
     ap.add_argument("--head", action="store_true", help="measure the streamed LM head (SFT) step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
