@@ -1,6 +1,8 @@
 // C-ABI layer: argument checks (all before any device call), workspace sizing,
-// the SpaCO chunk selector and the sparse backward driver. Kernels live in
-// attention.hip and projection.hip; this file only validates and enqueues.
+// the SpaCO chunk selector, the sparse backward driver, the layer-stack driver
+// (SeCO's inference pass, SpaCO's relayed backward) and the streamed LM head's
+// entry points. Kernels live in attention.hip, projection.hip, stack.hip and
+// lm_head.hip; this file validates, orders launches and enqueues them.
 #include "chunk_attn.h"
 
 #include <hip/hip_runtime.h>

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI layer (api.cpp) and the HIP kernels
-// (attention.hip, projection.hip). Arguments are already validated when these are called.
+// (attention.hip, projection.hip, stack.hip, lm_head.hip). Arguments are
+// already validated when these are called.
 #pragma once
 
 #include <hip/hip_runtime.h>
