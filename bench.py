@@ -401,6 +401,27 @@ def stack_main(args):
     print(json.dumps(out), flush=True)
 
 
+def head_bytes(T, dm, V, ps, group, B=1):
+    """Algorithmic HBM bytes of the head's three products over one step: per
+    partition of r positions, the logits product reads W^T and H rows and writes
+    the float32 logits; dH reads dZ (bf16) and W and writes its split-k partials
+    (12 splits for the LLaMA3 vocabulary); per group of partitions, dW reads dZ
+    and H rows and reads + writes the float32 weight gradient. At these sizes
+    (about 125 FLOP per byte, under MI355X's ~310 FLOP/B balance of bf16 MFMA to
+    HBM) the head is bound by memory."""
+    wbytes = V * dm * 2
+    splits = next(s for s in range(16, 0, -1) if (V // 64) % s == 0)
+    total = 0
+    for s0 in range(0, T, ps):
+        r = min(ps, T - s0)
+        total += wbytes + B * r * dm * 2 + B * r * V * 4            # logits
+        total += B * r * V * 2 + wbytes + splits * r * dm * 4       # dH partials
+    for g0 in range(0, T, ps * group):
+        rows = min(ps * group, T - g0)
+        total += B * rows * V * 2 + B * rows * dm * 2 + 2 * V * dm * 4  # dW
+    return total
+
+
 def head_main(args):
     import numpy as np
     import torch
@@ -454,6 +475,9 @@ def head_main(args):
     n_h, t_h = prof["head"]
     per_launch = flops / (n_h / args.steps)
     achieved = per_launch / (t_h / n_h * 1e-3) / 1e12
+    hbytes = head_bytes(T, dm, V, wl.ps, wl.dw_group, Bt)
+    bytes_per_launch = hbytes / (n_h / args.steps)
+    achieved_gbs = bytes_per_launch / (t_h / n_h * 1e-3) / 1e9
     loss = scale * float(row_loss.sum().item())
     from sequence_chunked_exact_amd.profile_summary import read_traffic
     out = {
@@ -474,10 +498,12 @@ def head_main(args):
         "config": {"workload": wl.name, "batch": Bt, "seq_len": T, "d_model": dm, "vocab": V, "ps_head": wl.ps,
                    "dw_group": wl.dw_group, "prompt": wl.prompt, "flops_per_step": flops, "loss": loss},
         "kernels": kernels,
-        "roofline": {"kernel": "head", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+        "roofline": {"kernel": "head", "bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / PEAK_HBM_GBS,
                      "traffic": read_traffic(os.path.join(ROOT, "profiles", f"head_{wl.name}.md"), "head"),
-                     "avg_launch_us": t_h / n_h * 1e3, "flops_per_launch": per_launch},
+                     "avg_launch_us": t_h / n_h * 1e3, "bytes_per_launch": bytes_per_launch,
+                     "flops_per_launch": per_launch, "mfma_tflops": achieved,
+                     "mfma_frac": achieved / PEAK_BF16_TFLOPS},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
