@@ -96,7 +96,7 @@ def cpu_baseline(wl, inp_raw, n_heads=8):
             "seconds": dt, "gflops": rate / 1e9}
 
 
-def layer_cpu_baseline(wl, raw, rows=2048, n_heads=4):
+def layer_cpu_baseline(wl, raw, rows=2048, n_heads=8):
     """The float64 oracle on a bounded sample of the layer step, extrapolated by FLOPs:
     the projections' forward and backward over the first `rows` positions, and the
     attention forward + backward of `n_heads` query heads over all positions."""
@@ -515,7 +515,7 @@ def head_main(args):
             threads = len(os.sched_getaffinity(0))
         hf = W.bf16_bits_to_f64(inp.raw["h"])
         wf = W.bf16_bits_to_f64(inp.raw["w"])
-        n_part = 3
+        n_part = 20
         t0 = time.perf_counter()
         for i in range(n_part):
             s0 = wl.prompt + i * wl.ps
