@@ -242,3 +242,20 @@ def test_lm_head_errors():
     assert lib.lm_head_dpo_finish(ctypes.byref(HD(2, 1024, 256, 1024, b.CA_BF16)), 100, FAKE, 0.0, 0.0, 0.1, FAKE,
                                   FAKE, None, ctypes.byref(c), None) == -1
 
+
+
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++17")])
+def test_header_compiles_standalone(lang, std, tmp_path):
+    # The public header is self-contained C (and C++) with no HIP or torch types.
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("host compiler not available")
+    src = tmp_path / ("use.c" if lang == "c" else "use.cpp")
+    src.write_text('#include "chunk_attn.h"\n'
+                   'int main(void) { chunk_attn_desc d; lm_head_desc e; spaco_layer l;\n'
+                   '  (void)sizeof d; (void)sizeof e; (void)sizeof l; return CA_OK; }\n')
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I",
+                        os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
