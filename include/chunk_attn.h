@@ -60,7 +60,7 @@ enum {
 
 enum { CA_F32 = 0, CA_BF16 = 1 };
 
-enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2 };
+enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2, CA_OP_BWD_MIN = 3 };
 
 typedef struct {
   int32_t batch;         /* >= 1 */
@@ -76,10 +76,18 @@ typedef struct {
   int32_t dtype;         /* CA_F32 or CA_BF16: type of q, k, v, o, dout */
 } chunk_attn_desc;
 
-/* Bytes of workspace the op needs for this descriptor (0 if none; the op then
+/* Bytes of workspace for the op on this descriptor (0 if none; the op then
  * accepts ws == NULL). op is CA_OP_*. For CA_OP_SPARSE_BWD the descriptor is
  * the whole-sequence one that sparse_chunk_bwd takes and chunk_len must be the
- * chunk size. Returns 0 for an invalid descriptor. */
+ * chunk size. Returns 0 for an invalid descriptor.
+ *
+ * The backward requires only CA_OP_BWD_MIN bytes (row statistics of the
+ * chunk). CA_OP_BWD and CA_OP_SPARSE_BWD add, for bf16, room for the chunk's
+ * dS^T in bf16 (n_q_heads * batch * chunk_len * kv_capacity * 2 bytes, rows and
+ * keys rounded up to 128), sized so that one workspace serves every chunk of a
+ * sweep: given that room, the dK/dV pass stores dS and the dQ pass streams it
+ * (dQ = dS K) instead of recomputing S, P and dP. The results agree within
+ * rounding; the larger workspace is faster. */
 size_t chunk_attn_workspace_size(const chunk_attn_desc* desc, int32_t op);
 
 /* Forward of one chunk (the inference-mode pass that fills the caches in SeCO,
@@ -98,7 +106,9 @@ int chunk_attn_fwd(const chunk_attn_desc* desc, const void* q, const void* k, co
  * grad_scale * dV^(:i) without atomics (each element has one writer), so the
  * caller zeroes them before the first chunk of a sweep and chunks of one sweep
  * must be issued in stream order. grad_scale is SpaCO's k/t for a sparse sweep
- * and 1 otherwise. Workspace: chunk_attn_workspace_size(desc, CA_OP_BWD). */
+ * and 1 otherwise. Workspace: at least chunk_attn_workspace_size(desc,
+ * CA_OP_BWD_MIN) bytes; chunk_attn_workspace_size(desc, CA_OP_BWD) selects the
+ * faster dQ pass for bf16. */
 int chunk_attn_bwd(const chunk_attn_desc* desc, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, const void* dout, float grad_scale,
                    float* dq, float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes,

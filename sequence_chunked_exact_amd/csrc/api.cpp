@@ -233,8 +233,14 @@ size_t chunk_attn_workspace_size(const chunk_attn_desc* d, int32_t op) {
   if (check_desc(d, op == CA_OP_SPARSE_BWD) != CA_OK) return 0;
   switch (op) {
     case CA_OP_FWD: return 0;
+    case CA_OP_BWD_MIN: return delta_bytes(d);
     case CA_OP_BWD:
-    case CA_OP_SPARSE_BWD: return delta_bytes(d);
+    case CA_OP_SPARSE_BWD:
+      // room for the dS^T blocks of any chunk of up to chunk_len rows whose
+      // prefix fits kv_capacity (bf16)
+      return delta_bytes(d) + (d->dtype == CA_BF16 ? round_up(ca::bwd_ds_bytes(d->batch, d->n_q_heads,
+                                                                                d->chunk_len, d->kv_capacity))
+                                                   : 0);
     default: return 0;
   }
 }
@@ -260,7 +266,7 @@ int chunk_attn_bwd(const chunk_attn_desc* d, const void* q, const void* k, const
     return fail(CA_ERR_SHAPE, "grad_scale is not finite");
   if ((rc = check_ws(ws, ws_bytes, delta_bytes(d)))) return rc;
   hipError_t e = ca::launch_bwd(shape_of(d), q, k, v, o, lse, dout, grad_scale, dq, dk_acc, dv_acc,
-                                (float*)ws, (hipStream_t)stream);
+                                (float*)ws, ws_bytes, (hipStream_t)stream);
   return e == hipSuccess ? CA_OK : hip_fail(e, "chunk_attn_bwd launch");
 }
 
@@ -359,7 +365,7 @@ int sparse_chunk_bwd(const chunk_attn_desc* d, int32_t seq_len, int32_t t, uint6
     s.start = i * C;
     s.q_off = i * C;
     s.len = std::min(C, seq_len - i * C);
-    e = ca::launch_bwd(s, q, k, v, o, lse, dout, gamma, dq, dk, dv, (float*)ws, st);
+    e = ca::launch_bwd(s, q, k, v, o, lse, dout, gamma, dq, dk, dv, (float*)ws, ws_bytes, st);
     if (e != hipSuccess) return hip_fail(e, "sparse_chunk_bwd chunk launch");
   }
   std::memcpy(selected_out, sel.data(), sizeof(int32_t) * t);
@@ -605,7 +611,7 @@ int spaco_stack_backward(const chunk_attn_desc* d, int32_t seq_len, int32_t n_la
       }
       if (e == hipSuccess)
         e = ca::launch_bwd(stack_attn_shape(d, s, len), q, y.k_cache, y.v_cache, o, lse, dout, 1.f, dq, y.dk_acc,
-                           y.dv_acc, (float*)(wsb + w.attn_ws), st);
+                           y.dv_acc, (float*)(wsb + w.attn_ws), delta_bytes(d), st);
       // dH_l = dH_{l+1} + (dQ W_q^T + dK W_k^T + dV W_v^T) over the chunk's rows
       float* dst = l == 0 ? dh0 : dh_nxt;
       const int32_t dst_cap = l == 0 ? h_capacity : C, dst_off = l == 0 ? s : 0;

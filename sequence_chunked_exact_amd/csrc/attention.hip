@@ -1,5 +1,8 @@
 // Chunked exact causal attention for gfx950 (CDNA4): forward, and the
-// backward split into a row-delta pass, a dK/dV pass and a dQ pass.
+// backward split into a row-delta pass, a dK/dV pass and a dQ pass. Given
+// workspace room (bf16), the dK/dV pass also stores the chunk's dS^T in bf16
+// and the dQ pass streams it (dQ = dS K, one product per visible pair);
+// otherwise the dQ pass recomputes S, P and dP (three products per pair).
 //
 // What is computed (StreamBP review, "What carries the argument": Property 3.1
 // and the partitioned attention of Eqs. (12)-(14)): chunk i's queries, at
@@ -334,6 +337,10 @@ struct BwdParams {
   float dq_scale;  // grad_scale * softmax scale
   float dk_scale;  // grad_scale * softmax scale
   float dv_scale;  // grad_scale
+  // Optional dS^T store (bf16): [batch*hq][ds_nqb blocks of kDsCols query
+  // rows][ds_keys][kDsCols]; null when dQ recomputes dS.
+  void* ds;
+  int ds_nqb, ds_keys;
 };
 
 // dQ pass. Same walk, split and staging as the forward: two groups of NW
@@ -526,9 +533,14 @@ template <typename T, int D, int NKT, int BQ, int NP>
 __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int NT = 2 * NP * 64, BKV = NP * NKT * 16, NB = 3;
+  constexpr int BKV = NP * NKT * 16, NB = 3;
   constexpr int DK = D / 32, MD = D / 16, MQ = BQ / 16, KQ = BQ / 32;
-  static_assert(2 * BQ <= NT, "row statistics: one value per thread");
+  // Only the P/dV waves load Q/dO blocks (and only the dS/dK waves store dS):
+  // vector loads and stores complete out of order with respect to each other
+  // on this chip, so a wave with both in flight has to wait for its stores
+  // whenever it waits for a load.
+  constexpr int NL = NP * 64;  // loading threads
+  static_assert(2 * BQ <= NL, "row statistics: one value per loading thread");
   __shared__ __attribute__((aligned(16))) T Qs[NB][BQ * PadLay<T, D>::RS];
   __shared__ __attribute__((aligned(16))) T Ds[NB][BQ * PadLay<T, D>::RS];
   // per buffer: LSE*log2(e) of the block's rows in [0, BQ), delta in [BQ, 2BQ)
@@ -559,7 +571,7 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
 
   // Next block to fetch, walked q tile fastest then q head.
   int f_qt = qt0, f_h = hk * G;
-  RegTile<T, BQ, D, NT> qreg, dreg;
+  RegTile<T, BQ, D, NL> qreg, dreg;
   float stat;
   bool past;  // this thread's LSE row lies past the chunk: zero weight
   auto fetch = [&]() {
@@ -605,8 +617,10 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int md = 0; md < MD; ++md) acc[nk][md] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  fetch();
-  publish(0);
+  if (pv_wave) {
+    fetch();
+    publish(0);
+  }
   wait_loads();
   __syncthreads();
 
@@ -616,7 +630,7 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   int qv = qt0;  // q tile of this wave's block
   for (int it = 0; it <= iters; ++it) {
     const bool more = it + 1 < iters;
-    if (more) fetch();
+    if (more && pv_wave) fetch();
     const int blk = pv_wave ? it : it - 1;
     const int q0 = qv * BQ;
     const int q_lo = p.start + q0, q_hi = p.start + min(q0 + BQ, p.len) - 1;
@@ -681,6 +695,28 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
             wf[kq][nk] = pack44<T>(lo, hi);
           }
         }
+        // Hand dS to the dQ pass: this lane's slots are keys wk0 + 16 nk + n
+        // against query rows q0 + 32 kq + {4g..4g+3, 16+4g..16+4g+3}; they are
+        // stored key-major (dS^T) as they are, so column 32 kq + 8 g + s of a
+        // key's row holds query row 32 kq + tile_row(8 g + s) and each lane
+        // writes one 16-byte run.
+        if constexpr (sizeof(T) == 2) {
+          static_assert(BKV == kDsKeyPad && kDsCols % BQ == 0, "dS^T block shape");
+          if (p.ds) {
+            const int nqb = qt_end - qt0;
+            const int hb = hk * G + blk / nqb;
+            bf16* dsb = (bf16*)p.ds +
+                        ((size_t)((b * p.hq + hb) * p.ds_nqb + q0 / kDsCols) * p.ds_keys + wk0) * kDsCols +
+                        q0 % kDsCols;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+              for (int nk = 0; nk < NKT; ++nk) {
+                *(bf16x8*)(dsb + (size_t)(nk * 16 + n) * kDsCols + kq * 32 + 8 * g) =
+                    __builtin_bit_cast(bf16x8, wf[kq][nk]);
+              }
+          }
+        }
       }
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq)
@@ -693,7 +729,7 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
     }
     // Buffer (it + 1) % NB last served block it - 2, whose dS/dK pass ended
     // before the previous barrier.
-    if (more) publish((it + 1) % NB);
+    if (more && pv_wave) publish((it + 1) % NB);
     __syncthreads();
   }
 
@@ -717,6 +753,152 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int md = 0; md < MD; ++md) dst[(size_t)key * D + md * 16 + n] = old[md][i] + scale * acc[nk][md][i];
       }
+    }
+  }
+}
+
+// Query row (within a group of 32) held by column p of a stored dS^T row:
+// the dK/dV pass writes each lane's fragment slots as they are, so column
+// 8 g + s holds row 4 g + s for s < 4 and 16 + 4 g + s - 4 otherwise.
+__device__ __forceinline__ int tile_row(int p) {
+  const int g = (p & 31) >> 3, s = p & 7;
+  return (p & ~31) + (s < 4 ? 4 * g + s : 12 + 4 * g + s);
+}
+
+// dQ from the dS^T blocks stored by the dK/dV pass (bf16): dQ^T = K^T dS^T
+// per key tile, so each lane owns one (stored) query column. Grid
+// (batch, q head, block of kDsCols query rows); two groups of NW waves own the
+// same query columns and take the even and odd key tiles; pairs of K and dS^T
+// tiles stream into double-buffered LDS by direct global->LDS loads one pair
+// ahead, and both operands are read through the transposing path. Entries
+// above the diagonal were never written (the dK/dV pass skips them), so
+// diagonal tiles select zero there. At the end group 1 hands its partial dQ^T
+// to group 0 through LDS.
+template <int D, int NQT, int BK, int NW>
+__global__ __launch_bounds__(2 * NW * 64) void dqs_kernel(BwdParams p) {
+  using T = bf16;
+  using E = Elt<T>;
+  using frag = typename E::frag;
+  using Lk = SwzLay<T, D>;
+  using Ls = SwzLay<T, kDsCols>;
+  constexpr int BQ = NW * NQT * 16, MD = D / 16, KB2 = BK / 32;
+  static_assert(BQ == kDsCols, "one workgroup per dS^T block");
+  __shared__ __attribute__((aligned(16))) T Kb0[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) T Sb0[2 * BK * BQ];
+  __shared__ __attribute__((aligned(16))) T Kb1[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) T Sb1[2 * BK * BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / NW, wq = wave % NW;
+  const int n = lane & 15, g = lane >> 4;
+  const int nqt = (p.len + BQ - 1) / BQ;
+  const int work_id = xcd_order(blockIdx.x, gridDim.x);
+  const int qt = nqt - 1 - work_id % nqt;  // longest rows first
+  const int h = (work_id / nqt) % p.hq, b = work_id / (nqt * p.hq);
+  const int hk = h / (p.hq / p.hkv);
+  const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
+  const T* S = (const T*)p.ds + ((size_t)(b * p.hq + h) * p.ds_nqb + qt) * p.ds_keys * BQ;
+  const int L = p.start + p.len;
+  const int r0 = qt * BQ;
+  const int n_tiles = (p.start + min(r0 + BQ, p.len) - 1) / BK + 1;
+  const int n_pairs = (n_tiles + 1) / 2;
+  static_assert(NQT * 16 == 32, "a wave owns one group of 32 stored columns");
+  const int wr0 = r0 + wq * NQT * 16;
+  const bool active = wr0 < p.len;
+  const int wq_lo = p.start + wr0;
+  const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
+  int qrow[NQT];  // chunk row of this lane's column in each 16-column tile
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) qrow[nt] = wr0 + tile_row(nt * 16 + n);
+
+  auto stage = [&](T* kd, T* sd, int pair) {
+    stage_tile<T, 2 * BK, D, 2 * NW>(kd, K, 2 * pair * BK, L, wave, lane);
+    stage_tile<T, 2 * BK, BQ, 2 * NW>(sd, S, 2 * pair * BK, p.ds_keys, wave, lane);
+  };
+  stage(Kb0, Sb0, 0);
+  f32x4 acc[MD][NQT];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) acc[md][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  wait_loads();
+  __syncthreads();
+
+  auto pair_step = [&](int i, const T* Kc, const T* Sc, T* Kn, T* Sn) {
+    if (i + 1 < n_pairs) stage(Kn, Sn, i + 1);
+    const int j = 2 * i + grp;
+    const int kb0 = j * BK;
+    if (active && j < n_tiles && kb0 <= wq_hi) {
+      const T* Kt = Kc + grp * BK * D;
+      const T* St = Sc + grp * BK * BQ;
+      const bool diag = kb0 + BK - 1 > wq_lo;
+#pragma unroll
+      for (int kb2 = 0; kb2 < KB2; ++kb2) {
+        frag sf[NQT];
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) {
+          sf[nt] = ldT8<Ls>(St, kb2 * 32, wq * NQT * 16 + nt * 16, lane);
+          if (diag) {
+            const int qp = p.start + qrow[nt];
+#pragma unroll
+            for (int sl = 0; sl < 8; ++sl) {
+              const int key = kb0 + kb2 * 32 + (sl < 4 ? 4 * g + sl : 16 + 4 * g + sl - 4);
+              if (key > qp) sf[nt][sl] = (T)0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+          const frag a = ldT8<Lk>(Kt, kb2 * 32, md * 16, lane);
+#pragma unroll
+          for (int nt = 0; nt < NQT; ++nt) E::mma(acc[md][nt], a, sf[nt]);
+        }
+      }
+    }
+    wait_loads();
+    __syncthreads();
+  };
+  for (int i = 0; i < n_pairs; i += 2) {
+    pair_step(i, Kb0, Sb0, Kb1, Sb1);
+    if (i + 1 < n_pairs) pair_step(i + 1, Kb1, Sb1, Kb0, Sb0);
+  }
+
+  // Merge: group 1 publishes its dQ^T per lane in two halves of the head
+  // dimension (Kb0 and Sb0), group 0 adds and stores.
+  constexpr int HALF = MD / 2 * 4;
+  static_assert(sizeof(Kb0) >= (size_t)NQT * NW * 64 * HALF * sizeof(float) &&
+                    sizeof(Sb0) >= (size_t)NQT * NW * 64 * HALF * sizeof(float),
+                "merge area");
+  float* xo0 = (float*)Kb0;
+  float* xo1 = (float*)Sb0;
+  if (grp == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      const size_t slot = (size_t)(nt * NW + wq);
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float* x = md < MD / 2 ? xo0 : xo1;
+          x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane] = acc[md][nt][e];
+        }
+    }
+  }
+  __syncthreads();
+  if (grp == 1 || !active) return;
+  float* DQ = p.dq + ((size_t)(b * p.hq + h) * p.q_cap + p.q_off) * D;
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    const size_t slot = (size_t)(nt * NW + wq);
+    const int row = qrow[nt];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const float* x = md < MD / 2 ? xo0 : xo1;
+      f32x4 v = acc[md][nt];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] += x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane];
+      if (row < p.len) *(f32x4*)(DQ + (size_t)row * D + md * 16 + 4 * g) = v * p.dq_scale;
     }
   }
 }
@@ -788,10 +970,14 @@ hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v,
 template <typename T, int D>
 hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
-                    float* ws, hipStream_t st) {
+                    float* ws, size_t ws_bytes, hipStream_t st) {
   using C = Cfg<T, D>;
   constexpr int LPR = D / Elt<T>::VEC;
   const int rows = s.batch * s.hq * s.len;
+  const int L = s.start + s.len;
+  // dS^T goes through the workspace when it has room (bf16 only).
+  const size_t ds_need = bwd_ds_bytes(s.batch, s.hq, s.len, L);
+  const bool use_ds = sizeof(T) == 2 && ws_bytes >= bwd_ws_base(rows) + ds_need;
   const int threads = rows * LPR;
   float* delta = ws;
   float* lse2 = ws + bwd_ws_stride(rows);
@@ -803,17 +989,25 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   if (e != hipSuccess) return e;
   BwdParams p{q,     k,     v,       dout,     lse,     delta,   lse2,  dq,   dk,
               dv,    s.hq,  s.hkv,   s.q_cap,  s.kv_cap, s.q_off, s.start, s.len,
-              exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs};
+              exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs,
+              use_ds ? (void*)((char*)ws + bwd_ws_base(rows)) : nullptr,
+              (s.len + kDsCols - 1) / kDsCols, (L + kDsKeyPad - 1) / kDsKeyPad * kDsKeyPad};
   constexpr int BKV = C::KV_NP * C::KV_NKT * 16;
-  const int L = s.start + s.len;
   prof_begin(CA_KERNEL_DKDV, st);
   hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(((L + BKV - 1) / BKV) * s.hkv * s.batch),
                      dim3(2 * C::KV_NP * 64), 0, st, p);
   prof_end(CA_KERNEL_DKDV, st);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int BQ = C::DQ_NW * C::DQ_NQT * 16;
   prof_begin(CA_KERNEL_DQ, st);
+  if constexpr (sizeof(T) == 2) {
+    if (use_ds) {
+      hipLaunchKernelGGL((dqs_kernel<D, 2, 64, 4>), dim3(p.ds_nqb * s.hq * s.batch), dim3(2 * 4 * 64), 0, st, p);
+      prof_end(CA_KERNEL_DQ, st);
+      return hipGetLastError();
+    }
+  }
+  constexpr int BQ = C::DQ_NW * C::DQ_NQT * 16;
   hipLaunchKernelGGL((dq_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW>), dim3(((s.len + BQ - 1) / BQ) * s.hq * s.batch),
                      dim3(2 * C::DQ_NW * 64), 0, st, p);
   prof_end(CA_KERNEL_DQ, st);
@@ -834,13 +1028,13 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
 
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
-                      float* ws, hipStream_t st) {
+                      float* ws, size_t ws_bytes, hipStream_t st) {
   if (s.dtype == CA_BF16) {
-    return s.head_dim == 128 ? bwd_impl<bf16, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, st)
-                             : bwd_impl<bf16, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, st);
+    return s.head_dim == 128 ? bwd_impl<bf16, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st)
+                             : bwd_impl<bf16, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st);
   }
-  return s.head_dim == 128 ? bwd_impl<float, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, st)
-                           : bwd_impl<float, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, st);
+  return s.head_dim == 128 ? bwd_impl<float, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st)
+                           : bwd_impl<float, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st);
 }
 
 hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap, int src_cap,

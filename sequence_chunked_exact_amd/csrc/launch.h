@@ -22,15 +22,26 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
                       float* lse, hipStream_t st);
 
 // Backward workspace: two float arrays of batch*hq*len rows (row delta and
-// LSE*log2(e)), each starting on a 256-byte boundary.
+// LSE*log2(e)), each starting on a 256-byte boundary; this much is required.
 inline size_t bwd_ws_stride(size_t rows) { return (rows + 63) / 64 * 64; }
 inline size_t bwd_ws_bytes(size_t rows) { return 2 * bwd_ws_stride(rows) * sizeof(float); }
+// Optional, after the required part rounded up to 256 bytes (bf16 only): the
+// chunk's dS^T in blocks of 128 query rows, [batch*hq][len/128][keys][128],
+// keys padded to 128, for a dQ pass that reads dS instead of recomputing it.
+constexpr int kDsCols = 128, kDsKeyPad = 128;
+inline size_t bwd_ws_base(size_t rows) { return (bwd_ws_bytes(rows) + 255) / 256 * 256; }
+inline size_t bwd_ds_bytes(size_t batch, size_t hq, size_t len, size_t keys) {
+  return batch * hq * ((len + kDsCols - 1) / kDsCols) * ((keys + kDsKeyPad - 1) / kDsKeyPad * kDsKeyPad) *
+         kDsCols * 2;
+}
 
 // Backward: row statistics into the workspace, then dq (overwritten, times
-// grad_scale) and the dk/dv accumulators (incremented).
+// grad_scale) and the dk/dv accumulators (incremented). ws_bytes decides the
+// dQ pass: with room for the dS^T blocks after the required part (bf16), the
+// dK/dV pass stores dS and dQ = dS K streams it; otherwise dQ recomputes dS.
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, float grad_scale,
-                      float* dq, float* dk, float* dv, float* ws, hipStream_t st);
+                      float* dq, float* dk, float* dv, float* ws, size_t ws_bytes, hipStream_t st);
 
 // acc[b][h][r][:] += scale * src[b][h][r][:], r < rows.
 hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap,

@@ -107,13 +107,30 @@ def test_pointer_errors():
 
 def test_workspace_errors():
     d = desc()
-    need = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD)
+    need = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD_MIN)
     assert need >= 4 * 4 * 256 and need % 256 == 0
     assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_FWD) == 0
     assert bwd(d, ws=None) == -5
     assert bwd(d, ws_bytes=need - 1) == -5
     assert bwd(d, ws=MISALIGNED, ws_bytes=need) == -4
     assert lib.chunk_attn_workspace_size(ctypes.byref(desc(head_dim=80)), b.CA_OP_BWD) == 0
+    assert lib.chunk_attn_workspace_size(ctypes.byref(desc(head_dim=80)), b.CA_OP_BWD_MIN) == 0
+
+
+def test_workspace_sizes_cover_the_ds_blocks():
+    # bf16: the full size adds the dS^T blocks of a chunk_len-row chunk against
+    # a kv_capacity prefix (rows and keys rounded up to 128, 2 bytes each), so
+    # one workspace serves every chunk of a sweep; float32 needs no more.
+    for kw, rows, keys in ((dict(), 256, 1024), (dict(chunk_len=200, kv_capacity=1000), 256, 1024),
+                           (dict(chunk_len=129, kv_capacity=130, q_capacity=129, chunk_start=0), 256, 256)):
+        d = desc(**kw)
+        lo = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD_MIN)
+        full = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD)
+        assert full - lo == d.batch * d.n_q_heads * rows * keys * 2
+        assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_SPARSE_BWD) == full
+        f32 = desc(dtype=b.CA_F32, **kw)
+        assert (lib.chunk_attn_workspace_size(ctypes.byref(f32), b.CA_OP_BWD)
+                == lib.chunk_attn_workspace_size(ctypes.byref(f32), b.CA_OP_BWD_MIN))
 
 
 def test_accumulate_errors():
