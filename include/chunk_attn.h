@@ -223,7 +223,9 @@ typedef struct {
 
 /* Workspace bytes for spaco_stack_forward / spaco_stack_backward (chunk-local
  * activations of every layer, the chunk's gradients, the attention and
- * projection workspaces). 0 for invalid arguments. */
+ * projection workspaces; the attention part is chunk_attn_workspace_size(desc,
+ * CA_OP_BWD), so a bf16 stack streams dS in its dQ passes). 0 for invalid
+ * arguments. */
 size_t spaco_stack_workspace_size(const chunk_attn_desc* desc, int32_t n_layers);
 
 /* Inference-mode pass: every chunk in ascending order through every layer,

@@ -416,7 +416,7 @@ namespace {
 
 // Chunk-local buffers in the stack workspace, each on a 256-byte boundary.
 struct StackWs {
-  size_t hbuf, q, o, lse, dout, dq, dh_a, dh_b, attn_ws, proj_ws, total;
+  size_t hbuf, q, o, lse, dout, dq, dh_a, dh_b, attn_ws, attn_bytes, proj_ws, total;
   size_t h_stride, q_stride, lse_stride;  // per-layer strides (bytes)
 };
 
@@ -445,7 +445,9 @@ StackWs stack_ws(const chunk_attn_desc* d, int32_t L) {
   w.dh_b = at;
   at += round_up(B * C * dm * 4);
   w.attn_ws = at;
-  at += delta_bytes(d);
+  // the attention backward's row statistics and, for bf16, its dS^T blocks
+  w.attn_bytes = std::max(delta_bytes(d), chunk_attn_workspace_size(d, CA_OP_BWD));
+  at += w.attn_bytes;
   w.proj_ws = at;
   ca::ProjShape ps = proj_shape(d, (int32_t)dm, d->chunk_len, 0);
   at += round_up(ca::proj_bwd_ws_bytes(ps));
@@ -611,7 +613,7 @@ int spaco_stack_backward(const chunk_attn_desc* d, int32_t seq_len, int32_t n_la
       }
       if (e == hipSuccess)
         e = ca::launch_bwd(stack_attn_shape(d, s, len), q, y.k_cache, y.v_cache, o, lse, dout, 1.f, dq, y.dk_acc,
-                           y.dv_acc, (float*)(wsb + w.attn_ws), delta_bytes(d), st);
+                           y.dv_acc, (float*)(wsb + w.attn_ws), w.attn_bytes, st);
       // dH_l = dH_{l+1} + (dQ W_q^T + dK W_k^T + dV W_v^T) over the chunk's rows
       float* dst = l == 0 ? dh0 : dh_nxt;
       const int32_t dst_cap = l == 0 ? h_capacity : C, dst_off = l == 0 ? s : 0;
