@@ -181,6 +181,41 @@ def test_bf16_ds_and_recompute_paths_agree():
     assert ea <= 2e-2 and eb <= 2e-2 and ab <= 2e-2
 
 
+def test_bf16_ds_workspace_garbage_never_read():
+    # The dQ pass reads only the dS^T entries the dK/dV pass wrote: fill the
+    # workspace with NaN (all-ones bytes) before every chunk's backward, with
+    # ragged chunks, a tail block and GQA, and the gradients stay exact.
+    B = binding()
+    wl = custom("bf16_nan_ws", 777, 200, 4, 2, 128, "bf16", seed=41, spike=1)
+    inp = W.make_inputs(wl)
+    t = to_dev(inp)
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    T, C = 777, 200
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    B.chunked_forward(q, k, v, o, lse, chunk=C, seq_len=T)
+    dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+    dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
+    desc = B.make_desc(q, k, chunk_start=0, chunk_len=C)
+    ws = torch.empty(B.chunk_attn_workspace_size(desc, B.CA_OP_BWD), dtype=torch.uint8, device=DEV)
+    assert ws.numel() > B.chunk_attn_workspace_size(desc, B.CA_OP_BWD_MIN)   # the dS path is taken
+    for i in reversed(range(-(-T // C))):
+        s = i * C
+        ws.fill_(255)
+        B.chunk_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, chunk_start=s, chunk_len=min(C, T - s), q_row_offset=s,
+                         workspace=ws)
+    torch.cuda.synchronize()
+    f = inp.f64
+    rdq, rdk, rdv = A.backward(f["q"], f["k"], f["v"], f["do"], 1.0)
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        g = got.cpu().double().numpy()
+        assert np.isfinite(g).all(), name
+        e = rel_inf(g, ref)
+        note(f"       {name} error {e:.2e}")
+        assert e <= 2e-2, (name, e)
+
+
 # ------------------------------------------------------------------ sparse driver
 def test_sparse_reduced_matches_oracle():
     wl = W.WORKLOADS["sparse_64k"]
