@@ -780,9 +780,9 @@ __global__ __launch_bounds__(2 * NW * 64) void dqs_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
   using Lk = SwzLay<T, D>;
-  using Ls = SwzLay<T, kDsCols>;
   constexpr int BQ = NW * NQT * 16, MD = D / 16, KB2 = BK / 32;
-  static_assert(BQ == kDsCols, "one workgroup per dS^T block");
+  using Ls = SwzLay<T, BQ>;
+  static_assert(kDsCols % BQ == 0 && NQT * 16 <= 32, "workgroups cover whole slices of a dS^T block");
   __shared__ __attribute__((aligned(16))) T Kb0[2 * BK * D];
   __shared__ __attribute__((aligned(16))) T Sb0[2 * BK * BQ];
   __shared__ __attribute__((aligned(16))) T Kb1[2 * BK * D];
@@ -798,23 +798,25 @@ __global__ __launch_bounds__(2 * NW * 64) void dqs_kernel(BwdParams p) {
   const int h = (work_id / nqt) % p.hq, b = work_id / (nqt * p.hq);
   const int hk = h / (p.hq / p.hkv);
   const T* K = (const T*)p.k + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
-  const T* S = (const T*)p.ds + ((size_t)(b * p.hq + h) * p.ds_nqb + qt) * p.ds_keys * BQ;
+  // This workgroup's columns [cb, cb + BQ) of stored block qt * BQ / kDsCols,
+  // whose column c holds chunk row rb + tile_row(c).
+  const int rb = qt * BQ / kDsCols * kDsCols, cb = qt * BQ % kDsCols;
+  const T* S = (const T*)p.ds + ((size_t)(b * p.hq + h) * p.ds_nqb + qt * BQ / kDsCols) * p.ds_keys * kDsCols + cb;
   const int L = p.start + p.len;
-  const int r0 = qt * BQ;
-  const int n_tiles = (p.start + min(r0 + BQ, p.len) - 1) / BK + 1;
+  const int n_tiles = (p.start + min(rb + tile_row(cb + BQ - 1), p.len - 1)) / BK + 1;
   const int n_pairs = (n_tiles + 1) / 2;
-  static_assert(NQT * 16 == 32, "a wave owns one group of 32 stored columns");
-  const int wr0 = r0 + wq * NQT * 16;
-  const bool active = wr0 < p.len;
-  const int wq_lo = p.start + wr0;
-  const int wq_hi = p.start + min(wr0 + NQT * 16, p.len) - 1;
+  const int c0 = cb + wq * NQT * 16;  // this wave's first stored column
+  const int row_lo = rb + tile_row(c0), row_hi = rb + tile_row(c0 + NQT * 16 - 1);
+  const bool active = row_lo < p.len;
+  const int wq_lo = p.start + row_lo;
+  const int wq_hi = p.start + min(row_hi, p.len - 1);
   int qrow[NQT];  // chunk row of this lane's column in each 16-column tile
 #pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) qrow[nt] = wr0 + tile_row(nt * 16 + n);
+  for (int nt = 0; nt < NQT; ++nt) qrow[nt] = rb + tile_row(c0 + nt * 16 + n);
 
   auto stage = [&](T* kd, T* sd, int pair) {
     stage_tile<T, 2 * BK, D, 2 * NW>(kd, K, 2 * pair * BK, L, wave, lane);
-    stage_tile<T, 2 * BK, BQ, 2 * NW>(sd, S, 2 * pair * BK, p.ds_keys, wave, lane);
+    stage_tile<T, 2 * BK, BQ, 2 * NW, kDsCols>(sd, S, 2 * pair * BK, p.ds_keys, wave, lane);
   };
   stage(Kb0, Sb0, 0);
   f32x4 acc[MD][NQT];
@@ -952,17 +954,43 @@ float exp2_coef(float scale) {
   return c > 1e-30f ? c : 1e-30f;
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Query-tile workgroups of a forward / recompute-dQ launch with NQT 16-row
+// tiles per wave.
+template <int NW, int NQT>
+int q_tiles(const Shape& s) {
+  constexpr int BQ = NW * NQT * 16;
+  return ((s.len + BQ - 1) / BQ) * s.hq * s.batch;
+}
+
 template <typename T, int D>
 hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v, void* o, float* lse,
                     hipStream_t st) {
   using C = Cfg<T, D>;
-  constexpr int BQ = C::FWD_NW * C::FWD_NQT * 16;
   FwdParams p{q,     k,     v,       o,        lse,     s.hq,    s.hkv, s.q_cap, s.kv_cap, s.q_off,
               s.start, s.len, exp2_coef(s.scale), s.scale < 0.f ? 1 : 0};
-  dim3 grid(((s.len + BQ - 1) / BQ) * s.hq * s.batch);
   prof_begin(CA_KERNEL_FWD, st);
-  hipLaunchKernelGGL((fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), grid, dim3(2 * C::FWD_NW * 64), 0,
-                     st, p);
+  // A chunk too short to give every compute unit a 128-row tile (e.g. 500
+  // rows x 32 heads = 128 tiles) runs 64-row tiles, one 16-row tile per wave.
+  if (C::FWD_NQT > 1 && q_tiles<C::FWD_NW, C::FWD_NQT>(s) < device_cus()) {
+    hipLaunchKernelGGL((fwd_kernel<T, D, 1, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, 1>(s)),
+                       dim3(2 * C::FWD_NW * 64), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, C::FWD_NQT>(s)),
+                       dim3(2 * C::FWD_NW * 64), 0, st, p);
+  }
   prof_end(CA_KERNEL_FWD, st);
   return hipGetLastError();
 }
@@ -1002,14 +1030,23 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   prof_begin(CA_KERNEL_DQ, st);
   if constexpr (sizeof(T) == 2) {
     if (use_ds) {
-      hipLaunchKernelGGL((dqs_kernel<D, 2, 64, 4>), dim3(p.ds_nqb * s.hq * s.batch), dim3(2 * 4 * 64), 0, st, p);
+      if (p.ds_nqb * s.hq * s.batch < device_cus()) {  // short chunk: 64-column workgroups
+        hipLaunchKernelGGL((dqs_kernel<D, 1, 64, 4>), dim3(((s.len + 63) / 64) * s.hq * s.batch), dim3(2 * 4 * 64),
+                           0, st, p);
+      } else {
+        hipLaunchKernelGGL((dqs_kernel<D, 2, 64, 4>), dim3(p.ds_nqb * s.hq * s.batch), dim3(2 * 4 * 64), 0, st, p);
+      }
       prof_end(CA_KERNEL_DQ, st);
       return hipGetLastError();
     }
   }
-  constexpr int BQ = C::DQ_NW * C::DQ_NQT * 16;
-  hipLaunchKernelGGL((dq_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW>), dim3(((s.len + BQ - 1) / BQ) * s.hq * s.batch),
-                     dim3(2 * C::DQ_NW * 64), 0, st, p);
+  if (C::DQ_NQT > 1 && q_tiles<C::DQ_NW, C::DQ_NQT>(s) < device_cus()) {
+    hipLaunchKernelGGL((dq_kernel<T, D, 1, C::DQ_BK, C::DQ_NW>), dim3(q_tiles<C::DQ_NW, 1>(s)),
+                       dim3(2 * C::DQ_NW * 64), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((dq_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW>), dim3(q_tiles<C::DQ_NW, C::DQ_NQT>(s)),
+                       dim3(2 * C::DQ_NW * 64), 0, st, p);
+  }
   prof_end(CA_KERNEL_DQ, st);
   return hipGetLastError();
 }

@@ -238,7 +238,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // side, and each instruction still reads whole rows). Rows at or beyond
 // `limit` (>= 1) re-read row limit-1; every consumer gives such rows zero
 // weight (keys past the prefix are causally masked).
-template <typename T, int ROWS, int D, int NW>
+// SRC_STRIDE: elements between consecutive source rows (a tile may be a
+// column slice of a wider row-major matrix).
+template <typename T, int ROWS, int D, int NW, int SRC_STRIDE = D>
 __device__ __forceinline__ void stage_tile(T* lds, const T* head, int row0, int limit, int wave, int lane) {
   using Lt = SwzLay<T, D>;
   constexpr int CH = Lt::CH, RPI = 64 / CH, PER_WAVE = ROWS / NW;
@@ -250,7 +252,7 @@ __device__ __forceinline__ void stage_tile(T* lds, const T* head, int row0, int 
     const int rb = wave * PER_WAVE + i * RPI;  // wave-uniform first row of this instruction
     const int r = rb + rl;
     const int c = slot ^ Lt::swz(r);
-    const T* src = head + (size_t)min(row0 + r, limit - 1) * D + c * Lt::EPC;
+    const T* src = head + (size_t)min(row0 + r, limit - 1) * SRC_STRIDE + c * Lt::EPC;
     __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + rb * D), 16, 0, 0);
   }
 #endif
