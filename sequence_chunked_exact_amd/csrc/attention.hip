@@ -341,6 +341,7 @@ struct BwdParams {
   // rows][ds_keys][kDsCols]; null when dQ recomputes dS.
   void* ds;
   int ds_nqb, ds_keys;
+  int kv_first, kv_end;  // dK/dV pass: the launch's key tiles cover keys [kv_first, kv_end)
 };
 
 // dQ pass. Same walk, split and staging as the forward: two groups of NW
@@ -555,11 +556,11 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   const int n = lane & 15, g = lane >> 4;
   const int G = p.hq / p.hkv;
   const int L = p.start + p.len;
-  const int nkt = (L + BKV - 1) / BKV;
+  const int nkt = (p.kv_end - p.kv_first + BKV - 1) / BKV;
   const int work_id = xcd_order(blockIdx.x, gridDim.x);
   const int kt = work_id % nkt;  // ascending: the first key tiles see the most queries
   const int hk = (work_id / nkt) % p.hkv, b = work_id / (nkt * p.hkv);
-  const int kb0 = kt * BKV;
+  const int kb0 = p.kv_first + kt * BKV;
   const int wk0 = kb0 + pair * NKT * 16;
   const float c2 = p.c2;
 
@@ -1019,19 +1020,36 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
               dv,    s.hq,  s.hkv,   s.q_cap,  s.kv_cap, s.q_off, s.start, s.len,
               exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs,
               use_ds ? (void*)((char*)ws + bwd_ws_base(rows)) : nullptr,
-              (s.len + kDsCols - 1) / kDsCols, (L + kDsKeyPad - 1) / kDsKeyPad * kDsKeyPad};
-  constexpr int BKV = C::KV_NP * C::KV_NKT * 16;
+              (s.len + kDsCols - 1) / kDsCols, (L + kDsKeyPad - 1) / kDsKeyPad * kDsKeyPad, 0, L};
+  // Every workgroup of the dK/dV pass owns one key tile and walks all the
+  // chunk's queries that see it, so the pass takes whole "rounds" of one tile
+  // per compute unit. Key tiles of half the size (16 keys per wave) take ~3/4
+  // of a round: a prefix that fills at most half the units runs on them alone,
+  // and when whole rounds of full tiles leave a remainder that half-size
+  // tiles can cover in one round, that remainder (the chunk's own diagonal
+  // keys, which the fewest queries see) goes to a second launch of them.
+  constexpr int BKV = C::KV_NP * C::KV_NKT * 16, BKV1 = C::KV_NP * 16;
+  const int cus = device_cus(), heads = s.hkv * s.batch;
+  const int tiles = (L + BKV - 1) / BKV;
+  const int rounds = tiles * heads / cus;
+  const int tiles_a = rounds * cus / heads;  // full tiles per head in whole rounds
+  const bool split = C::KV_NKT > 1 && rounds >= 1 && tiles_a < tiles &&
+                     (L - tiles_a * BKV + BKV1 - 1) / BKV1 * heads <= cus;
   prof_begin(CA_KERNEL_DKDV, st);
-  const int kv_tiles = ((L + BKV - 1) / BKV) * s.hkv * s.batch;
-  if (C::KV_NKT > 1 && 2 * kv_tiles <= device_cus()) {
-    // A prefix this short fills at most half the compute units: key tiles of
-    // half the size (16 keys per wave) finish in one round of ~3/4 the time.
-    constexpr int BKV1 = C::KV_NP * 16;
-    hipLaunchKernelGGL((dkdv_kernel<T, D, 1, C::KV_BQ, C::KV_NP>), dim3(((L + BKV1 - 1) / BKV1) * s.hkv * s.batch),
+  if (C::KV_NKT > 1 && 2 * tiles * heads <= cus) {
+    hipLaunchKernelGGL((dkdv_kernel<T, D, 1, C::KV_BQ, C::KV_NP>), dim3((L + BKV1 - 1) / BKV1 * heads),
+                       dim3(2 * C::KV_NP * 64), 0, st, p);
+  } else if (split) {
+    p.kv_end = tiles_a * BKV;
+    hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(tiles_a * heads),
+                       dim3(2 * C::KV_NP * 64), 0, st, p);
+    p.kv_first = tiles_a * BKV;
+    p.kv_end = L;
+    hipLaunchKernelGGL((dkdv_kernel<T, D, 1, C::KV_BQ, C::KV_NP>), dim3((L - p.kv_first + BKV1 - 1) / BKV1 * heads),
                        dim3(2 * C::KV_NP * 64), 0, st, p);
   } else {
-    hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(kv_tiles), dim3(2 * C::KV_NP * 64), 0,
-                       st, p);
+    hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(tiles * heads),
+                       dim3(2 * C::KV_NP * 64), 0, st, p);
   }
   prof_end(CA_KERNEL_DKDV, st);
   e = hipGetLastError();
