@@ -1043,6 +1043,8 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
     p.kv_end = tiles_a * BKV;
     hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(tiles_a * heads),
                        dim3(2 * C::KV_NP * 64), 0, st, p);
+    prof_end(CA_KERNEL_DKDV, st);  // timed as two launches, as a kernel trace counts them
+    prof_begin(CA_KERNEL_DKDV, st);
     p.kv_first = tiles_a * BKV;
     p.kv_end = L;
     hipLaunchKernelGGL((dkdv_kernel<T, D, 1, C::KV_BQ, C::KV_NP>), dim3((L - p.kv_first + BKV1 - 1) / BKV1 * heads),

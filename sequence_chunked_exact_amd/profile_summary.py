@@ -94,6 +94,13 @@ def summarize_main(args):
     for r in rows:
         lines.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
+    # a kernel built in several variants (tile shapes) has one row per variant
+    mine = [r for r in rows if short_name(r["Name"]) == args.kernel]
+    if mine:
+        calls = sum(int(r["Calls"]) for r in mine)
+        total_ns = sum(float(r["TotalDurationNs"]) for r in mine)
+        lines += ["", f"`{args.kernel}` over all its variants: {calls} dispatches, mean "
+                      f"{total_ns / calls / 1e3:.1f} us"]
     out = {}
     if args.fetch and args.write and args.cal_fetch and args.cal_write:
         match = args.match or args.kernel
