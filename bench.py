@@ -36,6 +36,44 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+
+def timed_steps(B, torch, step, steps, pick_dominant, profile_steps=2):
+    """Time `steps` calls of step() between two events on the current stream.
+
+    Every launch the library brackets with events costs a little GPU time
+    between kernels, so the per-kernel breakdown comes from `profile_steps`
+    untimed steps with every kernel bracketed, and inside the timed region
+    only the launches of the dominant kernel (pick_dominant(kernels)) carry
+    events: its average duration is measured live over the timed region.
+    Returns (ms_per_step, per_step_ms, kernels, dominant, (launches, total_ms)).
+    """
+    B.profile_select(None)
+    B.profile_start()
+    for _ in range(profile_steps):
+        step()
+    torch.cuda.synchronize()
+    B.profile_stop()
+    kernels = {n_: {"launches_per_step": c_ / profile_steps, "ms_per_step": t_ / profile_steps,
+                    "avg_us": t_ / c_ * 1e3}
+               for n_, (c_, t_) in B.profile_read().items() if c_}
+    dom = pick_dominant(kernels)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    B.profile_select([dom])
+    B.profile_start()
+    e0.record(stream)
+    for i in range(steps):
+        step()
+        marks[i].record(stream)
+    torch.cuda.synchronize()
+    B.profile_stop()
+    B.profile_select(None)
+    ms = e0.elapsed_time(marks[-1]) / steps
+    per_step = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, steps)]
+    return ms, per_step, kernels, dom, B.profile_read()[dom]
+
 def causal_pairs(start: int, length: int) -> int:
     """Visible (query, key) pairs of one chunk for one head."""
     return length * start + length * (length + 1) // 2
@@ -189,27 +227,14 @@ def layer_main(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} layer steps")
-    B.profile_start()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    B.profile_stop()
-    ms = e0.elapsed_time(e1) / args.steps
-    prof = B.profile_read()
+    ms, _, kernels, _, (n_proj, t_proj) = timed_steps(B, torch, step, args.steps, lambda k_: "proj")
     pairs = sum(causal_pairs(s, min(C, T - s)) for s in starts)
     attn_flops = 14 * d * Hq * pairs
     proj_flops = 3 * 2 * Bt * T * dm * (Hq + 2 * Hkv) * d
     total = attn_flops + proj_flops
-    kernels = {n_: {"launches_per_step": c_ / args.steps, "ms_per_step": t_ / args.steps, "avg_us": t_ / c_ * 1e3}
-               for n_, (c_, t_) in prof.items() if c_}
     log(f"[bench] {ms:.3f} ms/layer step; kernels " + json.dumps(kernels))
     from sequence_chunked_exact_amd.profile_summary import read_traffic
-    n_proj, t_proj = prof["proj"]
     proj_per_launch = proj_flops / (n_proj / args.steps)
     proj_achieved = proj_per_launch / (t_proj / n_proj * 1e-3) / 1e12
     out = {
@@ -340,25 +365,13 @@ def stack_main(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} stack steps")
-    B.profile_start()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    B.profile_stop()
-    ms = e0.elapsed_time(e1) / args.steps
-    prof = B.profile_read()
     kflops = stack_flops(wl, T, drawn)
     total = sum(kflops.values())
-    kernels = {n_: {"launches_per_step": c_ / args.steps, "ms_per_step": t_ / args.steps, "avg_us": t_ / c_ * 1e3}
-               for n_, (c_, t_) in prof.items() if c_}
+    ms, _, kernels, dom, (n_l, t_l) = timed_steps(
+        B, torch, step, args.steps,
+        lambda k_: max((n_ for n_ in k_ if n_ in kflops), key=lambda n_: k_[n_]["ms_per_step"]))
     log(f"[bench] {ms:.3f} ms/stack step; kernels " + json.dumps(kernels))
-    dom = max((n_ for n_ in kernels if n_ in kflops), key=lambda n_: kernels[n_]["ms_per_step"])
-    n_l, t_l = prof[dom]
     per_launch = kflops[dom] / (n_l / args.steps)
     achieved = per_launch / (t_l / n_l * 1e-3) / 1e12
     from sequence_chunked_exact_amd.profile_summary import read_traffic
@@ -456,23 +469,10 @@ def head_main(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     log(f"[bench] timing {args.steps} head steps")
-    B.profile_start()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    B.profile_stop()
-    ms = e0.elapsed_time(e1) / args.steps
-    prof = B.profile_read()
+    ms, _, kernels, _, (n_h, t_h) = timed_steps(B, torch, step, args.steps, lambda k_: "head")
     flops = 3 * 2 * Bt * T * V * dm                     # logits, dH, dW
-    kernels = {n_: {"launches_per_step": c_ / args.steps, "ms_per_step": t_ / args.steps, "avg_us": t_ / c_ * 1e3}
-               for n_, (c_, t_) in prof.items() if c_}
     log(f"[bench] {ms:.3f} ms/head step; kernels " + json.dumps(kernels))
-    n_h, t_h = prof["head"]
     per_launch = flops / (n_h / args.steps)
     achieved = per_launch / (t_h / n_h * 1e-3) / 1e12
     hbytes = head_bytes(T, dm, V, wl.ps, wl.dw_group, Bt)
@@ -592,41 +592,27 @@ def main():
         selected = step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
-    B.profile_start()
+    sel = {}
+
+    def run():
+        sel["v"] = step()
+
+    # roofline for the kernel with the most GPU time; its algorithmic FLOPs are
+    # the products it carries (forward: S, PV = 4d per pair; dK/dV: S, dP, dV,
+    # dK = 8d per pair; dQ: the dQ product, 2d)
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        selected = step()
-        marks[i].record(stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
+    ms, per_step, kernels, dom, (n_launch, tot_ms) = timed_steps(
+        B, torch, run, args.steps, lambda k_: max(k_, key=lambda n_: k_[n_]["ms_per_step"]))
     wall = time.perf_counter() - t_wall
-    B.profile_stop()
-    ms = e0.elapsed_time(e1) / args.steps
-    per_step = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)]
-    prof = B.profile_read()
-    log(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms/step)")
+    selected = sel["v"]
+    log(f"[bench] {ms:.3f} ms/step (wall incl. the profiled steps {wall / (args.steps + 2) * 1e3:.3f} ms/step)")
+    log("[bench] kernels " + json.dumps(kernels))
 
     plan = flop_plan(wl, selected if sparse else None)
     total_flops = plan["fwd"] + plan["bwd"]
     tflops = total_flops / (ms * 1e-3) / 1e12
-    kernels = {}
-    for name, (n, tot) in prof.items():
-        if n:
-            kernels[name] = {"launches_per_step": n / args.steps, "ms_per_step": tot / args.steps,
-                             "avg_us": tot / n * 1e3}
-    log("[bench] kernels " + json.dumps(kernels))
-    # roofline for the kernel with the most GPU time; its algorithmic FLOPs are
-    # the products it carries (forward: S, PV = 4d per pair; dK/dV: S, dP, dV,
-    # dK = 8d per pair; dQ: the dQ product, 2d, the rest being recompute)
-    dom = max(kernels, key=lambda n_: kernels[n_]["ms_per_step"])
     dom_flops = {"fwd": plan["fwd"], "dkdv": plan["dkdv"], "dq": plan["bwd"] // 5}.get(dom)
-    n_launch, tot_ms = prof[dom]
     roof = {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": None, "traffic": None}
     if dom_flops is not None:

@@ -343,6 +343,10 @@ enum {
   CA_KERNEL_COUNT = 11
 };
 int chunk_attn_profile_start(void);
+/* Bit k of kernel_mask (default all) selects kernel id k for the events;
+ * every event adds a little GPU time between launches, so a benchmark that
+ * needs one kernel's durations brackets only that kernel. */
+int chunk_attn_profile_select(uint32_t kernel_mask);
 int chunk_attn_profile_stop(void);
 int chunk_attn_profile_read(int32_t kernel, int64_t* launches, double* total_ms);
 

@@ -97,6 +97,7 @@ def _load() -> ctypes.CDLL:
         "chunk_attn_last_error": (ctypes.c_char_p, []),
         "chunk_attn_profile_start": (ctypes.c_int, []),
         "chunk_attn_profile_stop": (ctypes.c_int, []),
+        "chunk_attn_profile_select": (ctypes.c_int, [ctypes.c_uint32]),
         "chunk_attn_profile_read": (ctypes.c_int, [I32, ctypes.POINTER(ctypes.c_int64),
                                                    ctypes.POINTER(ctypes.c_double)]),
     }
@@ -386,6 +387,12 @@ def lm_head_dpo_finish(row_loss, dh, dw, w, *, ref_logp, beta: float, seq_len: O
 def profile_start():
     """Bracket every later kernel launch with HIP events (see chunk_attn.h)."""
     _check(lib.chunk_attn_profile_start())
+
+
+def profile_select(kernels=None):
+    """Record events only for the named kernels (None: all) from the next profile_start()."""
+    mask = 0xFFFFFFFF if kernels is None else sum(1 << KERNELS[k] for k in kernels)
+    _check(lib.chunk_attn_profile_select(mask))
 
 
 def profile_stop():

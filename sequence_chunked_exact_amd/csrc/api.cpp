@@ -137,6 +137,7 @@ struct ProfRec {
 struct ProfState {
   std::mutex mu;
   bool on = false;
+  uint32_t mask = 0xFFFFFFFFu;  // kernel ids that get events (bit per id)
   std::vector<hipEvent_t> pool;
   size_t used = 0;
   std::vector<ProfRec> recs;
@@ -150,7 +151,9 @@ thread_local long t_pending = -1;
 hipEvent_t take_event(ProfState& s) {
   if (s.used == s.pool.size()) {
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    // timing only: no system-scope fence (a default event's fence, per launch,
+    // costs the step several percent)
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     s.pool.push_back(e);
   }
   return s.pool[s.used++];
@@ -161,7 +164,7 @@ void prof_begin(int kernel, hipStream_t st) {
   ProfState& s = prof();
   std::lock_guard<std::mutex> g(s.mu);
   t_pending = -1;
-  if (!s.on) return;
+  if (!s.on || !((s.mask >> kernel) & 1u)) return;
   hipEvent_t a = take_event(s);
   if (!a || hipEventRecord(a, st) != hipSuccess) return;
   s.recs.push_back({kernel, a, nullptr});
@@ -378,6 +381,13 @@ int chunk_attn_profile_start(void) {
   s.recs.clear();
   s.used = 0;
   s.on = true;
+  return CA_OK;
+}
+
+int chunk_attn_profile_select(uint32_t kernel_mask) {
+  ca::ProfState& s = ca::prof();
+  std::lock_guard<std::mutex> g(s.mu);
+  s.mask = kernel_mask;
   return CA_OK;
 }
 

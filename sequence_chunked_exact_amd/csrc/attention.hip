@@ -3,6 +3,9 @@
 // workspace room (bf16), the dK/dV pass also stores the chunk's dS^T in bf16
 // and the dQ pass streams it (dQ = dS K, one product per visible pair);
 // otherwise the dQ pass recomputes S, P and dP (three products per pair).
+// Tile sizes follow the grid: chunks too short to give every compute unit a
+// 128-row query tile run 64-row tiles, and the dK/dV pass mixes 128- and
+// 64-key tiles so that its last round is a short one (see bwd_impl).
 //
 // What is computed (StreamBP review, "What carries the argument": Property 3.1
 // and the partitioned attention of Eqs. (12)-(14)): chunk i's queries, at
