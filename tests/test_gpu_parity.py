@@ -150,6 +150,17 @@ def test_bf16_tile_and_tail_cases(T, C, Hq, Hkv, d, spike, scale):
     check_dense(custom("bf16_var", T, C, Hq, Hkv, d, "bf16", seed=T * 3 + C, scale=scale, spike=spike))
 
 
+def test_bf16_dkdv_launch_plan_with_six_kv_heads():
+    # Six kv heads: the 2048-key prefix of chunk 0 runs on half-size key tiles
+    # (192 workgroups), chunk 1 on full tiles, and chunk 2 (48 full tiles per
+    # head, 288 workgroups) on 42 full tiles per head followed by a launch of
+    # half-size tiles from key 5376 on: the split falls inside the chunk's own
+    # diagonal block and off any multiple of the chunk size. 12 query heads
+    # also put the forward and the dQ pass on 64-row tiles.
+    wl = custom("bf16_plan6", 6144, 2048, 12, 6, 128, "bf16", seed=61, spike=1)
+    check_dense(wl, heads=[0, 1, 10, 11])
+
+
 @pytest.mark.parametrize("T,C,Hq,Hkv,d,spike,scale", [
     (777, 100, 4, 2, 64, 0, 1.0),
     (1000, 96, 2, 2, 128, 1, 1 / math.sqrt(128)),
