@@ -537,7 +537,7 @@ template <typename T, int D, int NKT, int BQ, int NP>
 __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int BKV = NP * NKT * 16, NB = 3;
+  constexpr int BKV = NP * NKT * 16, NB = 3, NBQ = 4;
   constexpr int DK = D / 32, MD = D / 16, MQ = BQ / 16, KQ = BQ / 32;
   // Only the P/dV waves load Q/dO blocks (and only the dS/dK waves store dS):
   // vector loads and stores complete out of order with respect to each other
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   // whenever it waits for a load.
   constexpr int NL = NP * 64;  // loading threads
   static_assert(2 * BQ <= NL, "row statistics: one value per loading thread");
-  __shared__ __attribute__((aligned(16))) T Qs[NB][BQ * PadLay<T, D>::RS];
+  __shared__ __attribute__((aligned(16))) T Qs[NBQ][BQ * PadLay<T, D>::RS];
   __shared__ __attribute__((aligned(16))) T Ds[NB][BQ * PadLay<T, D>::RS];
   // per buffer: LSE*log2(e) of the block's rows in [0, BQ), delta in [BQ, 2BQ)
   __shared__ __attribute__((aligned(16))) float stat_s[NB][2 * BQ];
@@ -594,10 +594,10 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   };
   // (The +inf substitution waits until here so that the fetch never waits
   // on its own loads.)
-  auto publish = [&](int buf) {
-    qreg.store(Qs[buf], tid);
-    dreg.store(Ds[buf], tid);
-    if (tid < 2 * BQ) stat_s[buf][tid] = past ? kInf : stat;
+  auto publish = [&](int blk) {
+    qreg.store(Qs[blk % NBQ], tid);
+    dreg.store(Ds[blk % NB], tid);
+    if (tid < 2 * BQ) stat_s[blk % NB][tid] = past ? kInf : stat;
   };
 
   // K (P/dV waves, negated for a negative scale) or V (dS/dK waves) rows of
@@ -628,113 +628,160 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   wait_loads();
   __syncthreads();
 
-  // One code path for both roles (only the VALU step between the two
-  // products differs), so that the accumulator chain has a single home in
-  // registers. The P/dV waves take block it, the dS/dK waves block it - 1.
-  int qv = qt0;  // q tile of this wave's block
-  for (int it = 0; it <= iters; ++it) {
-    const bool more = it + 1 < iters;
-    if (more && pv_wave) fetch();
-    const int blk = pv_wave ? it : it - 1;
-    const int q0 = qv * BQ;
-    const int q_lo = p.start + q0, q_hi = p.start + min(q0 + BQ, p.len) - 1;
-    if (blk >= 0 && blk < iters) qv = next_qt(qv);
-    if (blk >= 0 && blk < iters && wk0 <= q_hi) {
-      const int buf = blk % NB;
-      const T* A = pv_wave ? Qs[buf] : Ds[buf];  // row-major operand of S or dP
-      const T* X = pv_wave ? Ds[buf] : Qs[buf];  // transposed operand of dV or dK
-      f32x4 s[MQ][NKT];
-#pragma unroll
-      for (int mq = 0; mq < MQ; ++mq)
-#pragma unroll
-        for (int nk = 0; nk < NKT; ++nk) s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < DK; ++kb)
-#pragma unroll
-        for (int mq = 0; mq < MQ; ++mq) {
-          const frag a = ld8s<PadLay<T, D>>(A, mq * 16 + n, kb * 32 + 8 * g);
-#pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) E::mma(s[mq][nk], a, kv[nk][kb]);
-        }
-      frag wf[KQ][NKT];  // P (P/dV) or dS (dS/dK) as A fragments
-      if (pv_wave) {
-#pragma unroll
-        for (int mq = 0; mq < MQ; ++mq) {
-          const f32x4 l4 = *(const f32x4*)&stat_s[buf][mq * 16 + 4 * g];
-#pragma unroll
-          for (int nk = 0; nk < NKT; ++nk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[mq][nk][i] = fexp2(__builtin_fmaf(s[mq][nk][i], c2, -l4[i]));
-        }
-        if (q_lo < wk0 + NKT * 16 - 1) {  // block crosses this pair's diagonal
+  // The two roles run their phases in different orders so that one's
+  // products overlap the other's vector work: in iteration it the P/dV wave
+  // computes S = Q K^T of block it (products), P (exponentials) and dV +=
+  // P^T dO (products); the dS/dK wave first adds dK += dS^T Q for block it - 2
+  // (products, dS kept in registers since the previous iteration), then dP =
+  // dO V^T for block it - 1 (products) and dS (vector work). Q blocks stay in
+  // LDS for four iterations (four buffers), dO blocks and row statistics for
+  // three. Each role has its own loop; both pass the same number of barriers.
+  if (pv_wave) {
+    int qv = qt0;
+    for (int it = 0; it <= iters; ++it) {
+      const bool more = it + 1 < iters;
+      if (more) fetch();
+      if (it < iters) {
+        const int q0 = qv * BQ;
+        const int q_lo = p.start + q0, q_hi = p.start + min(q0 + BQ, p.len) - 1;
+        qv = next_qt(qv);
+        if (wk0 <= q_hi) {
+          const T* A = Qs[it % NBQ];
+          const T* X = Ds[it % NB];
+          f32x4 s[MQ][NKT];
 #pragma unroll
           for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
+            for (int nk = 0; nk < NKT; ++nk) s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+            for (int mq = 0; mq < MQ; ++mq) {
+              const frag a = ld8s<PadLay<T, D>>(A, mq * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+              for (int nk = 0; nk < NKT; ++nk) E::mma(s[mq][nk], a, kv[nk][kb]);
+            }
+#pragma unroll
+          for (int mq = 0; mq < MQ; ++mq) {
+            const f32x4 l4 = *(const f32x4*)&stat_s[it % NB][mq * 16 + 4 * g];
+#pragma unroll
             for (int nk = 0; nk < NKT; ++nk)
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (wk0 + nk * 16 + n > q_lo + mq * 16 + 4 * g + i) s[mq][nk][i] = 0.f;
+              for (int i = 0; i < 4; ++i) s[mq][nk][i] = fexp2(__builtin_fmaf(s[mq][nk][i], c2, -l4[i]));
+          }
+          if (q_lo < wk0 + NKT * 16 - 1) {  // block crosses this pair's diagonal
+#pragma unroll
+            for (int mq = 0; mq < MQ; ++mq)
+#pragma unroll
+              for (int nk = 0; nk < NKT; ++nk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (wk0 + nk * 16 + n > q_lo + mq * 16 + 4 * g + i) s[mq][nk][i] = 0.f;
+          }
+          frag wf[KQ][NKT];  // P as A fragments of dV
+#pragma unroll
+          for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+            for (int nk = 0; nk < NKT; ++nk) {
+              wf[kq][nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
+              Ps[it & 1][pair][kq][nk][lane] = wf[kq][nk];
+            }
+#pragma unroll
+          for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+              const frag x = ldT8<PadLay<T, D>>(X, kq * 32, md * 16, lane);
+#pragma unroll
+              for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], wf[kq][nk], x);
+            }
         }
+      }
+      // Q buffer (it + 1) % 4 last held block it - 3, whose dK product ran in
+      // iteration it - 1; dO buffer (it + 1) % 3 held block it - 2, read by
+      // iteration it - 1 at the latest.
+      if (more) publish(it + 1);
+      __syncthreads();
+    }
+    __syncthreads();  // the dS/dK loop runs one iteration more
+  } else {
+    int qv = qt0;
+    bool have_prev = false;  // dS of block it - 2 is held in dsp
+    frag dsp[KQ][NKT];
+    for (int it = 0; it <= iters + 1; ++it) {
+      if (have_prev) {  // dK += dS^T Q for block it - 2
+        const T* X = Qs[(it - 2) % NBQ];
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) {
-            wf[kq][nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
-            Ps[blk & 1][pair][kq][nk][lane] = wf[kq][nk];
+          for (int md = 0; md < MD; ++md) {
+            const frag x = ldT8<PadLay<T, D>>(X, kq * 32, md * 16, lane);
+#pragma unroll
+            for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], dsp[kq][nk], x);
           }
-      } else {
+      }
+      have_prev = false;
+      const int blk = it - 1;
+      if (blk >= 0 && blk < iters) {
+        const int q0 = qv * BQ;
+        const int q_hi = p.start + min(q0 + BQ, p.len) - 1;
+        qv = next_qt(qv);
+        if (wk0 <= q_hi) {
+          const T* A = Ds[blk % NB];
+          f32x4 s[MQ][NKT];
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) {
-          const f32x4 d4lo = *(const f32x4*)&stat_s[buf][BQ + kq * 32 + 4 * g];
-          const f32x4 d4hi = *(const f32x4*)&stat_s[buf][BQ + kq * 32 + 16 + 4 * g];
+          for (int mq = 0; mq < MQ; ++mq)
 #pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) {
-            const frag pf = Ps[blk & 1][pair][kq][nk][lane];
-            f32x4 lo, hi;
+            for (int nk = 0; nk < NKT; ++nk) s[mq][nk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              lo[i] = (float)pf[i] * (s[2 * kq][nk][i] - d4lo[i]);
-              hi[i] = (float)pf[4 + i] * (s[2 * kq + 1][nk][i] - d4hi[i]);
+          for (int kb = 0; kb < DK; ++kb)
+#pragma unroll
+            for (int mq = 0; mq < MQ; ++mq) {
+              const frag a = ld8s<PadLay<T, D>>(A, mq * 16 + n, kb * 32 + 8 * g);
+#pragma unroll
+              for (int nk = 0; nk < NKT; ++nk) E::mma(s[mq][nk], a, kv[nk][kb]);
             }
-            wf[kq][nk] = pack44<T>(lo, hi);
-          }
-        }
-        // Hand dS to the dQ pass: this lane's slots are keys wk0 + 16 nk + n
-        // against query rows q0 + 32 kq + {4g..4g+3, 16+4g..16+4g+3}; they are
-        // stored key-major (dS^T) as they are, so column 32 kq + 8 g + s of a
-        // key's row holds query row 32 kq + tile_row(8 g + s) and each lane
-        // writes one 16-byte run.
-        if constexpr (sizeof(T) == 2) {
-          static_assert(kDsKeyPad % BKV == 0 && kDsCols % BQ == 0, "dS^T block shape");
-          if (p.ds) {
-            const int nqb = qt_end - qt0;
-            const int hb = hk * G + blk / nqb;
-            bf16* dsb = (bf16*)p.ds +
-                        ((size_t)((b * p.hq + hb) * p.ds_nqb + q0 / kDsCols) * p.ds_keys + wk0) * kDsCols +
-                        q0 % kDsCols;
 #pragma unroll
-            for (int kq = 0; kq < KQ; ++kq)
+          for (int kq = 0; kq < KQ; ++kq) {
+            const f32x4 d4lo = *(const f32x4*)&stat_s[blk % NB][BQ + kq * 32 + 4 * g];
+            const f32x4 d4hi = *(const f32x4*)&stat_s[blk % NB][BQ + kq * 32 + 16 + 4 * g];
 #pragma unroll
-              for (int nk = 0; nk < NKT; ++nk) {
-                *(bf16x8*)(dsb + (size_t)(nk * 16 + n) * kDsCols + kq * 32 + 8 * g) =
-                    __builtin_bit_cast(bf16x8, wf[kq][nk]);
+            for (int nk = 0; nk < NKT; ++nk) {
+              const frag pf = Ps[blk & 1][pair][kq][nk][lane];
+              f32x4 lo, hi;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                lo[i] = (float)pf[i] * (s[2 * kq][nk][i] - d4lo[i]);
+                hi[i] = (float)pf[4 + i] * (s[2 * kq + 1][nk][i] - d4hi[i]);
               }
+              dsp[kq][nk] = pack44<T>(lo, hi);
+            }
+          }
+          have_prev = true;
+          // Hand dS to the dQ pass: this lane's slots are keys wk0 + 16 nk + n
+          // against query rows q0 + 32 kq + {4g..4g+3, 16+4g..16+4g+3}; they
+          // are stored key-major (dS^T) as they are, so column 32 kq + 8 g + s
+          // of a key's row holds query row 32 kq + tile_row(8 g + s) and each
+          // lane writes one 16-byte run.
+          if constexpr (sizeof(T) == 2) {
+            static_assert(kDsKeyPad % BKV == 0 && kDsCols % BQ == 0, "dS^T block shape");
+            if (p.ds) {
+              const int nqb = qt_end - qt0;
+              const int hb = hk * G + blk / nqb;
+              bf16* dsb = (bf16*)p.ds +
+                          ((size_t)((b * p.hq + hb) * p.ds_nqb + q0 / kDsCols) * p.ds_keys + wk0) * kDsCols +
+                          q0 % kDsCols;
+#pragma unroll
+              for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+                for (int nk = 0; nk < NKT; ++nk)
+                  *(bf16x8*)(dsb + (size_t)(nk * 16 + n) * kDsCols + kq * 32 + 8 * g) =
+                      __builtin_bit_cast(bf16x8, dsp[kq][nk]);
+            }
           }
         }
       }
-#pragma unroll
-      for (int kq = 0; kq < KQ; ++kq)
-#pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          const frag x = ldT8<PadLay<T, D>>(X, kq * 32, md * 16, lane);
-#pragma unroll
-          for (int nk = 0; nk < NKT; ++nk) E::mma(acc[nk][md], wf[kq][nk], x);
-        }
+      __syncthreads();
     }
-    // Buffer (it + 1) % NB last served block it - 2, whose dS/dK pass ended
-    // before the previous barrier.
-    if (more && pv_wave) publish((it + 1) % NB);
-    __syncthreads();
   }
 
   // Read-modify-write of the fp32 accumulator, 16 keys at a time: all reads
