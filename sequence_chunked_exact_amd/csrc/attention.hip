@@ -525,14 +525,16 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
 // K fragments and dV sums: S = Q K^T, P = exp(S - LSE) (causally masked),
 // dV += P^T dO, and P goes to LDS as the packed fragments of that product.
 // Its partner, wave NP + w, holds the V fragments and dK sums and runs one
-// block behind: dP = dO V^T, dS = P (dP - delta) with that (rounded) P,
-// dK += dS^T Q. Each wave then does two of
-// the four products per block and fits in half the register file, so the two
-// waves of a pair share a SIMD and overlap each other's LDS reads and
-// exponentials with their products. Q and dO blocks go through three LDS
-// buffers (the P/dV waves read block it, the dS/dK waves block it-1, the
-// loads fill block it+1), read row-major as the A operand of S and dP and
-// through the transposing path as the B operand of dV and dK.
+// block behind: dP = dO V^T, dS = P (dP - delta) with that (rounded) P, and
+// dK += dS^T Q one iteration later still, at the start of the next
+// iteration. Each wave then does two of the four products per block and fits
+// in half the register file, so the two waves of a pair share a SIMD, and
+// their phase orders differ (products, exponentials, products against
+// products, products, dS) so that one's vector work runs under the other's
+// products. Q blocks go through four LDS buffers (block it for S, it - 2 for
+// dK, it + 1 being filled), dO blocks and row statistics through three; they
+// are read row-major as the A operand of S and dP and through the transposing
+// path as the B operand of dV and dK.
 template <typename T, int D, int NKT, int BQ, int NP>
 __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   using E = Elt<T>;
