@@ -150,14 +150,15 @@ def test_bf16_tile_and_tail_cases(T, C, Hq, Hkv, d, spike, scale):
     check_dense(custom("bf16_var", T, C, Hq, Hkv, d, "bf16", seed=T * 3 + C, scale=scale, spike=spike))
 
 
-def test_bf16_dkdv_launch_plan_with_six_kv_heads():
+@pytest.mark.parametrize("d", [128, 64])
+def test_bf16_dkdv_launch_plan_with_six_kv_heads(d):
     # Six kv heads: the 2048-key prefix of chunk 0 runs on half-size key tiles
     # (192 workgroups), chunk 1 on full tiles, and chunk 2 (48 full tiles per
     # head, 288 workgroups) on 42 full tiles per head followed by a launch of
     # half-size tiles from key 5376 on: the split falls inside the chunk's own
     # diagonal block and off any multiple of the chunk size. 12 query heads
     # also put the forward and the dQ pass on 64-row tiles.
-    wl = custom("bf16_plan6", 6144, 2048, 12, 6, 128, "bf16", seed=61, spike=1)
+    wl = custom("bf16_plan6", 6144, 2048, 12, 6, d, "bf16", seed=61 + d, spike=1)
     check_dense(wl, heads=[0, 1, 10, 11])
 
 
