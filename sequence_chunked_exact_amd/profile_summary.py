@@ -139,6 +139,54 @@ def summarize_main(args):
     return out
 
 
+STALL_A = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS",
+           "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE")
+STALL_B = ("SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_MISC", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES",
+           "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")
+
+
+def stalls_main(args):
+    """Per-kernel stall fractions from two counter passes (STALL_A, STALL_B):
+    wait and issue counters over SQ_WAVE_CYCLES, matrix-core busy over the
+    elapsed cycles of all SIMDs, co-issue over matrix-core busy."""
+    sums = {}
+    for tag, path in (("a", args.a), ("b", args.b)):
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"])
+            d = sums.setdefault(k, {})
+            key = (tag, r["Counter_Name"])
+            d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+    lines = [f"# rocprofv3 summary: stall counters, `{args.workload}` workload", "",
+             "Commands (run from the repository root):", "", "```"]
+    lines += [c.strip() for c in args.commands.split(";;") if c.strip()]
+    lines += ["```", "",
+              "Fractions of wave cycles (SQ_WAVE_CYCLES) for the wait and issue counters; matrix cores busy as",
+              "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8) / 1024; co-issue as",
+              "SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES.", "",
+              "| kernel | wait on dependency | wait on LDS | other waits | VALU issuing | LDS issuing | "
+              "matrix cores busy | co-issue with busy matrix cores |",
+              "|---|---|---|---|---|---|---|---|"]
+    for k in sorted(sums):
+        d = sums[k]
+        wc = d.get(("a", "SQ_WAVE_CYCLES"), 0.0)
+        busy = d.get(("b", "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0)
+        grbm = d.get(("b", "GRBM_GUI_ACTIVE"), 0.0)
+        if wc <= 0 or grbm <= 0:
+            continue
+
+        def f(x):
+            return f"{100.0 * x:.1f}%"
+        lines.append(f"| {k} | {f(d.get(('a', 'SQ_WAIT_INST_ANY'), 0.0) / wc)} | "
+                     f"{f(d.get(('a', 'SQ_WAIT_INST_LDS'), 0.0) / wc)} | {f(d.get(('a', 'SQ_WAIT_ANY'), 0.0) / wc)} | "
+                     f"{f(d.get(('a', 'SQ_ACTIVE_INST_VALU'), 0.0) / wc)} | "
+                     f"{f(d.get(('a', 'SQ_ACTIVE_INST_LDS'), 0.0) / wc)} | {f(busy / (grbm / N_XCD) / N_SIMD)} | "
+                     f"{f(d.get(('b', 'SQ_VALU_MFMA_COEXEC_CYCLES'), 0.0) / busy) if busy else '-'} |")
+    lines.append("")
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def read_traffic(path: str, kernel: str):
     """traffic_bytes_per_launch from a summary, or None if missing or stale (the
     kernel's sources have changed since the counters were taken)."""
@@ -158,6 +206,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     sub.add_parser("copy")
+    st = sub.add_parser("stalls")
+    for opt in ("--a", "--b", "--workload", "--out", "--commands"):
+        st.add_argument(opt, default=None)
     s = sub.add_parser("summarize")
     for opt in ("--stats", "--fetch", "--write", "--cal-fetch", "--cal-write", "--kernel", "--workload",
                 "--out", "--commands", "--mfma", "--match"):
@@ -165,6 +216,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "copy":
         copy_main()
+    elif args.cmd == "stalls":
+        stalls_main(args)
     else:
         summarize_main(args)
 
