@@ -36,6 +36,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_info():
+    """The host the CPU baseline runs on: CPU model (from /proc/cpuinfo), the
+    BLAS library numpy calls (threadpoolctl) and the threads it uses."""
+    import numpy  # noqa: F401  (threadpoolctl lists only loaded libraries)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            blas = f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')}, " \
+                   f"{i.get('architecture')} kernels)"
+            threads = int(i.get("num_threads", threads))
+    except Exception:
+        pass
+    return {"cores": threads, "cpu_model": model, "blas": blas}
+
+
+def with_host(baseline):
+    """Add the host description to a cpu_baseline record."""
+    h = host_info()
+    baseline.update({"cpu_model": h["cpu_model"], "blas": h["blas"]})
+    return baseline
+
+
 
 def timed_steps(B, torch, step, steps, pick_dominant, profile_steps=2):
     """Time `steps` calls of step() between two events on the current stream.
@@ -103,11 +137,7 @@ def cpu_baseline(wl, inp_raw, n_heads=8):
     import numpy as np
     from oracle import attention as A
     from sequence_chunked_exact_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = host_info()["cores"]
     G = wl.n_q_heads // wl.n_kv_heads
 
     def head(name, h):
@@ -142,11 +172,7 @@ def layer_cpu_baseline(wl, raw, rows=2048, n_heads=8):
     from oracle import attention as A
     from oracle import projection as P
     from sequence_chunked_exact_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = host_info()["cores"]
     f = {n: (W.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)) for n, a in raw.items()}
     Hq, Hkv, d, dm, T = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.d_model, wl.seq_len
     G = Hq // Hkv
@@ -267,7 +293,7 @@ def layer_main(args):
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = layer_cpu_baseline(wl, inp.raw)
+        out["cpu_baseline"] = with_host(layer_cpu_baseline(wl, inp.raw))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -302,11 +328,7 @@ def stack_cpu_baseline(wl, raw, sample_len=4096):
     import numpy as np
     from oracle import stack as S
     from sequence_chunked_exact_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = host_info()["cores"]
 
     def f64(a):
         return W.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
@@ -407,12 +429,12 @@ def stack_main(args):
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         rate, dt, threads = stack_cpu_baseline(wl, r)
-        out["cpu_baseline"] = {"value": Bt * T / (total / rate), "unit": "tokens/s", "cores": int(threads),
+        out["cpu_baseline"] = with_host({"value": Bt * T / (total / rate), "unit": "tokens/s", "cores": int(threads),
                                "kind": "oracle",
                                "sample": f"float64 stack oracle on the first 4096 positions with the last chunk "
                                          f"drawn ({dt:.1f} s, {rate / 1e9:.1f} GFLOP/s in this step's FLOP "
                                          f"accounting), extrapolated to the full step by FLOPs",
-                               "seconds": dt}
+                               "seconds": dt})
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -512,11 +534,7 @@ def head_main(args):
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         from oracle import lm_head as O
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            threads = len(os.sched_getaffinity(0))
+        threads = host_info()["cores"]
         hf = W.bf16_bits_to_f64(inp.raw["h"])
         wf = W.bf16_bits_to_f64(inp.raw["w"])
         n_part = 20
@@ -526,11 +544,11 @@ def head_main(args):
             O.sft_partition(hf, wf, lab_np, slice(s0, s0 + wl.ps), scale)
         dt = time.perf_counter() - t0
         rate = 3 * 2 * n_part * wl.ps * V * dm / dt
-        out["cpu_baseline"] = {"value": Bt * T / (flops / rate), "unit": "tokens/s", "cores": int(threads),
+        out["cpu_baseline"] = with_host({"value": Bt * T / (flops / rate), "unit": "tokens/s", "cores": int(threads),
                                "kind": "oracle",
                                "sample": f"float64 oracle on {n_part} partitions of {wl.ps} positions at the full "
                                          f"vocabulary ({dt:.1f} s, {rate / 1e9:.1f} GFLOP/s), extrapolated to all "
-                                         f"{T} positions by FLOPs", "seconds": dt}
+                                         f"{T} positions by FLOPs", "seconds": dt})
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -660,7 +678,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(wl, inp.raw)
+        out["cpu_baseline"] = with_host(cpu_baseline(wl, inp.raw))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

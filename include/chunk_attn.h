@@ -314,8 +314,12 @@ int lm_head_sft_sweep(const lm_head_desc* desc, int32_t seq_len, int32_t ps, int
  * lp_b = -(sum of entry b's row losses), margin = (lp_0 - ref_logp_chosen) -
  * (lp_1 - ref_logp_rejected), loss = -log sigmoid(beta * margin), and dh (rows
  * [0, seq_len) of both entries) and dw are multiplied by c = beta *
- * sigmoid(-beta * margin). Copies the row losses to the host (synchronizes the
- * stream). Writes *loss_out and *c_out. CA_ERR_SHAPE unless batch == 2. */
+ * sigmoid(-beta * margin). The multiplication covers the whole of dw and
+ * those dh rows, so they must hold this pair's sweep only: zero dw before the
+ * pair's sweep, and to accumulate over several pairs or microbatches, sweep
+ * each pair into a zeroed buffer, finish it, then add it to the accumulator.
+ * Copies the row losses to the host (synchronizes the stream). Writes
+ * *loss_out and *c_out. CA_ERR_SHAPE unless batch == 2. */
 int lm_head_dpo_finish(const lm_head_desc* desc, int32_t seq_len, const float* row_loss, float ref_logp_chosen,
                        float ref_logp_rejected, float beta, float* dh, float* dw, float* loss_out, float* c_out,
                        void* stream);

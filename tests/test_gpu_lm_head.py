@@ -221,3 +221,32 @@ def test_dpo_scalar_correction(offset):
             "dh": rel(dh.cpu().double().numpy(), dh_ref), "dw": rel(dw.cpu().double().numpy(), dw_ref)}
     print("dpo", offset, {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
     assert errs["loss"] <= 2e-3 and errs["c"] <= 2e-3 and errs["dh"] <= 2e-2 and errs["dw"] <= 2e-2
+
+
+def test_dpo_two_pairs_accumulated_by_the_documented_pattern():
+    """lm_head_dpo_finish scales all of dw, so the header asks each pair to be swept
+    into a zeroed buffer, finished, then added to the accumulator. Two pairs done
+    that way give the sum of the two pairs' DPO weight gradients."""
+    Bn = None
+    total_ref = None
+    acc = None
+    beta = 0.3
+    for offset in (1.0, -2.0):   # two pairs on one head: different margins, so different c
+        wl = W.HeadWorkload("dpo", 2, 80, 128, 448, 32, 16, "bf16", seed=41)
+        inp = W.make_head_inputs(wl)
+        lab = inp.raw["labels"]
+        f = inp.f64
+        lp = -O.row_losses(f["h"], f["w"], lab).sum(axis=1)
+        ref = np.array([lp[0] - offset, lp[1] + offset])
+        Bn, torch, h, w, wt, labels, row_loss, dh, dw = _device_head(inp)
+        dw.zero_()
+        weight = torch.tensor([[1.0], [-1.0]], device=h.device).expand(2, lab.shape[1]).contiguous()
+        Bn.lm_head_sft(h, w, wt, labels, row_loss, dh, dw, loss_scale=1.0, ps=wl.ps, dw_group=2, row_weight=weight)
+        Bn.lm_head_dpo_finish(row_loss, dh, dw, w, ref_logp=ref, beta=beta)
+        acc = dw.clone() if acc is None else acc + dw
+        _, _, dw_ref, _ = O.dpo_dense(f["h"], f["w"], lab, ref, beta)
+        total_ref = dw_ref if total_ref is None else total_ref + dw_ref
+    torch.cuda.synchronize()
+    e = rel(acc.cpu().double().numpy(), total_ref)
+    print("dpo two pairs dw", f"{e:.2e}", flush=True)
+    assert e <= 2e-2

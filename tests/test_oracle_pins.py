@@ -30,7 +30,8 @@ def small(T=9, Hq=4, Hkv=2, d=5, B=1, seed=0):
 
 
 # ---------------------------------------------------------------- finite differences
-@pytest.mark.parametrize("Hq,Hkv,scale,block", [(2, 1, 0.7, 4), (2, 2, 1.0, 3), (3, 1, 0.5, 100)])
+@pytest.mark.parametrize("Hq,Hkv,scale,block", [(2, 1, 0.7, 4), (2, 2, 1.0, 3), (3, 1, 0.5, 100),
+                                                (2, 1, -0.6, 4)])
 def test_finite_differences(Hq, Hkv, scale, block):
     q, k, v, do = small(T=6, Hq=Hq, Hkv=Hkv, d=3, seed=11)
 
@@ -78,6 +79,7 @@ def torch_reference(q, k, v, do, scale):
     (33, 8, 2, 16, 2, 0.25, 8),
     (70, 3, 3, 7, 1, 1.0, 256),
     (1, 2, 1, 4, 1, 1.0, 4),
+    (40, 4, 1, 8, 1, -0.9, 16),       # negative scale: the softmax favours anti-aligned keys
 ])
 def test_torch_autograd_crosscheck(T, Hq, Hkv, d, B, scale, block):
     q, k, v, do = small(T=T, Hq=Hq, Hkv=Hkv, d=d, B=B, seed=T)
