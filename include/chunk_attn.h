@@ -114,6 +114,22 @@ int chunk_attn_bwd(const chunk_attn_desc* desc, const void* q, const void* k, co
                    float* dq, float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* chunk_attn_bwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Arguments, outputs and ordering as chunk_attn_bwd. The
+ * chunk's row statistics (8 bytes per row of batch * n_q_heads * chunk_len,
+ * rounded up) go to a static device array of 8 MiB that every device holds
+ * for the life of the process, so batch * n_q_heads * chunk_len may not
+ * exceed about one million rows (CA_ERR_WORKSPACE beyond). dQ is recomputed
+ * (the pass chunk_attn_bwd takes with its minimal workspace); results equal
+ * chunk_attn_bwd's with a CA_OP_BWD_MIN workspace. Calls no allocator. stream
+ * must belong to the current device (CA_ERR_SHAPE otherwise). Every call on a
+ * device shares that device's array: calls that overlap on one device (other
+ * streams, other threads) race and give wrong results. */
+int chunk_attn_bwd_noalloc(const chunk_attn_desc* desc, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout, float grad_scale,
+                           float* dq, float* dk_acc, float* dv_acc, void* stream);
+
 /* acc[b][h][r][:] += scale * src[b][h][r][:] for r < prefix_len (float32,
  * device pointers). This is the relay of an accumulated cache gradient,
  * m_i.grad <- (k/t) * m'_i.grad in SpaCO (SeCO/SpaCO review, Referee Report

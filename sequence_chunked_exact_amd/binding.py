@@ -73,6 +73,7 @@ def _load() -> ctypes.CDLL:
         "chunk_attn_workspace_size": (SZ, [D, I32]),
         "chunk_attn_fwd": (ctypes.c_int, [D, P, P, P, P, P, P, SZ, P]),
         "chunk_attn_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, F, P, P, P, P, SZ, P]),
+        "chunk_attn_bwd_noalloc": (ctypes.c_int, [D, P, P, P, P, P, P, F, P, P, P, P]),
         "prefix_grad_accumulate": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, I32, F, P]),
         "chunk_select": (ctypes.c_int, [I32, I32, U64, ctypes.POINTER(I32)]),
         "sparse_chunk_bwd": (ctypes.c_int, [D, I32, I32, U64, P, P, P, P, P, P, P, P, P,
@@ -183,6 +184,17 @@ def chunk_attn_bwd(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, *, chunk_start: in
     _check(lib.chunk_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                               _ptr(dout), float(grad_scale), _ptr(dq), _ptr(dk_acc), _ptr(dv_acc),
                               None if ws is None else _ptr(ws), nbytes, _stream(q)))
+
+
+def chunk_attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, *, chunk_start: int, chunk_len: int,
+                           q_row_offset: int = 0, softmax_scale: float = 1.0, grad_scale: float = 1.0):
+    """chunk_attn_bwd with the library's static scratch instead of a workspace (allocates nothing)."""
+    _contig(q, k, v, o, lse, dout, dq, dk_acc, dv_acc)
+    desc = make_desc(q, k, chunk_start=chunk_start, chunk_len=chunk_len, q_row_offset=q_row_offset,
+                     softmax_scale=softmax_scale)
+    _check(lib.chunk_attn_bwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      _ptr(dout), float(grad_scale), _ptr(dq), _ptr(dk_acc), _ptr(dv_acc),
+                                      _stream(q)))
 
 
 def prefix_grad_accumulate(acc, src, prefix_len: int, scale: float = 1.0):

@@ -273,6 +273,37 @@ int chunk_attn_bwd(const chunk_attn_desc* d, const void* q, const void* k, const
   return e == hipSuccess ? CA_OK : hip_fail(e, "chunk_attn_bwd launch");
 }
 
+int chunk_attn_bwd_noalloc(const chunk_attn_desc* d, const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, float grad_scale, float* dq, float* dk_acc,
+                           float* dv_acc, void* stream) {
+  int rc = check_desc(d, false);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q, k, v, o, lse, dout, dq, dk_acc, dv_acc}))) return rc;
+  if (!(grad_scale == grad_scale) || grad_scale > 3.0e38f || grad_scale < -3.0e38f)
+    return fail(CA_ERR_SHAPE, "grad_scale is not finite");
+  const size_t need = delta_bytes(d);
+  if (need > ca::kScratchBytes)
+    return fail(CA_ERR_WORKSPACE,
+                "chunk_attn_bwd_noalloc: batch * n_q_heads * chunk_len = %lld rows need %zu bytes of scratch; "
+                "the static scratch holds %zu",
+                (long long)d->batch * d->n_q_heads * d->chunk_len, need, ca::kScratchBytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "chunk_attn_bwd_noalloc: hipGetDevice");
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "chunk_attn_bwd_noalloc: hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(CA_ERR_SHAPE, "chunk_attn_bwd_noalloc: stream is on device %d, current device is %d", sdev, dev);
+  }
+  void* ws = nullptr;
+  if ((e = ca::scratch_address(&ws)) != hipSuccess) return hip_fail(e, "chunk_attn_bwd_noalloc: scratch address");
+  e = ca::launch_bwd(shape_of(d), q, k, v, o, lse, dout, grad_scale, dq, dk_acc, dv_acc, (float*)ws, need,
+                     (hipStream_t)stream);
+  return e == hipSuccess ? CA_OK : hip_fail(e, "chunk_attn_bwd_noalloc launch");
+}
+
 int prefix_grad_accumulate(float* acc, const float* src, int32_t batch, int32_t n_heads, int32_t acc_capacity,
                            int32_t src_capacity, int32_t head_dim, int32_t prefix_len, float scale,
                            void* stream) {

@@ -41,7 +41,34 @@
 //    score exceeds it by more than 2^8, which keeps every exponent <= 2^8.
 #include "device_common.h"
 
+#include <mutex>
+
+// Scratch of the allocation-free backward (chunk_attn_bwd_noalloc): the
+// chunk's row statistics go here instead of into a caller workspace. Every
+// device holds its own copy for the life of the process; host code reaches it
+// only through the address scratch_address() looks up, never by this name.
+static __device__ __align__(256) char scratch[ca::kScratchBytes];
+
 namespace ca {
+
+hipError_t scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 namespace {
 
 // ----------------------------------------------------------------------------

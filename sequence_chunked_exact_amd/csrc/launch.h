@@ -43,6 +43,12 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* 
                       const void* o, const float* lse, const void* dout, float grad_scale,
                       float* dq, float* dk, float* dv, float* ws, size_t ws_bytes, hipStream_t st);
 
+// Allocation-free backward: the row statistics live in a static device array
+// of kScratchBytes per device (attention.hip). scratch_address() returns the
+// current device's copy (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kScratchBytes = size_t(8) << 20;
+hipError_t scratch_address(void** ptr);
+
 // acc[b][h][r][:] += scale * src[b][h][r][:], r < rows.
 hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap,
                              int src_cap, int head_dim, int rows, float scale, hipStream_t st);

@@ -276,3 +276,16 @@ def test_header_compiles_standalone(lang, std, tmp_path):
     r = subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I",
                         os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_noalloc_backward_rejects_before_any_device_call():
+    d = desc(n_q_heads=64, n_kv_heads=8, q_capacity=32768, kv_capacity=32768, chunk_start=0, chunk_len=32768)
+    args = [FAKE] * 6 + [1.0] + [FAKE] * 3 + [None]
+    assert lib.chunk_attn_bwd_noalloc(ctypes.byref(d), *args) == -5      # scratch too small
+    assert b"static scratch" in lib.chunk_attn_last_error()
+    assert lib.chunk_attn_bwd_noalloc(None, *args) == -1
+    d2 = desc()
+    bad = [FAKE] * 6 + [1.0] + [MISALIGNED] + [FAKE] * 2 + [None]
+    assert lib.chunk_attn_bwd_noalloc(ctypes.byref(d2), *bad) == -4
+    nan = [FAKE] * 6 + [float("nan")] + [FAKE] * 3 + [None]
+    assert lib.chunk_attn_bwd_noalloc(ctypes.byref(d2), *nan) == -2
