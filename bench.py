@@ -567,6 +567,9 @@ def main():
                     help="measure SpaCO's step on a stack of attention layers (relayed cache gradients)")
     ap.add_argument("--seed", type=int, default=0, help="chunk draw seed for --stack")
     ap.add_argument("--head", action="store_true", help="measure the streamed LM head (SFT) step")
+    ap.add_argument("--ds-handover", action="store_true",
+                    help="give the backward the CA_OP_BWD_DS workspace (dS handed to the dQ pass; memory grows "
+                         "with the sequence) instead of the bounded one")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -598,8 +601,12 @@ def main():
     dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
     dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
     desc = B.make_desc(q, k, chunk_start=0, chunk_len=C, softmax_scale=wl.softmax_scale)
-    ws = torch.empty(max(B.chunk_attn_workspace_size(desc, B.CA_OP_SPARSE_BWD), 256), dtype=torch.uint8,
-                     device=dev)
+    # The backward's workspace: the bounded one (the chunk's row statistics; the
+    # dQ pass recomputes dS), or with --ds-handover room for dS^T of a chunk
+    # against the whole prefix (memory that grows with the sequence).
+    ws_op = B.CA_OP_BWD_DS if args.ds_handover else B.CA_OP_SPARSE_BWD
+    ws_bytes = B.chunk_attn_workspace_size(desc, ws_op)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     sparse = wl.sparse_t > 0
     t_sel = wl.sparse_t if sparse else wl.n_chunks      # t = k: every chunk, scale 1
     seed = wl.select_seed
@@ -672,7 +679,8 @@ def main():
                    "head_dim": wl.head_dim, "softmax_scale": wl.softmax_scale,
                    "key_spike": (f"rank {wl.spike_rank} amplitude {wl.spike_amp}" if wl.spike_rank else None),
                    "sparse_t": wl.sparse_t or None, "selected_chunks": selected if sparse else None,
-                   "causal_flops_per_step": total_flops},
+                   "causal_flops_per_step": total_flops, "workspace_bytes": ws_bytes,
+                   "dq_pass": "stored dS (CA_OP_BWD_DS)" if args.ds_handover else "recompute (CA_OP_SPARSE_BWD)"},
         "kernels": kernels,
         "roofline": roof,
     }

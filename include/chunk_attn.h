@@ -60,7 +60,7 @@ enum {
 
 enum { CA_F32 = 0, CA_BF16 = 1 };
 
-enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2, CA_OP_BWD_MIN = 3 };
+enum { CA_OP_FWD = 0, CA_OP_BWD = 1, CA_OP_SPARSE_BWD = 2, CA_OP_BWD_MIN = 3, CA_OP_BWD_DS = 4 };
 
 typedef struct {
   int32_t batch;         /* >= 1 */
@@ -81,13 +81,20 @@ typedef struct {
  * the whole-sequence one that sparse_chunk_bwd takes and chunk_len must be the
  * chunk size. Returns 0 for an invalid descriptor.
  *
- * The backward requires only CA_OP_BWD_MIN bytes (row statistics of the
- * chunk). CA_OP_BWD and CA_OP_SPARSE_BWD add, for bf16, room for the chunk's
- * dS^T in bf16 (n_q_heads * batch * chunk_len * kv_capacity * 2 bytes, rows and
- * keys rounded up to 128), sized so that one workspace serves every chunk of a
- * sweep: given that room, the dK/dV pass stores dS and the dQ pass streams it
- * (dQ = dS K) instead of recomputing S, P and dP. The results agree within
- * rounding; the larger workspace is faster. */
+ * CA_OP_BWD, CA_OP_SPARSE_BWD and CA_OP_BWD_MIN (the same size) give what the
+ * backward needs: the chunk's row statistics, 8 bytes per row of batch *
+ * n_q_heads * chunk_len (rounded up), independent of the sequence length and
+ * the capacities, as the method's per-chunk working set asks (StreamBP
+ * review, "What carries the argument"). The dQ pass then recomputes S, P and
+ * dP from Q, K, V, dO and the row statistics.
+ *
+ * CA_OP_BWD_DS (either descriptor) adds, for bf16, room for a chunk's dS^T in
+ * bf16: batch * n_q_heads * chunk_len * kv_capacity * 2 bytes, rows and keys
+ * rounded up to 128 (1.07 GB for 32 heads, 1024-row chunks and 16384 keys),
+ * so it grows with the sequence. Given that much workspace, chunk_attn_bwd and
+ * sparse_chunk_bwd hand dS from the dK/dV pass to the dQ pass (dQ = dS K)
+ * instead of recomputing it: faster, at memory that scales with the prefix.
+ * The results agree within rounding. */
 size_t chunk_attn_workspace_size(const chunk_attn_desc* desc, int32_t op);
 
 /* Forward of one chunk (the inference-mode pass that fills the caches in SeCO,
@@ -107,8 +114,8 @@ int chunk_attn_fwd(const chunk_attn_desc* desc, const void* q, const void* k, co
  * caller zeroes them before the first chunk of a sweep and chunks of one sweep
  * must be issued in stream order. grad_scale is SpaCO's k/t for a sparse sweep
  * and 1 otherwise. Workspace: at least chunk_attn_workspace_size(desc,
- * CA_OP_BWD_MIN) bytes; chunk_attn_workspace_size(desc, CA_OP_BWD) selects the
- * faster dQ pass for bf16. */
+ * CA_OP_BWD) bytes; chunk_attn_workspace_size(desc, CA_OP_BWD_DS) bytes select
+ * the dS hand-over for bf16. */
 int chunk_attn_bwd(const chunk_attn_desc* desc, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, const void* dout, float grad_scale,
                    float* dq, float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes,
@@ -122,7 +129,7 @@ int chunk_attn_bwd(const chunk_attn_desc* desc, const void* q, const void* k, co
  * for the life of the process, so batch * n_q_heads * chunk_len may not
  * exceed about one million rows (CA_ERR_WORKSPACE beyond). dQ is recomputed
  * (the pass chunk_attn_bwd takes with its minimal workspace); results equal
- * chunk_attn_bwd's with a CA_OP_BWD_MIN workspace. Calls no allocator. stream
+ * chunk_attn_bwd's with a CA_OP_BWD workspace. Calls no allocator. stream
  * must belong to the current device (CA_ERR_SHAPE otherwise). Every call on a
  * device shares that device's array: calls that overlap on one device (other
  * streams, other threads) race and give wrong results. */
@@ -156,12 +163,38 @@ int chunk_select(int32_t k, int32_t t, uint64_t seed, int32_t* out_sorted);
  * the exact chunked backward (SeCO). q, o, dout, dq, lse are whole-sequence
  * tensors (q_capacity >= seq_len) and o, lse come from forwards of all
  * chunks; desc->chunk_start and q_row_offset are ignored. The selected indices
- * go to the host array selected_out[t]. Workspace:
- * chunk_attn_workspace_size(desc, CA_OP_SPARSE_BWD). */
+ * go to the host array selected_out[t]. Workspace: at least
+ * chunk_attn_workspace_size(desc, CA_OP_SPARSE_BWD) bytes (CA_OP_BWD_DS for the
+ * dS hand-over). */
 int sparse_chunk_bwd(const chunk_attn_desc* desc, int32_t seq_len, int32_t t, uint64_t seed,
                      const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
                      int32_t* selected_out, void* ws, size_t ws_bytes, void* stream);
+
+/* The chunk schedule of a whole sequence of seq_len positions in chunks of
+ * desc->chunk_len (chunk i starts at s_i = i * chunk_len and holds
+ * min(chunk_len, seq_len - s_i) positions; the last may be short), computed
+ * here rather than by the caller. desc is the whole-sequence descriptor:
+ * q, o, dout, dq, lse hold every position (q_capacity >= seq_len) and k, v,
+ * dk_acc, dv_acc every key (kv_capacity >= seq_len); chunk_start and
+ * q_row_offset are ignored. SeCO runs the inference-mode pass over the chunks
+ * in order, then backpropagates them one at a time from the last (SeCO/SpaCO
+ * review, Referee Report summary).
+ *
+ * chunked_fwd_sweep: chunk_attn_fwd of every chunk, ascending; writes o and
+ * lse rows [0, seq_len). */
+int chunked_fwd_sweep(const chunk_attn_desc* desc, int32_t seq_len, const void* q, const void* k,
+                      const void* v, void* o, float* lse, void* stream);
+
+/* chunked_bwd_sweep: chunk_attn_bwd of every chunk, descending, with
+ * grad_scale. dq rows [0, seq_len) are OVERWRITTEN; dk_acc and dv_acc rows
+ * [0, seq_len) are INCREMENTED by the full gradient (zero them first for the
+ * gradient alone). Workspace as for sparse_chunk_bwd: at least
+ * chunk_attn_workspace_size(desc, CA_OP_SPARSE_BWD) bytes, CA_OP_BWD_DS for the
+ * dS hand-over. Errors as for sparse_chunk_bwd. */
+int chunked_bwd_sweep(const chunk_attn_desc* desc, int32_t seq_len, const void* q, const void* k,
+                      const void* v, const void* o, const float* lse, const void* dout, float grad_scale,
+                      float* dq, float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes, void* stream);
 
 /* The projections on either side of the attention of chunk i, which complete
  * one attention layer's chunked backward. The layer input H_in is
@@ -240,7 +273,7 @@ typedef struct {
 /* Workspace bytes for spaco_stack_forward / spaco_stack_backward (chunk-local
  * activations of every layer, the chunk's gradients, the attention and
  * projection workspaces; the attention part is chunk_attn_workspace_size(desc,
- * CA_OP_BWD), so a bf16 stack streams dS in its dQ passes). 0 for invalid
+ * CA_OP_BWD), so the stack's dQ passes recompute dS). 0 for invalid
  * arguments. */
 size_t spaco_stack_workspace_size(const chunk_attn_desc* desc, int32_t n_layers);
 

@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libchunk_attn.so")
 
 CA_F32, CA_BF16 = 0, 1
-CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD, CA_OP_BWD_MIN = 0, 1, 2, 3
+CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD, CA_OP_BWD_MIN, CA_OP_BWD_DS = 0, 1, 2, 3, 4
 KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7, "residual": 8, "head": 9, "head_aux": 10}
 ERRORS = {0: "CA_OK", -1: "CA_ERR_NULL", -2: "CA_ERR_SHAPE", -3: "CA_ERR_DTYPE", -4: "CA_ERR_ALIGN",
           -5: "CA_ERR_WORKSPACE", -6: "CA_ERR_UNSUPPORTED", -7: "CA_ERR_HIP"}
@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
         "chunk_attn_fwd": (ctypes.c_int, [D, P, P, P, P, P, P, SZ, P]),
         "chunk_attn_bwd": (ctypes.c_int, [D, P, P, P, P, P, P, F, P, P, P, P, SZ, P]),
         "chunk_attn_bwd_noalloc": (ctypes.c_int, [D, P, P, P, P, P, P, F, P, P, P, P]),
+        "chunked_fwd_sweep": (ctypes.c_int, [D, I32, P, P, P, P, P, P]),
+        "chunked_bwd_sweep": (ctypes.c_int, [D, I32, P, P, P, P, P, P, F, P, P, P, P, SZ, P]),
         "prefix_grad_accumulate": (ctypes.c_int, [P, P, I32, I32, I32, I32, I32, I32, F, P]),
         "chunk_select": (ctypes.c_int, [I32, I32, U64, ctypes.POINTER(I32)]),
         "sparse_chunk_bwd": (ctypes.c_int, [D, I32, I32, U64, P, P, P, P, P, P, P, P, P,
@@ -175,12 +177,14 @@ def chunk_attn_fwd(q, k, v, o, lse, *, chunk_start: int, chunk_len: int, q_row_o
 
 def chunk_attn_bwd(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, *, chunk_start: int, chunk_len: int,
                    q_row_offset: int = 0, softmax_scale: float = 1.0, grad_scale: float = 1.0,
-                   workspace=None):
-    """Backward of one chunk: dq rows overwritten, dk_acc/dv_acc prefix rows incremented."""
+                   workspace=None, ds_handover: bool = False):
+    """Backward of one chunk: dq rows overwritten, dk_acc/dv_acc prefix rows incremented.
+    Without a workspace one is allocated: CA_OP_BWD (bounded, dQ recomputes dS), or
+    CA_OP_BWD_DS when ds_handover (dS handed to the dQ pass; memory grows with the prefix)."""
     _contig(q, k, v, o, lse, dout, dq, dk_acc, dv_acc)
     desc = make_desc(q, k, chunk_start=chunk_start, chunk_len=chunk_len, q_row_offset=q_row_offset,
                      softmax_scale=softmax_scale)
-    ws, nbytes = _workspace(desc, CA_OP_BWD, q, workspace)
+    ws, nbytes = _workspace(desc, CA_OP_BWD_DS if ds_handover else CA_OP_BWD, q, workspace)
     _check(lib.chunk_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                               _ptr(dout), float(grad_scale), _ptr(dq), _ptr(dk_acc), _ptr(dv_acc),
                               None if ws is None else _ptr(ws), nbytes, _stream(q)))
@@ -247,11 +251,11 @@ def chunk_select(k: int, t: int, seed: int) -> list:
 
 
 def sparse_chunk_bwd(q, k, v, o, lse, dout, dq, dk, dv, *, seq_len: int, chunk: int, t: int, seed: int,
-                     softmax_scale: float = 1.0, workspace=None) -> list:
+                     softmax_scale: float = 1.0, workspace=None, ds_handover: bool = False) -> list:
     """SpaCO backward over t of the k chunks (scaled by k/t); returns the selected chunks."""
     _contig(q, k, v, o, lse, dout, dq, dk, dv)
     desc = make_desc(q, k, chunk_start=0, chunk_len=chunk, softmax_scale=softmax_scale)
-    ws, nbytes = _workspace(desc, CA_OP_SPARSE_BWD, q, workspace)
+    ws, nbytes = _workspace(desc, CA_OP_BWD_DS if ds_handover else CA_OP_SPARSE_BWD, q, workspace)
     sel = (ctypes.c_int32 * t)()
     _check(lib.sparse_chunk_bwd(ctypes.byref(desc), int(seq_len), int(t),
                                 ctypes.c_uint64(seed & (2**64 - 1)), _ptr(q), _ptr(k), _ptr(v),
@@ -262,28 +266,33 @@ def sparse_chunk_bwd(q, k, v, o, lse, dout, dq, dk, dv, *, seq_len: int, chunk: 
 
 def chunked_forward(q, k, v, o, lse, *, chunk: int, seq_len: Optional[int] = None,
                     softmax_scale: float = 1.0, chunks: Optional[Sequence[int]] = None):
-    """SeCO's inference-mode pass: chunk_attn_fwd on every chunk in ascending order."""
+    """SeCO's inference-mode pass: every chunk's forward in ascending order
+    (chunked_fwd_sweep), or only the chunks listed in ``chunks``."""
     T = q.shape[2] if seq_len is None else seq_len
-    n = -(-T // chunk)
-    for i in (range(n) if chunks is None else chunks):
-        s = i * chunk
-        chunk_attn_fwd(q, k, v, o, lse, chunk_start=s, chunk_len=min(chunk, T - s), q_row_offset=s,
-                       softmax_scale=softmax_scale)
+    if chunks is not None:
+        for i in chunks:
+            s = i * chunk
+            chunk_attn_fwd(q, k, v, o, lse, chunk_start=s, chunk_len=min(chunk, T - s), q_row_offset=s,
+                           softmax_scale=softmax_scale)
+        return
+    _contig(q, k, v, o, lse)
+    desc = make_desc(q, k, chunk_start=0, chunk_len=chunk, softmax_scale=softmax_scale)
+    _check(lib.chunked_fwd_sweep(ctypes.byref(desc), int(T), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 _stream(q)))
 
 
 def chunked_backward(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, *, chunk: int,
-                     seq_len: Optional[int] = None, softmax_scale: float = 1.0, workspace=None):
-    """Exact chunked backward (SeCO): every chunk, descending, into zeroed accumulators."""
+                     seq_len: Optional[int] = None, softmax_scale: float = 1.0, grad_scale: float = 1.0,
+                     workspace=None, ds_handover: bool = False):
+    """Exact chunked backward (SeCO, chunked_bwd_sweep): every chunk, descending; dk_acc/dv_acc
+    are incremented (zero them first), dq rows overwritten."""
+    _contig(q, k, v, o, lse, dout, dq, dk_acc, dv_acc)
     T = q.shape[2] if seq_len is None else seq_len
-    n = -(-T // chunk)
-    if workspace is None:
-        desc = make_desc(q, k, chunk_start=0, chunk_len=chunk, softmax_scale=softmax_scale)
-        workspace, _ = _workspace(desc, CA_OP_BWD, q, None)
-    for i in reversed(range(n)):
-        s = i * chunk
-        chunk_attn_bwd(q, k, v, o, lse, dout, dq, dk_acc, dv_acc, chunk_start=s,
-                       chunk_len=min(chunk, T - s), q_row_offset=s, softmax_scale=softmax_scale,
-                       workspace=workspace)
+    desc = make_desc(q, k, chunk_start=0, chunk_len=chunk, softmax_scale=softmax_scale)
+    ws, nbytes = _workspace(desc, CA_OP_BWD_DS if ds_handover else CA_OP_SPARSE_BWD, q, workspace)
+    _check(lib.chunked_bwd_sweep(ctypes.byref(desc), int(T), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                 _ptr(dout), float(grad_scale), _ptr(dq), _ptr(dk_acc), _ptr(dv_acc),
+                                 None if ws is None else _ptr(ws), nbytes, _stream(q)))
 
 
 def _stack_layers(layers):

@@ -233,14 +233,15 @@ const char* chunk_attn_strerror(int code) {
 const char* chunk_attn_last_error(void) { return g_err; }
 
 size_t chunk_attn_workspace_size(const chunk_attn_desc* d, int32_t op) {
-  if (check_desc(d, op == CA_OP_SPARSE_BWD) != CA_OK) return 0;
+  if (check_desc(d, op == CA_OP_SPARSE_BWD || op == CA_OP_BWD_DS) != CA_OK) return 0;
   switch (op) {
     case CA_OP_FWD: return 0;
-    case CA_OP_BWD_MIN: return delta_bytes(d);
     case CA_OP_BWD:
     case CA_OP_SPARSE_BWD:
-      // room for the dS^T blocks of any chunk of up to chunk_len rows whose
-      // prefix fits kv_capacity (bf16)
+    case CA_OP_BWD_MIN: return delta_bytes(d);  // the chunk's row statistics only
+    case CA_OP_BWD_DS:
+      // plus room for the dS^T blocks of any chunk of up to chunk_len rows
+      // whose prefix fits kv_capacity (bf16)
       return delta_bytes(d) + (d->dtype == CA_BF16 ? round_up(ca::bwd_ds_bytes(d->batch, d->n_q_heads,
                                                                                 d->chunk_len, d->kv_capacity))
                                                    : 0);
@@ -406,6 +407,48 @@ int sparse_chunk_bwd(const chunk_attn_desc* d, int32_t seq_len, int32_t t, uint6
   return CA_OK;
 }
 
+int chunked_fwd_sweep(const chunk_attn_desc* d, int32_t seq_len, const void* q, const void* k, const void* v,
+                      void* o, float* lse, void* stream) {
+  int rc = check_desc(d, true);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q, k, v, o, lse}))) return rc;
+  if (seq_len < 1 || seq_len > d->q_capacity || seq_len > d->kv_capacity)
+    return fail(CA_ERR_SHAPE, "seq_len %d must be in [1, min(q_capacity, kv_capacity)]", seq_len);
+  const int32_t C = d->chunk_len;
+  ca::Shape s = shape_of(d);
+  for (int64_t start = 0; start < seq_len; start += C) {  // ascending: the inference-mode pass
+    s.start = s.q_off = (int)start;
+    s.len = (int)std::min<int64_t>(C, seq_len - start);
+    hipError_t e = ca::launch_fwd(s, q, k, v, o, lse, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "chunked_fwd_sweep chunk launch");
+  }
+  return CA_OK;
+}
+
+int chunked_bwd_sweep(const chunk_attn_desc* d, int32_t seq_len, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, float grad_scale, float* dq,
+                      float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(d, true);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q, k, v, o, lse, dout, dq, dk_acc, dv_acc}))) return rc;
+  if (seq_len < 1 || seq_len > d->q_capacity || seq_len > d->kv_capacity)
+    return fail(CA_ERR_SHAPE, "seq_len %d must be in [1, min(q_capacity, kv_capacity)]", seq_len);
+  if (!(grad_scale == grad_scale) || grad_scale > 3.0e38f || grad_scale < -3.0e38f)
+    return fail(CA_ERR_SHAPE, "grad_scale is not finite");
+  if ((rc = check_ws(ws, ws_bytes, delta_bytes(d)))) return rc;
+  const int32_t C = d->chunk_len;
+  const int32_t n = (int32_t)(((int64_t)seq_len + C - 1) / C);
+  ca::Shape s = shape_of(d);
+  for (int32_t i = n - 1; i >= 0; --i) {  // descending, as SeCO's backward
+    s.start = s.q_off = i * C;
+    s.len = std::min(C, seq_len - i * C);
+    hipError_t e = ca::launch_bwd(s, q, k, v, o, lse, dout, grad_scale, dq, dk_acc, dv_acc, (float*)ws, ws_bytes,
+                                  (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "chunked_bwd_sweep chunk launch");
+  }
+  return CA_OK;
+}
+
 int chunk_attn_profile_start(void) {
   ca::ProfState& s = ca::prof();
   std::lock_guard<std::mutex> g(s.mu);
@@ -486,8 +529,8 @@ StackWs stack_ws(const chunk_attn_desc* d, int32_t L) {
   w.dh_b = at;
   at += round_up(B * C * dm * 4);
   w.attn_ws = at;
-  // the attention backward's row statistics and, for bf16, its dS^T blocks
-  w.attn_bytes = std::max(delta_bytes(d), chunk_attn_workspace_size(d, CA_OP_BWD));
+  // the attention backward's row statistics (its dQ passes recompute dS)
+  w.attn_bytes = delta_bytes(d);
   at += w.attn_bytes;
   w.proj_ws = at;
   ca::ProjShape ps = proj_shape(d, (int32_t)dm, d->chunk_len, 0);

@@ -122,6 +122,24 @@ static void accumulate_and_sparse_errors(void) {
 #undef SPARSE
 }
 
+static void sweep_errors(void) {
+  chunk_attn_desc d = base();
+  d.chunk_start = 0;
+  d.chunk_len = 128;
+  d.q_capacity = 1024;
+  float* F = (float*)FAKE;
+  EXPECT(chunked_fwd_sweep(NULL, 1024, FAKE, FAKE, FAKE, FAKE, F, NULL) == CA_ERR_NULL);
+  EXPECT(chunked_fwd_sweep(&d, 0, FAKE, FAKE, FAKE, FAKE, F, NULL) == CA_ERR_SHAPE);
+  EXPECT(chunked_fwd_sweep(&d, 1025, FAKE, FAKE, FAKE, FAKE, F, NULL) == CA_ERR_SHAPE);
+  EXPECT(chunked_fwd_sweep(&d, 1024, FAKE, MIS, FAKE, FAKE, F, NULL) == CA_ERR_ALIGN);
+#define BS(seq, gs, wsp, wsb) chunked_bwd_sweep(&d, seq, FAKE, FAKE, FAKE, FAKE, F, FAKE, gs, F, F, F, wsp, wsb, NULL)
+  EXPECT(BS(2048, 1.0f, FAKE, 1 << 20) == CA_ERR_SHAPE);
+  EXPECT(BS(1024, INFINITY, FAKE, 1 << 20) == CA_ERR_SHAPE);
+  EXPECT(BS(1024, 1.0f, NULL, 0) == CA_ERR_WORKSPACE);
+  EXPECT(BS(1024, 1.0f, FAKE, 16) == CA_ERR_WORKSPACE);
+#undef BS
+}
+
 static void selector(void) {
   static const int32_t ks[] = {1, 2, 3, 4, 5, 16, 17, 64, 129};
   static const uint64_t seeds[] = {0ull, 1ull, 12345ull, 9223372036854775815ull, 18446744073709551615ull};
@@ -241,6 +259,7 @@ int main(void) {
   descriptor_errors();
   pointer_and_workspace_errors();
   accumulate_and_sparse_errors();
+  sweep_errors();
   selector();
   projection_stack_head_errors();
   names_and_profiling();

@@ -118,19 +118,34 @@ def test_workspace_errors():
 
 
 def test_workspace_sizes_cover_the_ds_blocks():
-    # bf16: the full size adds the dS^T blocks of a chunk_len-row chunk against
-    # a kv_capacity prefix (rows and keys rounded up to 128, 2 bytes each), so
-    # one workspace serves every chunk of a sweep; float32 needs no more.
+    # bf16: CA_OP_BWD_DS adds the dS^T blocks of a chunk_len-row chunk against a
+    # kv_capacity prefix (rows and keys rounded up to 128, 2 bytes each), so one
+    # workspace serves every chunk of a sweep; float32 needs no more.
     for kw, rows, keys in ((dict(), 256, 1024), (dict(chunk_len=200, kv_capacity=1000), 256, 1024),
                            (dict(chunk_len=129, kv_capacity=130, q_capacity=129, chunk_start=0), 256, 256)):
         d = desc(**kw)
-        lo = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD_MIN)
-        full = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD)
+        lo = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD)
+        full = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD_DS)
         assert full - lo == d.batch * d.n_q_heads * rows * keys * 2
-        assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_SPARSE_BWD) == full
+        assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_SPARSE_BWD) == lo
+        assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD_MIN) == lo
         f32 = desc(dtype=b.CA_F32, **kw)
-        assert (lib.chunk_attn_workspace_size(ctypes.byref(f32), b.CA_OP_BWD)
-                == lib.chunk_attn_workspace_size(ctypes.byref(f32), b.CA_OP_BWD_MIN))
+        assert (lib.chunk_attn_workspace_size(ctypes.byref(f32), b.CA_OP_BWD_DS)
+                == lib.chunk_attn_workspace_size(ctypes.byref(f32), b.CA_OP_BWD))
+
+
+def test_backward_workspace_is_bounded_by_the_chunk():
+    # The backward's workspace (CA_OP_BWD, CA_OP_SPARSE_BWD) depends only on the
+    # chunk's rows (8 bytes per row of batch * Hq * C, rounded up), not on the
+    # sequence length or the capacities. 32B layer (Hq 64, C 2048): 1 MiB at
+    # T = 32768 and at T = 131072.
+    sizes = set()
+    for T in (32768, 131072):
+        d = desc(n_q_heads=64, n_kv_heads=8, q_capacity=T, kv_capacity=T, chunk_start=0, chunk_len=2048)
+        for op in (b.CA_OP_BWD, b.CA_OP_SPARSE_BWD):
+            sizes.add(lib.chunk_attn_workspace_size(ctypes.byref(d), op))
+    assert sizes == {2 * 64 * 2048 * 4}
+    assert max(sizes) <= 256 << 20
 
 
 def test_accumulate_errors():
@@ -289,3 +304,23 @@ def test_noalloc_backward_rejects_before_any_device_call():
     assert lib.chunk_attn_bwd_noalloc(ctypes.byref(d2), *bad) == -4
     nan = [FAKE] * 6 + [float("nan")] + [FAKE] * 3 + [None]
     assert lib.chunk_attn_bwd_noalloc(ctypes.byref(d2), *nan) == -2
+
+
+def test_sweep_errors():
+    d = desc(chunk_start=0, chunk_len=128, q_capacity=1024, kv_capacity=1024)
+    fs, bs = lib.chunked_fwd_sweep, lib.chunked_bwd_sweep
+    assert fs(None, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert fs(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert fs(ctypes.byref(d), 1025, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2       # past the capacities
+    assert fs(ctypes.byref(d), 1024, FAKE, MISALIGNED, FAKE, FAKE, FAKE, None) == -4
+    assert fs(ctypes.byref(desc(head_dim=80)), 1024, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -6
+
+    def bwd_(seq_len=1024, gs=1.0, ws=FAKE, ws_bytes=1 << 20, dq=FAKE):
+        return bs(ctypes.byref(d), seq_len, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, gs, dq, FAKE, FAKE, ws, ws_bytes,
+                  None)
+
+    assert bwd_(seq_len=2048) == -2
+    assert bwd_(gs=float("inf")) == -2
+    assert bwd_(ws=None, ws_bytes=0) == -5
+    assert bwd_(ws_bytes=16) == -5
+    assert bwd_(dq=None) == -1

@@ -52,11 +52,11 @@ def to_dev(inp):
     return {n: W.to_torch(inp.raw[n], DEV) for n in ("q", "k", "v", "do")}
 
 
-def run_chunked(wl, inp, T, scale, sparse=None, min_ws=False):
+def run_chunked(wl, inp, T, scale, sparse=None, ds=False):
     """Forward over all chunks, then the backward (dense chunked or sparse).
 
-    min_ws: give the dense backward only the workspace it requires, so the dQ
-    pass recomputes dS instead of reading the dS^T blocks (bf16)."""
+    ds: give the backward the CA_OP_BWD_DS workspace, so (bf16) the dK/dV pass
+    hands dS^T to the dQ pass instead of the dQ pass recomputing it."""
     B = binding()
     t = to_dev(inp)
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
@@ -68,17 +68,12 @@ def run_chunked(wl, inp, T, scale, sparse=None, min_ws=False):
     dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
     sel = None
     if sparse is None:
-        ws = None
-        if min_ws:
-            desc = B.make_desc(q, k, chunk_start=0, chunk_len=wl.chunk, softmax_scale=scale)
-            ws = torch.empty(max(B.chunk_attn_workspace_size(desc, B.CA_OP_BWD_MIN), 256), dtype=torch.uint8,
-                             device=DEV)
         B.chunked_backward(q, k, v, o, lse, do, dq, dk, dv, chunk=wl.chunk, seq_len=T, softmax_scale=scale,
-                           workspace=ws)
+                           ds_handover=ds)
     else:
         t_, seed = sparse
         sel = B.sparse_chunk_bwd(q, k, v, o, lse, do, dq, dk, dv, seq_len=T, chunk=wl.chunk, t=t_,
-                                 seed=seed, softmax_scale=scale)
+                                 seed=seed, softmax_scale=scale, ds_handover=ds)
     torch.cuda.synchronize()
     out = {"o": o.float().cpu().double().numpy(), "lse": lse.cpu().double().numpy(),
            "dq": dq.cpu().double().numpy(), "dk": dk.cpu().double().numpy(),
@@ -91,13 +86,13 @@ def custom(name, T, C, Hq, Hkv, d, dtype, seed, scale=1.0, spike=0):
                       spike_rank=4 if spike else 0, spike_amp=3.0 if spike else 0.0)
 
 
-def check_dense(wl, heads=None, T=None, scale=None, min_ws=False):
+def check_dense(wl, heads=None, T=None, scale=None, ds=False):
     T = wl.seq_len if T is None else T
     scale = wl.softmax_scale if scale is None else scale
     inp = W.make_inputs(wl, seq_len=T)
     note(f"[case] {wl.name} T={T} C={wl.chunk} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} d={wl.head_dim} "
-         f"{wl.dtype} scale={scale:.4g} heads={heads} min_ws={min_ws}")
-    got, _ = run_chunked(wl, inp, T, scale, min_ws=min_ws)
+         f"{wl.dtype} scale={scale:.4g} heads={heads} ds_handover={ds}")
+    got, _ = run_chunked(wl, inp, T, scale, ds=ds)
     f = inp.f64
     ro, rlse = A.forward(f["q"], f["k"], f["v"], scale, heads=heads)
     rdq, rdk, rdv = A.backward(f["q"], f["k"], f["v"], f["do"], scale, heads=heads)
@@ -174,11 +169,18 @@ def test_bf16_dkdv_launch_plan_with_six_kv_heads(d):
     (2048, 1024, 8, 2, 128, 1, 1.0),
     (700, 256, 4, 2, 128, 1, -1.0),     # negative scale
 ])
-def test_bf16_minimal_workspace_recomputes_ds(T, C, Hq, Hkv, d, spike, scale):
-    # The dQ pass that recomputes S, P and dP (taken when the workspace has no
-    # room for dS^T) against the oracle.
-    check_dense(custom("bf16_minws", T, C, Hq, Hkv, d, "bf16", seed=T + 5 * C, scale=scale, spike=spike),
-                min_ws=True)
+def test_bf16_ds_handover(T, C, Hq, Hkv, d, spike, scale):
+    # The dS hand-over (CA_OP_BWD_DS workspace: the dK/dV pass stores dS^T and
+    # the dQ pass streams it) against the oracle.
+    check_dense(custom("bf16_ds", T, C, Hq, Hkv, d, "bf16", seed=T + 5 * C, scale=scale, spike=spike),
+                ds=True)
+
+
+@pytest.mark.parametrize("name,T", [("8b_layer", 2048), ("32b_layer", 4096)])
+def test_bf16_ds_handover_workload_shapes_reduced(name, T):
+    wl = W.WORKLOADS[name]
+    G = wl.n_q_heads // wl.n_kv_heads
+    check_dense(wl, heads=list(range(G)) + list(range(wl.n_q_heads - G, wl.n_q_heads)), T=T, ds=True)
 
 
 def test_bf16_ds_and_recompute_paths_agree():
@@ -189,8 +191,8 @@ def test_bf16_ds_and_recompute_paths_agree():
     # and match bitwise.
     wl = custom("bf16_paths", 1500, 256, 8, 2, 128, "bf16", seed=17, spike=1)
     inp = W.make_inputs(wl)
-    a, _ = run_chunked(wl, inp, 1500, 1.0)
-    b, _ = run_chunked(wl, inp, 1500, 1.0, min_ws=True)
+    a, _ = run_chunked(wl, inp, 1500, 1.0, ds=True)
+    b, _ = run_chunked(wl, inp, 1500, 1.0)
     for n_ in ("o", "lse", "dk", "dv"):
         assert np.array_equal(a[n_], b[n_]), n_
     f = inp.f64
@@ -217,8 +219,8 @@ def test_bf16_ds_workspace_garbage_never_read():
     dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
     dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
     desc = B.make_desc(q, k, chunk_start=0, chunk_len=C)
-    ws = torch.empty(B.chunk_attn_workspace_size(desc, B.CA_OP_BWD), dtype=torch.uint8, device=DEV)
-    assert ws.numel() > B.chunk_attn_workspace_size(desc, B.CA_OP_BWD_MIN)   # the dS path is taken
+    ws = torch.empty(B.chunk_attn_workspace_size(desc, B.CA_OP_BWD_DS), dtype=torch.uint8, device=DEV)
+    assert ws.numel() > B.chunk_attn_workspace_size(desc, B.CA_OP_BWD)   # the dS path is taken
     for i in reversed(range(-(-T // C))):
         s = i * C
         ws.fill_(255)
@@ -258,22 +260,64 @@ def test_sparse_reduced_matches_oracle():
         assert np.all(got["dq"][:, :, i * wl.chunk:(i + 1) * wl.chunk] == 0.0)
 
 
-def test_sparse_all_chunks_equals_chunked_backward_bitwise():
+@pytest.mark.parametrize("ds", [False, True])
+def test_sparse_all_chunks_equals_chunked_backward_bitwise(ds):
     wl = custom("sp_all", 1000, 128, 4, 2, 128, "bf16", seed=21)
     inp = W.make_inputs(wl)
-    dense, _ = run_chunked(wl, inp, 1000, 1.0)
+    dense, _ = run_chunked(wl, inp, 1000, 1.0, ds=ds)
     k_chunks = wl.n_chunks
-    sparse, sel = run_chunked(wl, inp, 1000, 1.0, sparse=(k_chunks, 99))
+    sparse, sel = run_chunked(wl, inp, 1000, 1.0, sparse=(k_chunks, 99), ds=ds)
     assert sel == list(range(k_chunks))
     for n_ in ("dq", "dk", "dv"):
         assert np.array_equal(dense[n_], sparse[n_]), n_
 
 
-def test_deterministic():
+@pytest.mark.parametrize("dtype,ds", [("bf16", False), ("bf16", True), ("f32", False)])
+def test_sweeps_equal_per_chunk_calls(dtype, ds):
+    # chunked_fwd_sweep / chunked_bwd_sweep (the schedule computed in the
+    # library) against chunk_attn_fwd / chunk_attn_bwd called chunk by chunk
+    # (the schedule computed here): bitwise equal, with a ragged last chunk
+    # and a grad_scale.
+    B = binding()
+    wl = custom("sweep", 1100, 256, 4, 2, 128, dtype, seed=13, spike=1)
+    inp = W.make_inputs(wl)
+    t = to_dev(inp)
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    outs = []
+    for lib_sweep in (True, False):
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+        dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+        dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
+        if lib_sweep:
+            B.chunked_forward(q, k, v, o, lse, chunk=256)
+            B.chunked_backward(q, k, v, o, lse, do, dq, dk, dv, chunk=256, grad_scale=0.5, ds_handover=ds)
+        else:
+            for i in range(wl.n_chunks):
+                s_, c_ = wl.chunk_bounds(i)
+                B.chunk_attn_fwd(q, k, v, o, lse, chunk_start=s_, chunk_len=c_, q_row_offset=s_)
+            for i in reversed(range(wl.n_chunks)):
+                s_, c_ = wl.chunk_bounds(i)
+                B.chunk_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, chunk_start=s_, chunk_len=c_, q_row_offset=s_,
+                                 grad_scale=0.5, ds_handover=ds)
+        torch.cuda.synchronize()
+        outs.append([x.float().cpu() for x in (o, lse, dq, dk, dv)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    f = inp.f64
+    rdq, rdk, rdv = A.backward(f["q"], f["k"], f["v"], f["do"], 1.0)
+    bar = 1e-5 if dtype == "f32" else 2e-2
+    for got, ref in zip(outs[0][2:], (rdq, rdk, rdv)):
+        assert rel_inf(got.double().numpy(), 0.5 * ref) <= bar
+
+
+@pytest.mark.parametrize("ds", [False, True])
+def test_deterministic(ds):
     wl = custom("det", 700, 256, 4, 2, 128, "bf16", seed=3)
     inp = W.make_inputs(wl)
-    a, _ = run_chunked(wl, inp, 700, 1.0)
-    b, _ = run_chunked(wl, inp, 700, 1.0)
+    a, _ = run_chunked(wl, inp, 700, 1.0, ds=ds)
+    b, _ = run_chunked(wl, inp, 700, 1.0, ds=ds)
     for n_ in a:
         assert np.array_equal(a[n_], b[n_]), n_
 
