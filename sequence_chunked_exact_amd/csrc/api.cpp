@@ -389,7 +389,9 @@ int sparse_chunk_bwd(const chunk_attn_desc* d, int32_t seq_len, int32_t t, uint6
   hipStream_t st = (hipStream_t)stream;
   const size_t nq = (size_t)d->batch * d->n_q_heads * d->q_capacity * d->head_dim;
   const size_t nkv = (size_t)d->batch * d->n_kv_heads * d->kv_capacity * d->head_dim;
-  hipError_t e = ca::launch_zero(dq, nq, st);
+  // dq rows of the selected chunks are overwritten: with every chunk selected
+  // and no rows past seq_len, nothing is left to zero
+  hipError_t e = (t < kch || seq_len < d->q_capacity) ? ca::launch_zero(dq, nq, st) : hipSuccess;
   if (e == hipSuccess) e = ca::launch_zero(dk, nkv, st);
   if (e == hipSuccess) e = ca::launch_zero(dv, nkv, st);
   if (e != hipSuccess) return hip_fail(e, "sparse_chunk_bwd zero");

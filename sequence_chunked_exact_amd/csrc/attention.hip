@@ -464,7 +464,7 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
 #pragma unroll
           for (int nt = 0; nt < NQT; ++nt) {
             s[hh][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            dp[hh][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[hh][nt] = f32x4{-dl[nt], -dl[nt], -dl[nt], -dl[nt]};  // the products give dP - delta
           }
 #pragma unroll
         for (int kb = 0; kb < DK; ++kb)
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
             for (int ii = 0; ii < 4; ++ii) {
               float pv = fexp2(__builtin_fmaf(s[hh][nt][ii], c2, -lse2[nt]));
               if (diag && kb0 + (2 * kb2 + hh) * 16 + 4 * g + ii > qp) pv = 0.f;
-              dp[hh][nt][ii] = pv * (dp[hh][nt][ii] - dl[nt]);
+              dp[hh][nt][ii] = pv * dp[hh][nt][ii];
             }
           dsf[nt] = pack44<T>(dp[0][nt], dp[1][nt]);
         }
