@@ -259,7 +259,8 @@ def layer_main(args):
     proj_flops = 3 * 2 * Bt * T * dm * (Hq + 2 * Hkv) * d
     total = attn_flops + proj_flops
     # algorithmic FLOPs of the products each kernel carries (as in the attention step)
-    kflops = {"proj": proj_flops, "fwd": 4 * d * Hq * pairs, "dkdv": 8 * d * Hq * pairs, "dq": 2 * d * Hq * pairs}
+    kflops = {"proj": proj_flops, "fwd": 4 * d * Hq * pairs, "dkdv": 8 * d * Hq * pairs, "dq": 2 * d * Hq * pairs,
+              "bwd": 10 * d * Hq * pairs}
     ms, _, kernels, dom, (n_dom, t_dom) = timed_steps(
         B, torch, step, args.steps,
         lambda k_: max((n_ for n_ in k_ if n_ in kflops), key=lambda n_: k_[n_]["ms_per_step"]))
@@ -305,7 +306,7 @@ def stack_flops(wl, T, drawn):
     attention forward) and the backward (attention and projections)."""
     Hq, Hkv, d, dm, C, L = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.d_model, wl.chunk, wl.n_layers
     proj_row = 2 * dm * (Hq + 2 * Hkv) * d          # one row of Q|K|V
-    f = {"proj": 0, "fwd": 0, "dkdv": 0, "dq": 0}
+    f = {"proj": 0, "fwd": 0, "bwd": 0}
     for s in range(0, T, C):
         c = min(C, T - s)
         f["proj"] += L * c * proj_row
@@ -316,8 +317,7 @@ def stack_flops(wl, T, drawn):
         pairs = causal_pairs(s, c)
         f["proj"] += L * c * proj_row * 3           # rebuild, dW, dH
         f["fwd"] += L * 4 * d * pairs * Hq          # rebuild
-        f["dkdv"] += L * 8 * d * pairs * Hq
-        f["dq"] += L * 2 * d * pairs * Hq
+        f["bwd"] += L * 10 * d * pairs * Hq        # dK/dV (8 d) and dQ (2 d), one launch
     return f
 
 
@@ -629,7 +629,8 @@ def main():
 
     # roofline for the kernel with the most GPU time; its algorithmic FLOPs are
     # the products it carries (forward: S, PV = 4d per pair; dK/dV: S, dP, dV,
-    # dK = 8d per pair; dQ: the dQ product, 2d)
+    # dK = 8d per pair; dQ: the dQ product, 2d; the fused backward launch, dK/dV
+    # and dQ together: 10d; recomputed products are not counted)
     t_wall = time.perf_counter()
     ms, per_step, kernels, dom, (n_launch, tot_ms) = timed_steps(
         B, torch, run, args.steps, lambda k_: max(k_, key=lambda n_: k_[n_]["ms_per_step"]))
@@ -641,7 +642,7 @@ def main():
     plan = flop_plan(wl, selected if sparse else None)
     total_flops = plan["fwd"] + plan["bwd"]
     tflops = total_flops / (ms * 1e-3) / 1e12
-    dom_flops = {"fwd": plan["fwd"], "dkdv": plan["dkdv"], "dq": plan["bwd"] // 5}.get(dom)
+    dom_flops = {"fwd": plan["fwd"], "dkdv": plan["dkdv"], "dq": plan["bwd"] // 5, "bwd": plan["bwd"]}.get(dom)
     roof = {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": None, "traffic": None}
     if dom_flops is not None:
@@ -653,7 +654,7 @@ def main():
     from sequence_chunked_exact_amd.profile_summary import read_traffic
     roof["traffic"] = read_traffic(os.path.join(ROOT, "profiles", f"{dom}_{wl.name}.md"), dom)
     fwd_ms = kernels.get("fwd", {}).get("ms_per_step", 0.0)
-    bwd_ms = sum(kernels.get(k_, {}).get("ms_per_step", 0.0) for k_ in ("delta", "dkdv", "dq", "zero"))
+    bwd_ms = sum(kernels.get(k_, {}).get("ms_per_step", 0.0) for k_ in ("delta", "dkdv", "dq", "bwd", "zero"))
 
     out = {
         "metric": METRIC,

@@ -375,8 +375,9 @@ int lm_head_dpo_finish(const lm_head_desc* desc, int32_t seq_len, const float* r
 
 /* Kernel timing for benchmarks (instrumentation only; results are unchanged).
  * chunk_attn_profile_start() clears the record and, until
- * chunk_attn_profile_stop(), brackets every kernel this library launches with
- * two HIP events recorded on the launching stream. chunk_attn_profile_read()
+ * chunk_attn_profile_stop(), times every kernel this library launches with a
+ * pair of HIP events that the launch itself stamps with the kernel's start and
+ * end (hipExtLaunchKernelGGL on the launching stream). chunk_attn_profile_read()
  * waits for the recorded events and returns, for one kernel id, the number of
  * launches and their summed GPU time in milliseconds. Events are created on
  * first use and reused; start/stop/read are serialized by a lock. Returns
@@ -384,8 +385,8 @@ int lm_head_dpo_finish(const lm_head_desc* desc, int32_t seq_len, const float* r
 enum {
   CA_KERNEL_FWD = 0,        /* chunk forward */
   CA_KERNEL_DELTA = 1,      /* rowsum(dO * O) */
-  CA_KERNEL_DKDV = 2,       /* dK/dV accumulation over the prefix */
-  CA_KERNEL_DQ = 3,         /* dQ of the chunk */
+  CA_KERNEL_DKDV = 2,       /* dK/dV accumulation over the prefix (dS hand-over backward) */
+  CA_KERNEL_DQ = 3,         /* dQ of the chunk from the handed-over dS */
   CA_KERNEL_ACCUMULATE = 4, /* prefix_grad_accumulate */
   CA_KERNEL_ZERO = 5,       /* zero fill used by sparse_chunk_bwd */
   CA_KERNEL_PROJ = 6,       /* projection GEMMs of qkv_proj_fwd / qkv_proj_bwd */
@@ -393,7 +394,8 @@ enum {
   CA_KERNEL_RESIDUAL = 8,   /* spaco_stack_*: residual connections between layers */
   CA_KERNEL_HEAD = 9,       /* lm_head_sft_partition: logits, dH and dW products */
   CA_KERNEL_HEAD_AUX = 10,  /* lm_head_*: softmax/cross-entropy rows, weight transpose */
-  CA_KERNEL_COUNT = 11
+  CA_KERNEL_BWD = 11,       /* dQ and dK/dV of the chunk in one launch (backward without the dS hand-over) */
+  CA_KERNEL_COUNT = 12
 };
 int chunk_attn_profile_start(void);
 /* Bit k of kernel_mask (default all) selects kernel id k for the events;

@@ -125,8 +125,9 @@ struct SplitMix64 {
 
 
 // ---------------------------------------------------------------------------
-// Launch timing: HIP events recorded on the launching stream around each
-// kernel while profiling is on. Events come from a reusable pool.
+// Launch timing: while profiling is on, each selected launch gets a pair of
+// HIP events from a reusable pool, which the dispatch stamps with the
+// kernel's start and end (hipExtLaunchKernelGGL).
 // ---------------------------------------------------------------------------
 namespace ca {
 namespace {
@@ -146,7 +147,6 @@ ProfState& prof() {
   static ProfState s;
   return s;
 }
-thread_local long t_pending = -1;
 
 hipEvent_t take_event(ProfState& s) {
   if (s.used == s.pool.size()) {
@@ -160,24 +160,14 @@ hipEvent_t take_event(ProfState& s) {
 }
 }  // namespace
 
-void prof_begin(int kernel, hipStream_t st) {
+ProfPair prof_launch(int kernel) {
   ProfState& s = prof();
   std::lock_guard<std::mutex> g(s.mu);
-  t_pending = -1;
-  if (!s.on || !((s.mask >> kernel) & 1u)) return;
-  hipEvent_t a = take_event(s);
-  if (!a || hipEventRecord(a, st) != hipSuccess) return;
-  s.recs.push_back({kernel, a, nullptr});
-  t_pending = (long)s.recs.size() - 1;
-}
-
-void prof_end(int kernel, hipStream_t st) {
-  ProfState& s = prof();
-  std::lock_guard<std::mutex> g(s.mu);
-  if (!s.on || t_pending < 0 || t_pending >= (long)s.recs.size() || s.recs[t_pending].kernel != kernel) return;
-  hipEvent_t b = take_event(s);
-  if (b && hipEventRecord(b, st) == hipSuccess) s.recs[t_pending].b = b;
-  t_pending = -1;
+  if (!s.on || !((s.mask >> kernel) & 1u)) return {nullptr, nullptr};
+  hipEvent_t a = take_event(s), b = take_event(s);
+  if (!a || !b) return {nullptr, nullptr};
+  s.recs.push_back({kernel, a, b});
+  return {a, b};
 }
 }  // namespace ca
 

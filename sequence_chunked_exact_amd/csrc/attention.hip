@@ -40,8 +40,10 @@
 //    running maximum is only moved (rescaling O and the row sum) when a new
 //    score exceeds it by more than 2^8, which keeps every exponent <= 2^8.
 #include "device_common.h"
+#include "timed_launch.h"
 
 #include <mutex>
+#include <type_traits>
 
 // Scratch of the allocation-free backward (chunk_attn_bwd_noalloc): the
 // chunk's row statistics go here instead of into a caller workspace. Every
@@ -380,24 +382,32 @@ struct BwdParams {
 // dP^T = V dO^T with K, V read row-major, P from the stored LSE, and
 // dQ^T += K^T dS^T with K read through the transposing path. Group 1 hands
 // its partial dQ to group 0 through LDS at the end.
+template <typename T, int D, int BK>
+struct DqLds {
+  __attribute__((aligned(16))) T Kb0[2 * BK * D];
+  __attribute__((aligned(16))) T Vb0[2 * BK * D];
+  __attribute__((aligned(16))) T Kb1[2 * BK * D];
+  __attribute__((aligned(16))) T Vb1[2 * BK * D];
+};
+// Workgroup `block` of `nblocks` (the pass's own grid) with its LDS in `sm`.
 template <typename T, int D, int NQT, int BK, int NW>
-__global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_body(const BwdParams& p, int block, int nblocks, DqLds<T, D, BK>& sm) {
   using E = Elt<T>;
   using frag = typename E::frag;
   using Lt = SwzLay<T, D>;
   constexpr int BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, KB2 = BK / 32;
-  __shared__ __attribute__((aligned(16))) T Kb0[2 * BK * D];
-  __shared__ __attribute__((aligned(16))) T Vb0[2 * BK * D];
-  __shared__ __attribute__((aligned(16))) T Kb1[2 * BK * D];
-  __shared__ __attribute__((aligned(16))) T Vb1[2 * BK * D];
+  T* const Kb0 = sm.Kb0;
+  T* const Vb0 = sm.Vb0;
+  T* const Kb1 = sm.Kb1;
+  T* const Vb1 = sm.Vb1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave / NW, wq = wave % NW;
   const int n = lane & 15, g = lane >> 4;
   const int nqt = (p.len + BQ - 1) / BQ;
-  const int work_id = xcd_order(blockIdx.x, gridDim.x);
+  const int work_id = xcd_order(block, nblocks);
   const int qt = nqt - 1 - work_id % nqt;  // longest rows first
   const int h = (work_id / nqt) % p.hq, b = work_id / (nqt * p.hq);
   const int hk = h / (p.hq / p.hkv);
@@ -479,19 +489,30 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
               E::mma(dp[hh][nt], av, df[nt][kb]);
             }
           }
+        // dS = P (dP - delta), with the causal mask only on tiles that cross
+        // the diagonal: two copies of this step, chosen per tile.
         frag dsf[NQT];
+        auto make_ds = [&](auto masked) {
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) {
-          const int qp = wq_lo + nt * 16 + n;
+          for (int nt = 0; nt < NQT; ++nt) {
+            const int qp = wq_lo + nt * 16 + n;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
+            for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-              float pv = fexp2(__builtin_fmaf(s[hh][nt][ii], c2, -lse2[nt]));
-              if (diag && kb0 + (2 * kb2 + hh) * 16 + 4 * g + ii > qp) pv = 0.f;
-              dp[hh][nt][ii] = pv * dp[hh][nt][ii];
-            }
-          dsf[nt] = pack44<T>(dp[0][nt], dp[1][nt]);
+              for (int ii = 0; ii < 4; ++ii) {
+                float pv = fexp2(__builtin_fmaf(s[hh][nt][ii], c2, -lse2[nt]));
+                if constexpr (decltype(masked)::value) {
+                  if (kb0 + (2 * kb2 + hh) * 16 + 4 * g + ii > qp) pv = 0.f;
+                }
+                dp[hh][nt][ii] = pv * dp[hh][nt][ii];
+              }
+            dsf[nt] = pack44<T>(dp[0][nt], dp[1][nt]);
+          }
+        };
+        if (diag) {
+          make_ds(std::true_type{});
+        } else {
+          make_ds(std::false_type{});
         }
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
@@ -512,7 +533,7 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
   // Merge: group 1 publishes its partial dQ^T per lane (columns [0, D/2) in
   // Kb0, [D/2, D) in Vb0), group 0 adds it.
   constexpr int HALF = MD / 2 * 4;
-  static_assert(sizeof(Kb0) >= (size_t)NQT * NW * 64 * HALF * sizeof(float), "merge area");
+  static_assert(sizeof(sm.Kb0) >= (size_t)NQT * NW * 64 * HALF * sizeof(float), "merge area");
   float* xo0 = (float*)Kb0;
   float* xo1 = (float*)Vb0;
   if (grp == 1) {
@@ -563,10 +584,23 @@ __global__ __launch_bounds__(2 * NW * 64) void dq_kernel(BwdParams p) {
 // are read row-major as the A operand of S and dP and through the transposing
 // path as the B operand of dV and dK.
 template <typename T, int D, int NKT, int BQ, int NP>
-__global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
+struct DkdvLds {
+  static constexpr int NB = 3, NBQ = 4, KQ = BQ / 32;
+  __attribute__((aligned(16))) T Qs[NBQ][BQ * PadLay<T, D>::RS];
+  __attribute__((aligned(16))) T Ds[NB][BQ * PadLay<T, D>::RS];
+  // per buffer: LSE*log2(e) of the block's rows in [0, BQ), delta in [BQ, 2BQ)
+  __attribute__((aligned(16))) float stat_s[NB][2 * BQ];
+  // P of a pair's block as the A fragments of dV: [block parity][pair][kq][nk][lane]
+  typename Elt<T>::frag Ps[2][NP][KQ][NKT][64];
+};
+// Workgroup `block` of `nblocks` (the pass's own grid) with its LDS in `sm`.
+template <typename T, int D, int NKT, int BQ, int NP>
+__device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nblocks,
+                                          DkdvLds<T, D, NKT, BQ, NP>& sm) {
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int BKV = NP * NKT * 16, NB = 3, NBQ = 4;
+  using Lds = DkdvLds<T, D, NKT, BQ, NP>;
+  constexpr int BKV = NP * NKT * 16, NB = Lds::NB, NBQ = Lds::NBQ;
   constexpr int DK = D / 32, MD = D / 16, MQ = BQ / 16, KQ = BQ / 32;
   // Only the P/dV waves load Q/dO blocks (and only the dS/dK waves store dS):
   // vector loads and stores complete out of order with respect to each other
@@ -574,12 +608,10 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   // whenever it waits for a load.
   constexpr int NL = NP * 64;  // loading threads
   static_assert(2 * BQ <= NL, "row statistics: one value per loading thread");
-  __shared__ __attribute__((aligned(16))) T Qs[NBQ][BQ * PadLay<T, D>::RS];
-  __shared__ __attribute__((aligned(16))) T Ds[NB][BQ * PadLay<T, D>::RS];
-  // per buffer: LSE*log2(e) of the block's rows in [0, BQ), delta in [BQ, 2BQ)
-  __shared__ __attribute__((aligned(16))) float stat_s[NB][2 * BQ];
-  // P of a pair's block as the A fragments of dV: [block parity][pair][kq][nk][lane]
-  __shared__ frag Ps[2][NP][KQ][NKT][64];
+  auto& Qs = sm.Qs;
+  auto& Ds = sm.Ds;
+  auto& stat_s = sm.stat_s;
+  auto& Ps = sm.Ps;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -589,7 +621,7 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   const int G = p.hq / p.hkv;
   const int L = p.start + p.len;
   const int nkt = (p.kv_end - p.kv_first + BKV - 1) / BKV;
-  const int work_id = xcd_order(blockIdx.x, gridDim.x);
+  const int work_id = xcd_order(block, nblocks);
   const int kt = work_id % nkt;  // ascending: the first key tiles see the most queries
   const int hk = (work_id / nkt) % p.hkv, b = work_id / (nkt * p.hkv);
   const int kb0 = p.kv_first + kt * BKV;
@@ -837,6 +869,47 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   }
 }
 
+// dK/dV pass as its own launch (the dS hand-over path, whose dQ pass reads
+// what this one stores).
+template <typename T, int D, int NKT, int BQ, int NP>
+__global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
+  __shared__ DkdvLds<T, D, NKT, BQ, NP> sm;
+  dkdv_body<T, D, NKT, BQ, NP>(p, blockIdx.x, gridDim.x, sm);
+}
+
+template <typename A, typename B>
+union LdsUnion {
+  A a;
+  B b;
+};
+
+// The chunk's dQ (recomputing dS) and dK/dV passes in one launch: a sub-grid
+// of n_dq query-tile workgroups and one of n_kv key-tile workgroups. The
+// sub-grid whose longest workgroup carries more work goes first, and the
+// other's workgroups fill the compute units it leaves idle in its last round.
+// Both read the same inputs and write disjoint outputs (dQ rows; dK/dV keys,
+// each owned by one workgroup), so the result does not depend on how their
+// workgroups interleave. Their LDS layouts share one allocation. The first
+// sub-grid is padded to a multiple of the 8 XCDs (padding workgroups exit at
+// once) so that each keeps the XCD-aware order of its own grid.
+template <typename T, int D, int NQT, int BK, int NW, int NKT, int BQ, int NP>
+__global__ __launch_bounds__(2 * NW * 64) void bwd_kernel(BwdParams p, int n_dq, int n_kv, int dq_first) {
+  static_assert(NW == NP, "one workgroup shape for both passes");
+  __shared__ LdsUnion<DqLds<T, D, BK>, DkdvLds<T, D, NKT, BQ, NP>> sm;
+  const int first_pad = ((dq_first ? n_dq : n_kv) + 7) / 8 * 8;
+  int blk = blockIdx.x;
+  const bool in_first = blk < first_pad;
+  if (!in_first) blk -= first_pad;
+  const bool is_dq = in_first == (dq_first != 0);
+  const int nb = is_dq ? n_dq : n_kv;
+  if (blk >= nb) return;
+  if (is_dq) {
+    dq_body<T, D, NQT, BK, NW>(p, blk, nb, sm.a);
+  } else {
+    dkdv_body<T, D, NKT, BQ, NP>(p, blk, nb, sm.b);
+  }
+}
+
 // Query row (within a group of 32) held by column p of a stored dS^T row:
 // the dK/dV pass writes each lane's fragment slots as they are, so column
 // 8 g + s holds row 4 g + s for s < 4 and 16 + 4 g + s - 4 otherwise.
@@ -1061,17 +1134,15 @@ hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   using C = Cfg<T, D>;
   FwdParams p{q,     k,     v,       o,        lse,     s.hq,    s.hkv, s.q_cap, s.kv_cap, s.q_off,
               s.start, s.len, exp2_coef(s.scale), s.scale < 0.f ? 1 : 0};
-  prof_begin(CA_KERNEL_FWD, st);
   // A chunk too short to give every compute unit a 128-row tile (e.g. 500
   // rows x 32 heads = 128 tiles) runs 64-row tiles, one 16-row tile per wave.
   if (C::FWD_NQT > 1 && q_tiles<C::FWD_NW, C::FWD_NQT>(s) < device_cus()) {
-    hipLaunchKernelGGL((fwd_kernel<T, D, 1, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, 1>(s)),
+    CA_LAUNCH(CA_KERNEL_FWD, (fwd_kernel<T, D, 1, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, 1>(s)),
                        dim3(2 * C::FWD_NW * 64), 0, st, p);
   } else {
-    hipLaunchKernelGGL((fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, C::FWD_NQT>(s)),
+    CA_LAUNCH(CA_KERNEL_FWD, (fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, C::FWD_NQT>(s)),
                        dim3(2 * C::FWD_NW * 64), 0, st, p);
   }
-  prof_end(CA_KERNEL_FWD, st);
   return hipGetLastError();
 }
 
@@ -1089,10 +1160,8 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   const int threads = rows * LPR;
   float* delta = ws;
   float* lse2 = ws + bwd_ws_stride(rows);
-  prof_begin(CA_KERNEL_DELTA, st);
-  hipLaunchKernelGGL((delta_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0, st, (const T*)o,
+  CA_LAUNCH(CA_KERNEL_DELTA, (delta_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0, st, (const T*)o,
                      (const T*)dout, lse, delta, lse2, s.q_cap, s.q_off, s.len, rows);
-  prof_end(CA_KERNEL_DELTA, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   BwdParams p{q,     k,     v,       dout,     lse,     delta,   lse2,  dq,   dk,
@@ -1100,62 +1169,62 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
               exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs,
               use_ds ? (void*)((char*)ws + bwd_ws_base(rows)) : nullptr,
               (s.len + kDsCols - 1) / kDsCols, (L + kDsKeyPad - 1) / kDsKeyPad * kDsKeyPad, 0, L};
-  // Every workgroup of the dK/dV pass owns one key tile and walks all the
-  // chunk's queries that see it, so the pass takes whole "rounds" of one tile
-  // per compute unit. Key tiles of half the size (16 keys per wave) take ~3/4
-  // of a round: a prefix that fills at most half the units runs on them alone,
-  // and when whole rounds of full tiles leave a remainder that half-size
-  // tiles can cover in one round, that remainder (the chunk's own diagonal
-  // keys, which the fewest queries see) goes to a second launch of them.
   constexpr int BKV = C::KV_NP * C::KV_NKT * 16, BKV1 = C::KV_NP * 16;
-  const int cus = device_cus(), heads = s.hkv * s.batch;
+  const int heads = s.hkv * s.batch;
   const int tiles = (L + BKV - 1) / BKV;
-  const int rounds = tiles * heads / cus;
-  const int tiles_a = rounds * cus / heads;  // full tiles per head in whole rounds
-  const bool split = C::KV_NKT > 1 && rounds >= 1 && tiles_a < tiles &&
-                     (L - tiles_a * BKV + BKV1 - 1) / BKV1 * heads <= cus;
-  prof_begin(CA_KERNEL_DKDV, st);
-  if (C::KV_NKT > 1 && 2 * tiles * heads <= cus) {
-    hipLaunchKernelGGL((dkdv_kernel<T, D, 1, C::KV_BQ, C::KV_NP>), dim3((L + BKV1 - 1) / BKV1 * heads),
-                       dim3(2 * C::KV_NP * 64), 0, st, p);
-  } else if (split) {
-    p.kv_end = tiles_a * BKV;
-    hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(tiles_a * heads),
-                       dim3(2 * C::KV_NP * 64), 0, st, p);
-    prof_end(CA_KERNEL_DKDV, st);  // timed as two launches, as a kernel trace counts them
-    prof_begin(CA_KERNEL_DKDV, st);
-    p.kv_first = tiles_a * BKV;
-    p.kv_end = L;
-    hipLaunchKernelGGL((dkdv_kernel<T, D, 1, C::KV_BQ, C::KV_NP>), dim3((L - p.kv_first + BKV1 - 1) / BKV1 * heads),
-                       dim3(2 * C::KV_NP * 64), 0, st, p);
-  } else {
-    hipLaunchKernelGGL((dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(tiles * heads),
-                       dim3(2 * C::KV_NP * 64), 0, st, p);
+  if (!use_ds) {
+    // dQ recomputes dS: both passes in one launch. A dQ workgroup (BQD query
+    // rows) walks the whole prefix with three products per key; a dK/dV
+    // workgroup (BKV keys) walks up to all G * len query rows of its group
+    // with four, so the dQ sub-grid goes first once 3 L >= 4 G len.
+    constexpr int BQD = C::DQ_NW * C::DQ_NQT * 16;
+    const int n_dq = (s.len + BQD - 1) / BQD * s.hq * s.batch;
+    const int n_kv = tiles * heads;
+    const int dq_first = 3LL * L >= 4LL * (s.hq / s.hkv) * s.len ? 1 : 0;
+    const int grid = ((dq_first ? n_dq : n_kv) + 7) / 8 * 8 + (dq_first ? n_kv : n_dq);
+    CA_LAUNCH(CA_KERNEL_BWD, (bwd_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW, C::KV_NKT, C::KV_BQ, C::KV_NP>),
+              dim3(grid), dim3(2 * C::DQ_NW * 64), 0, st, p, n_dq, n_kv, dq_first);
+    return hipGetLastError();
   }
-  prof_end(CA_KERNEL_DKDV, st);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  prof_begin(CA_KERNEL_DQ, st);
   if constexpr (sizeof(T) == 2) {
-    if (use_ds) {
-      if (p.ds_nqb * s.hq * s.batch < device_cus()) {  // short chunk: 64-column workgroups
-        hipLaunchKernelGGL((dqs_kernel<D, 1, 64, 4>), dim3(((s.len + 63) / 64) * s.hq * s.batch), dim3(2 * 4 * 64),
-                           0, st, p);
-      } else {
-        hipLaunchKernelGGL((dqs_kernel<D, 2, 64, 4>), dim3(p.ds_nqb * s.hq * s.batch), dim3(2 * 4 * 64), 0, st, p);
-      }
-      prof_end(CA_KERNEL_DQ, st);
-      return hipGetLastError();
+    // dS hand-over: the dK/dV pass stores dS^T, then dQ = dS K streams it.
+    // Every workgroup of the dK/dV pass owns one key tile and walks all the
+    // chunk's queries that see it, so the pass takes whole "rounds" of one
+    // tile per compute unit. Key tiles of half the size (16 keys per wave)
+    // take ~3/4 of a round: a prefix that fills at most half the units runs
+    // on them alone, and when whole rounds of full tiles leave a remainder
+    // that half-size tiles can cover in one round, that remainder (the
+    // chunk's own diagonal keys, which the fewest queries see) goes to a
+    // second launch of them.
+    const int cus = device_cus();
+    const int rounds = tiles * heads / cus;
+    const int tiles_a = rounds * cus / heads;  // full tiles per head in whole rounds
+    const bool split = C::KV_NKT > 1 && rounds >= 1 && tiles_a < tiles &&
+                       (L - tiles_a * BKV + BKV1 - 1) / BKV1 * heads <= cus;
+    if (C::KV_NKT > 1 && 2 * tiles * heads <= cus) {
+      CA_LAUNCH(CA_KERNEL_DKDV, (dkdv_kernel<T, D, 1, C::KV_BQ, C::KV_NP>), dim3((L + BKV1 - 1) / BKV1 * heads),
+                dim3(2 * C::KV_NP * 64), 0, st, p);
+    } else if (split) {
+      p.kv_end = tiles_a * BKV;
+      CA_LAUNCH(CA_KERNEL_DKDV, (dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(tiles_a * heads),
+                dim3(2 * C::KV_NP * 64), 0, st, p);
+      p.kv_first = tiles_a * BKV;
+      p.kv_end = L;
+      CA_LAUNCH(CA_KERNEL_DKDV, (dkdv_kernel<T, D, 1, C::KV_BQ, C::KV_NP>),
+                dim3((L - p.kv_first + BKV1 - 1) / BKV1 * heads), dim3(2 * C::KV_NP * 64), 0, st, p);
+    } else {
+      CA_LAUNCH(CA_KERNEL_DKDV, (dkdv_kernel<T, D, C::KV_NKT, C::KV_BQ, C::KV_NP>), dim3(tiles * heads),
+                dim3(2 * C::KV_NP * 64), 0, st, p);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.ds_nqb * s.hq * s.batch < cus) {  // short chunk: 64-column workgroups
+      CA_LAUNCH(CA_KERNEL_DQ, (dqs_kernel<D, 1, 64, 4>), dim3(((s.len + 63) / 64) * s.hq * s.batch),
+                dim3(2 * 4 * 64), 0, st, p);
+    } else {
+      CA_LAUNCH(CA_KERNEL_DQ, (dqs_kernel<D, 2, 64, 4>), dim3(p.ds_nqb * s.hq * s.batch), dim3(2 * 4 * 64), 0, st, p);
     }
   }
-  if (C::DQ_NQT > 1 && q_tiles<C::DQ_NW, C::DQ_NQT>(s) < device_cus()) {
-    hipLaunchKernelGGL((dq_kernel<T, D, 1, C::DQ_BK, C::DQ_NW>), dim3(q_tiles<C::DQ_NW, 1>(s)),
-                       dim3(2 * C::DQ_NW * 64), 0, st, p);
-  } else {
-    hipLaunchKernelGGL((dq_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW>), dim3(q_tiles<C::DQ_NW, C::DQ_NQT>(s)),
-                       dim3(2 * C::DQ_NW * 64), 0, st, p);
-  }
-  prof_end(CA_KERNEL_DQ, st);
   return hipGetLastError();
 }
 
@@ -1187,10 +1256,8 @@ hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads,
   const size_t total = (size_t)batch * heads * rows * (head_dim / 4);
   if (total == 0) return hipSuccess;
   const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-  prof_begin(CA_KERNEL_ACCUMULATE, st);
-  hipLaunchKernelGGL(accumulate_kernel, dim3(blocks), dim3(256), 0, st, acc, src, batch * heads, acc_cap,
+  CA_LAUNCH(CA_KERNEL_ACCUMULATE, accumulate_kernel, dim3(blocks), dim3(256), 0, st, acc, src, batch * heads, acc_cap,
                      src_cap, head_dim / 4, rows, scale);
-  prof_end(CA_KERNEL_ACCUMULATE, st);
   return hipGetLastError();
 }
 
@@ -1198,9 +1265,7 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const size_t want = (n / 4 + 255) / 256;
   const int blocks = (int)(want < 4096 ? (want > 0 ? want : 1) : 4096);
-  prof_begin(CA_KERNEL_ZERO, st);
-  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, st, p, n);
-  prof_end(CA_KERNEL_ZERO, st);
+  CA_LAUNCH(CA_KERNEL_ZERO, zero_kernel, dim3(blocks), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

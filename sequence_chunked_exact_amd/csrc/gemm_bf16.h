@@ -14,6 +14,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "timed_launch.h"
 
 namespace ca {
 namespace {
@@ -265,13 +266,11 @@ int pg_rows_pad(int len) { return (len + 63) / 64 * 64; }
 template <int MODE>
 hipError_t pg_launch(const ProjGemmParams& p, int grid_batch, int prof_id, hipStream_t st) {
   const int tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * grid_batch;
-  prof_begin(prof_id, st);
   if (tiles < 384) {
-    hipLaunchKernelGGL((proj_gemm_kernel<MODE, 2>), dim3(tiles), dim3(512), 0, st, p);
+    CA_LAUNCH(prof_id, (proj_gemm_kernel<MODE, 2>), dim3(tiles), dim3(512), 0, st, p);
   } else {
-    hipLaunchKernelGGL((proj_gemm_kernel<MODE, 1>), dim3(tiles), dim3(256), 0, st, p);
+    CA_LAUNCH(prof_id, (proj_gemm_kernel<MODE, 1>), dim3(tiles), dim3(256), 0, st, p);
   }
-  prof_end(prof_id, st);
   return hipGetLastError();
 }
 

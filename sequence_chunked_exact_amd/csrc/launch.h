@@ -53,9 +53,14 @@ hipError_t scratch_address(void** ptr);
 hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap,
                              int src_cap, int head_dim, int rows, float scale, hipStream_t st);
 
-// Timing hooks around each launch (no-ops unless profiling is on).
-void prof_begin(int kernel, hipStream_t st);
-void prof_end(int kernel, hipStream_t st);
+// Launch timing: while profiling is on and selects `kernel`, a start/stop
+// event pair (from a reusable pool) recorded for one launch, which the
+// launch hands to the dispatch (CA_LAUNCH in timed_launch.h); both null
+// otherwise.
+struct ProfPair {
+  hipEvent_t a, b;
+};
+ProfPair prof_launch(int kernel);
 
 // Projections around one chunk's attention. h is [batch][h_cap][d_model]
 // (rows h_off.. are the chunk's positions); wq is [d_model][hq*head_dim], wk and

@@ -153,10 +153,8 @@ size_t head_ws_bytes(const HeadShape& s) {
 }
 
 hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hipStream_t st) {
-  prof_begin(CA_KERNEL_HEAD_AUX, st);
-  hipLaunchKernelGGL(wt_head_kernel, dim3((s.vocab / 64) * (s.d_model / 64)), dim3(256), 0, st, (const bf16*)w,
+  CA_LAUNCH(CA_KERNEL_HEAD_AUX, wt_head_kernel, dim3((s.vocab / 64) * (s.d_model / 64)), dim3(256), 0, st, (const bf16*)w,
                      (bf16*)wt, s.vocab, s.d_model);
-  prof_end(CA_KERNEL_HEAD_AUX, st);
   return hipGetLastError();
 }
 
@@ -210,9 +208,7 @@ hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zer
   cp.rows_pad = zero_to;
   cp.vocab = V;
   cp.batch = s.batch;
-  prof_begin(CA_KERNEL_HEAD_AUX, st);
-  hipLaunchKernelGGL(ce_kernel, dim3(s.batch * zero_to), dim3(256), 0, st, cp);
-  prof_end(CA_KERNEL_HEAD_AUX, st);
+  CA_LAUNCH(CA_KERNEL_HEAD_AUX, ce_kernel, dim3(s.batch * zero_to), dim3(256), 0, st, cp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -241,10 +237,8 @@ hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zer
     if (e != hipSuccess) return e;
     const long long n4 = (long long)rows * dm / 4;
     const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
-    prof_begin(CA_KERNEL_HEAD_AUX, st);
-    hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks), dim3(256), 0, st, part,
+    CA_LAUNCH(CA_KERNEL_HEAD_AUX, splitk_sum_kernel, dim3(blocks), dim3(256), 0, st, part,
                        dh + ((size_t)b * s.capacity + s0) * dm, S, rows, dm);
-    prof_end(CA_KERNEL_HEAD_AUX, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -288,10 +288,8 @@ __global__ __launch_bounds__(256) void wt_kernel(WtParams p) {
 
 template <typename T, typename SA, typename SB, bool A_MN, bool B_MN, bool OUT_F32>
 hipError_t gemm_launch(const GemmParams& p, int batch, hipStream_t st) {
-  prof_begin(CA_KERNEL_PROJ, st);
-  hipLaunchKernelGGL((gemm_kernel<T, SA, SB, A_MN, B_MN, OUT_F32>), dim3((p.N + 127) / 128, (p.M + 127) / 128, batch),
+  CA_LAUNCH(CA_KERNEL_PROJ, (gemm_kernel<T, SA, SB, A_MN, B_MN, OUT_F32>), dim3((p.N + 127) / 128, (p.M + 127) / 128, batch),
                      dim3(256), 0, st, p);
-  prof_end(CA_KERNEL_PROJ, st);
   return hipGetLastError();
 }
 constexpr int kNoSplit = 1 << 30;
@@ -408,9 +406,7 @@ hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], con
   gp.out = gcat;
   const long long vecs = (long long)s.batch * rows_pad * (N / 8);
   const int blocks = (int)((vecs + 255) / 256 < 8192 ? (vecs + 255) / 256 : 8192);
-  prof_begin(CA_KERNEL_PROJ_PREP, st);
-  hipLaunchKernelGGL(gcat_kernel, dim3(blocks), dim3(256), 0, st, gp);
-  prof_end(CA_KERNEL_PROJ_PREP, st);
+  CA_LAUNCH(CA_KERNEL_PROJ_PREP, gcat_kernel, dim3(blocks), dim3(256), 0, st, gp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -422,9 +418,7 @@ hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], con
   tp.d_model = s.d_model;
   tp.ncols = N;
   tp.out = wt;
-  prof_begin(CA_KERNEL_PROJ_PREP, st);
-  hipLaunchKernelGGL(wt_kernel, dim3((N / 64) * (s.d_model / 64)), dim3(256), 0, st, tp);
-  prof_end(CA_KERNEL_PROJ_PREP, st);
+  CA_LAUNCH(CA_KERNEL_PROJ_PREP, wt_kernel, dim3((N / 64) * (s.d_model / 64)), dim3(256), 0, st, tp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -10,6 +10,7 @@
 // type out). Both are memory-bound layout passes over one chunk's rows, four
 // elements per thread.
 #include "device_common.h"
+#include "timed_launch.h"
 
 namespace ca {
 namespace {
@@ -101,13 +102,11 @@ hipError_t launch_residual_fwd(const ResidualShape& s, const void* h_in, const v
   p.a = (const char*)h_in + (size_t)s.a_off * dm * es;
   p.o = (const char*)o + (size_t)s.o_off * s.head_dim * es;
   p.c = (char*)h_out + (size_t)s.c_off * dm * es;
-  prof_begin(CA_KERNEL_RESIDUAL, st);
   if (s.dtype == CA_BF16) {
-    hipLaunchKernelGGL(residual_fwd_kernel<bf16>, dim3(residual_blocks(s)), dim3(256), 0, st, p);
+    CA_LAUNCH(CA_KERNEL_RESIDUAL, residual_fwd_kernel<bf16>, dim3(residual_blocks(s)), dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL(residual_fwd_kernel<float>, dim3(residual_blocks(s)), dim3(256), 0, st, p);
+    CA_LAUNCH(CA_KERNEL_RESIDUAL, residual_fwd_kernel<float>, dim3(residual_blocks(s)), dim3(256), 0, st, p);
   }
-  prof_end(CA_KERNEL_RESIDUAL, st);
   return hipGetLastError();
 }
 
@@ -117,13 +116,11 @@ hipError_t launch_residual_bwd(const ResidualShape& s, const float* dh, void* do
   ResidualParams p = residual_params(s);
   p.a = dh + (size_t)s.a_off * dm;
   p.c = (char*)dout + (size_t)s.o_off * s.head_dim * es;
-  prof_begin(CA_KERNEL_RESIDUAL, st);
   if (s.dtype == CA_BF16) {
-    hipLaunchKernelGGL(residual_bwd_kernel<bf16>, dim3(residual_blocks(s)), dim3(256), 0, st, p);
+    CA_LAUNCH(CA_KERNEL_RESIDUAL, residual_bwd_kernel<bf16>, dim3(residual_blocks(s)), dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL(residual_bwd_kernel<float>, dim3(residual_blocks(s)), dim3(256), 0, st, p);
+    CA_LAUNCH(CA_KERNEL_RESIDUAL, residual_bwd_kernel<float>, dim3(residual_blocks(s)), dim3(256), 0, st, p);
   }
-  prof_end(CA_KERNEL_RESIDUAL, st);
   return hipGetLastError();
 }
 
