@@ -81,12 +81,16 @@ typedef struct {
  * the whole-sequence one that sparse_chunk_bwd takes and chunk_len must be the
  * chunk size. Returns 0 for an invalid descriptor.
  *
- * CA_OP_BWD, CA_OP_SPARSE_BWD and CA_OP_BWD_MIN (the same size) give what the
- * backward needs: the chunk's row statistics, 8 bytes per row of batch *
- * n_q_heads * chunk_len (rounded up), independent of the sequence length and
- * the capacities, as the method's per-chunk working set asks (StreamBP
- * review, "What carries the argument"). The dQ pass then recomputes S, P and
- * dP from Q, K, V, dO and the row statistics.
+ * CA_OP_BWD and CA_OP_BWD_MIN (the same size) give what the backward needs:
+ * the chunk's row statistics, 8 bytes per row of batch * n_q_heads *
+ * chunk_len (rounded up), independent of the sequence length and the
+ * capacities, as the method's per-chunk working set asks (StreamBP review,
+ * "What carries the argument"). The dQ pass then recomputes S, P and dP from
+ * Q, K, V, dO and the row statistics. CA_OP_SPARSE_BWD gives two such slots:
+ * with them the whole-sequence drivers (sparse_chunk_bwd, chunked_bwd_sweep)
+ * compute the next chunk's row statistics in the same launch as this chunk's
+ * backward instead of in a launch of their own (one slot is enough for them
+ * to run).
  *
  * CA_OP_BWD_DS (either descriptor) adds, for bf16, room for a chunk's dS^T in
  * bf16: batch * n_q_heads * chunk_len * kv_capacity * 2 bytes, rows and keys
@@ -164,8 +168,9 @@ int chunk_select(int32_t k, int32_t t, uint64_t seed, int32_t* out_sorted);
  * tensors (q_capacity >= seq_len) and o, lse come from forwards of all
  * chunks; desc->chunk_start and q_row_offset are ignored. The selected indices
  * go to the host array selected_out[t]. Workspace: at least
- * chunk_attn_workspace_size(desc, CA_OP_SPARSE_BWD) bytes (CA_OP_BWD_DS for the
- * dS hand-over). */
+ * chunk_attn_workspace_size(desc, CA_OP_BWD) bytes; CA_OP_SPARSE_BWD's size
+ * (two slots of row statistics) saves a launch per chunk, CA_OP_BWD_DS's selects
+ * the dS hand-over. */
 int sparse_chunk_bwd(const chunk_attn_desc* desc, int32_t seq_len, int32_t t, uint64_t seed,
                      const void* q, const void* k, const void* v, const void* o,
                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
@@ -189,9 +194,9 @@ int chunked_fwd_sweep(const chunk_attn_desc* desc, int32_t seq_len, const void* 
 /* chunked_bwd_sweep: chunk_attn_bwd of every chunk, descending, with
  * grad_scale. dq rows [0, seq_len) are OVERWRITTEN; dk_acc and dv_acc rows
  * [0, seq_len) are INCREMENTED by the full gradient (zero them first for the
- * gradient alone). Workspace as for sparse_chunk_bwd: at least
- * chunk_attn_workspace_size(desc, CA_OP_SPARSE_BWD) bytes, CA_OP_BWD_DS for the
- * dS hand-over. Errors as for sparse_chunk_bwd. */
+ * gradient alone). Workspace as for sparse_chunk_bwd (at least the CA_OP_BWD
+ * size; the CA_OP_SPARSE_BWD size saves a launch per chunk; CA_OP_BWD_DS
+ * selects the dS hand-over). Errors as for sparse_chunk_bwd. */
 int chunked_bwd_sweep(const chunk_attn_desc* desc, int32_t seq_len, const void* q, const void* k,
                       const void* v, const void* o, const float* lse, const void* dout, float grad_scale,
                       float* dq, float* dk_acc, float* dv_acc, void* ws, size_t ws_bytes, void* stream);

@@ -93,6 +93,17 @@ size_t delta_bytes(const chunk_attn_desc* d) {
   return round_up(ca::bwd_ws_bytes((size_t)d->batch * d->n_q_heads * d->chunk_len));
 }
 
+// The whole-sequence drivers keep two slots of row statistics when the
+// workspace holds both and is not a dS hand-over workspace (CA_OP_BWD_DS):
+// each chunk's launch then also computes the next chunk's statistics, and no
+// chunk needs a launch of its own for them.
+bool two_stat_slots(const chunk_attn_desc* d, size_t ws_bytes) {
+  const size_t slot = delta_bytes(d);
+  if (ws_bytes < 2 * slot) return false;
+  return !(d->dtype == CA_BF16 &&
+           ws_bytes >= slot + round_up(ca::bwd_ds_bytes(d->batch, d->n_q_heads, d->chunk_len, d->kv_capacity)));
+}
+
 int check_ptrs(std::initializer_list<const void*> ps) {
   for (const void* p : ps) {
     if (!p) return fail(CA_ERR_NULL, "a tensor pointer is NULL");
@@ -227,8 +238,8 @@ size_t chunk_attn_workspace_size(const chunk_attn_desc* d, int32_t op) {
   switch (op) {
     case CA_OP_FWD: return 0;
     case CA_OP_BWD:
-    case CA_OP_SPARSE_BWD:
     case CA_OP_BWD_MIN: return delta_bytes(d);  // the chunk's row statistics only
+    case CA_OP_SPARSE_BWD: return 2 * delta_bytes(d);  // this chunk's and the next one's
     case CA_OP_BWD_DS:
       // plus room for the dS^T blocks of any chunk of up to chunk_len rows
       // whose prefix fits kv_capacity (bf16)
@@ -387,12 +398,22 @@ int sparse_chunk_bwd(const chunk_attn_desc* d, int32_t seq_len, int32_t t, uint6
   if (e != hipSuccess) return hip_fail(e, "sparse_chunk_bwd zero");
 
   ca::Shape s = shape_of(d);
+  const bool two = two_stat_slots(d, ws_bytes);
+  const size_t slot = delta_bytes(d);
+  auto slot_of = [&](int32_t idx) { return (float*)((char*)ws + (two && (t - 1 - idx) % 2 ? slot : 0)); };
   for (int32_t idx = t - 1; idx >= 0; --idx) {
     const int32_t i = sel[idx];
     s.start = i * C;
     s.q_off = i * C;
     s.len = std::min(C, seq_len - i * C);
-    e = ca::launch_bwd(s, q, k, v, o, lse, dout, gamma, dq, dk, dv, (float*)ws, ws_bytes, st);
+    ca::NextStats nx;
+    if (two && idx > 0) {
+      nx.q_off = sel[idx - 1] * C;
+      nx.len = std::min(C, seq_len - nx.q_off);
+      nx.ws = slot_of(idx - 1);
+    }
+    e = ca::launch_bwd(s, q, k, v, o, lse, dout, gamma, dq, dk, dv, slot_of(idx), two ? slot : ws_bytes, st,
+                       two && idx < t - 1, nx);
     if (e != hipSuccess) return hip_fail(e, "sparse_chunk_bwd chunk launch");
   }
   std::memcpy(selected_out, sel.data(), sizeof(int32_t) * t);
@@ -431,11 +452,20 @@ int chunked_bwd_sweep(const chunk_attn_desc* d, int32_t seq_len, const void* q, 
   const int32_t C = d->chunk_len;
   const int32_t n = (int32_t)(((int64_t)seq_len + C - 1) / C);
   ca::Shape s = shape_of(d);
+  const bool two = two_stat_slots(d, ws_bytes);
+  const size_t slot = delta_bytes(d);
+  auto slot_of = [&](int32_t i) { return (float*)((char*)ws + (two && (n - 1 - i) % 2 ? slot : 0)); };
   for (int32_t i = n - 1; i >= 0; --i) {  // descending, as SeCO's backward
     s.start = s.q_off = i * C;
     s.len = std::min(C, seq_len - i * C);
-    hipError_t e = ca::launch_bwd(s, q, k, v, o, lse, dout, grad_scale, dq, dk_acc, dv_acc, (float*)ws, ws_bytes,
-                                  (hipStream_t)stream);
+    ca::NextStats nx;
+    if (two && i > 0) {
+      nx.q_off = (i - 1) * C;
+      nx.len = std::min(C, seq_len - nx.q_off);
+      nx.ws = slot_of(i - 1);
+    }
+    hipError_t e = ca::launch_bwd(s, q, k, v, o, lse, dout, grad_scale, dq, dk_acc, dv_acc, slot_of(i),
+                                  two ? slot : ws_bytes, (hipStream_t)stream, two && i < n - 1, nx);
     if (e != hipSuccess) return hip_fail(e, "chunked_bwd_sweep chunk launch");
   }
   return CA_OK;

@@ -42,6 +42,7 @@
 #include "device_common.h"
 #include "timed_launch.h"
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -322,31 +323,50 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
 }
 
 // ----------------------------------------------------------------------------
-// delta_r = sum_c dO_rc O_rc (float32) and lse2_r = LSE_r * log2(e) for the
-// chunk's rows, both [batch*hq][len]; LPR lanes share one row.
+// delta_r = sum_c dO_rc O_rc (float32) and lse2_r = LSE_r * log2(e) for a
+// chunk's rows, both [batch*hq][len]; LPR lanes share one row. Workgroup
+// `block` of `nblocks` (THREADS threads each) takes every nblocks-th group of
+// THREADS / LPR rows.
 // ----------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const T* o, const T* dout, const float* lse, float* delta,
-                                                    float* lse2, int q_cap, int q_off, int len, int rows) {
+struct StatsArgs {
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  float* lse2;
+  int q_cap, q_off, len, rows;
+  int blocks;  // workgroups of a fused launch that compute these (0: none)
+};
+
+template <typename T, int D, int THREADS>
+__device__ __forceinline__ void row_stats(const StatsArgs& a, int block, int nblocks) {
   using V = typename Elt<T>::vec;
-  constexpr int VEC = Elt<T>::VEC, LPR = D / VEC;
-  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = gid / LPR, sub = gid % LPR;
-  float acc = 0.f;
-  size_t qrow = 0;
-  if (row < rows) {
-    const int bh = row / len, r = row % len;
-    qrow = (size_t)bh * q_cap + q_off + r;
-    const V a = *(const V*)(o + qrow * D + sub * VEC), c = *(const V*)(dout + qrow * D + sub * VEC);
+  constexpr int VEC = Elt<T>::VEC, LPR = D / VEC, RPB = THREADS / LPR;
+  const int sub = threadIdx.x % LPR;
+  for (int row0 = block * RPB; row0 < a.rows; row0 += nblocks * RPB) {
+    const int row = row0 + threadIdx.x / LPR;
+    float acc = 0.f;
+    size_t qrow = 0;
+    if (row < a.rows) {
+      const int bh = row / a.len, r = row % a.len;
+      qrow = (size_t)bh * a.q_cap + a.q_off + r;
+      const V x = *(const V*)((const T*)a.o + qrow * D + sub * VEC);
+      const V y = *(const V*)((const T*)a.dout + qrow * D + sub * VEC);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc += (float)a[e] * (float)c[e];
-  }
+      for (int e = 0; e < VEC; ++e) acc += (float)x[e] * (float)y[e];
+    }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && sub == 0) {
-    delta[row] = acc;
-    lse2[row] = lse[qrow] * kLog2e;
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (row < a.rows && sub == 0) {
+      a.delta[row] = acc;
+      a.lse2[row] = a.lse[qrow] * kLog2e;
+    }
   }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void delta_kernel(StatsArgs a) {
+  row_stats<T, D, 256>(a, blockIdx.x, gridDim.x);
 }
 
 // ----------------------------------------------------------------------------
@@ -884,7 +904,9 @@ union LdsUnion {
 };
 
 // The chunk's dQ (recomputing dS) and dK/dV passes in one launch: a sub-grid
-// of n_dq query-tile workgroups and one of n_kv key-tile workgroups. The
+// of n_dq query-tile workgroups and one of n_kv key-tile workgroups (and,
+// last, next.blocks workgroups computing another chunk's row statistics, which
+// nothing in this launch reads). The
 // sub-grid whose longest workgroup carries more work goes first, and the
 // other's workgroups fill the compute units it leaves idle in its last round.
 // Both read the same inputs and write disjoint outputs (dQ rows; dK/dV keys,
@@ -893,11 +915,17 @@ union LdsUnion {
 // sub-grid is padded to a multiple of the 8 XCDs (padding workgroups exit at
 // once) so that each keeps the XCD-aware order of its own grid.
 template <typename T, int D, int NQT, int BK, int NW, int NKT, int BQ, int NP>
-__global__ __launch_bounds__(2 * NW * 64) void bwd_kernel(BwdParams p, int n_dq, int n_kv, int dq_first) {
+__global__ __launch_bounds__(2 * NW * 64) void bwd_kernel(BwdParams p, int n_dq, int n_kv, int dq_first,
+                                                          StatsArgs next) {
   static_assert(NW == NP, "one workgroup shape for both passes");
   __shared__ LdsUnion<DqLds<T, D, BK>, DkdvLds<T, D, NKT, BQ, NP>> sm;
   const int first_pad = ((dq_first ? n_dq : n_kv) + 7) / 8 * 8;
+  const int second = dq_first ? n_kv : n_dq;
   int blk = blockIdx.x;
+  if (blk >= first_pad + second) {  // row statistics of the driver's next chunk
+    row_stats<T, D, 2 * NW * 64>(next, blk - first_pad - second, next.blocks);
+    return;
+  }
   const bool in_first = blk < first_pad;
   if (!in_first) blk -= first_pad;
   const bool is_dq = in_first == (dq_first != 0);
@@ -1149,7 +1177,7 @@ hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v,
 template <typename T, int D>
 hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
-                    float* ws, size_t ws_bytes, hipStream_t st) {
+                    float* ws, size_t ws_bytes, hipStream_t st, bool stats_ready, const NextStats& next) {
   using C = Cfg<T, D>;
   constexpr int LPR = D / Elt<T>::VEC;
   const int rows = s.batch * s.hq * s.len;
@@ -1157,13 +1185,20 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   // dS^T goes through the workspace when it has room (bf16 only).
   const size_t ds_need = bwd_ds_bytes(s.batch, s.hq, s.len, L);
   const bool use_ds = sizeof(T) == 2 && ws_bytes >= bwd_ws_base(rows) + ds_need;
-  const int threads = rows * LPR;
-  float* delta = ws;
-  float* lse2 = ws + bwd_ws_stride(rows);
-  CA_LAUNCH(CA_KERNEL_DELTA, (delta_kernel<T, D>), dim3((threads + 255) / 256), dim3(256), 0, st, (const T*)o,
-                     (const T*)dout, lse, delta, lse2, s.q_cap, s.q_off, s.len, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  auto stats_of = [&](int q_off, int len, float* w) {
+    const int r = s.batch * s.hq * len;
+    return StatsArgs{o, dout, lse, w, w + bwd_ws_stride(r), s.q_cap, q_off, len, r, 0};
+  };
+  auto stats_launch = [&](const StatsArgs& a) {
+    CA_LAUNCH(CA_KERNEL_DELTA, (delta_kernel<T, D>), dim3((a.rows * LPR + 255) / 256), dim3(256), 0, st, a);
+    return hipGetLastError();
+  };
+  const StatsArgs cur = stats_of(s.q_off, s.len, ws);
+  hipError_t e = hipSuccess;
+  if (!stats_ready && (e = stats_launch(cur)) != hipSuccess) return e;
+  StatsArgs nx = stats_of(next.q_off, next.len, next.ws);
+  float* const delta = cur.delta;
+  float* const lse2 = cur.lse2;
   BwdParams p{q,     k,     v,       dout,     lse,     delta,   lse2,  dq,   dk,
               dv,    s.hq,  s.hkv,   s.q_cap,  s.kv_cap, s.q_off, s.start, s.len,
               exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs,
@@ -1181,9 +1216,14 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
     const int n_dq = (s.len + BQD - 1) / BQD * s.hq * s.batch;
     const int n_kv = tiles * heads;
     const int dq_first = 3LL * L >= 4LL * (s.hq / s.hkv) * s.len ? 1 : 0;
-    const int grid = ((dq_first ? n_dq : n_kv) + 7) / 8 * 8 + (dq_first ? n_kv : n_dq);
+    // The next chunk's row statistics, if asked for, go to at most one
+    // workgroup per compute unit at the end of the grid, where they fill the
+    // units the last round leaves idle.
+    constexpr int RPB = 2 * C::DQ_NW * 64 / LPR;
+    if (next.len > 0) nx.blocks = std::min((nx.rows + RPB - 1) / RPB, device_cus());
+    const int grid = ((dq_first ? n_dq : n_kv) + 7) / 8 * 8 + (dq_first ? n_kv : n_dq) + nx.blocks;
     CA_LAUNCH(CA_KERNEL_BWD, (bwd_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW, C::KV_NKT, C::KV_BQ, C::KV_NP>),
-              dim3(grid), dim3(2 * C::DQ_NW * 64), 0, st, p, n_dq, n_kv, dq_first);
+              dim3(grid), dim3(2 * C::DQ_NW * 64), 0, st, p, n_dq, n_kv, dq_first, nx);
     return hipGetLastError();
   }
   if constexpr (sizeof(T) == 2) {
@@ -1224,6 +1264,8 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
     } else {
       CA_LAUNCH(CA_KERNEL_DQ, (dqs_kernel<D, 2, 64, 4>), dim3(p.ds_nqb * s.hq * s.batch), dim3(2 * 4 * 64), 0, st, p);
     }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (next.len > 0) return stats_launch(nx);
   }
   return hipGetLastError();
 }
@@ -1242,13 +1284,15 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k, const void* 
 
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, float gs, float* dq, float* dk, float* dv,
-                      float* ws, size_t ws_bytes, hipStream_t st) {
+                      float* ws, size_t ws_bytes, hipStream_t st, bool stats_ready, const NextStats& next) {
   if (s.dtype == CA_BF16) {
-    return s.head_dim == 128 ? bwd_impl<bf16, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st)
-                             : bwd_impl<bf16, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st);
+    return s.head_dim == 128
+               ? bwd_impl<bf16, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st, stats_ready, next)
+               : bwd_impl<bf16, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st, stats_ready, next);
   }
-  return s.head_dim == 128 ? bwd_impl<float, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st)
-                           : bwd_impl<float, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st);
+  return s.head_dim == 128
+             ? bwd_impl<float, 128>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st, stats_ready, next)
+             : bwd_impl<float, 64>(s, q, k, v, o, lse, dout, gs, dq, dk, dv, ws, ws_bytes, st, stats_ready, next);
 }
 
 hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads, int acc_cap, int src_cap,

@@ -35,13 +35,25 @@ inline size_t bwd_ds_bytes(size_t batch, size_t hq, size_t len, size_t keys) {
          kDsCols * 2;
 }
 
-// Backward: row statistics into the workspace, then dq (overwritten, times
+// Row statistics of another chunk of the same tensors (rows [q_off, q_off +
+// len) of o, dout and lse), written to `ws` laid out as the required part of
+// a backward workspace for that chunk; len == 0: none.
+struct NextStats {
+  int q_off = 0, len = 0;
+  float* ws = nullptr;
+};
+
+// Backward: row statistics into the workspace (unless stats_ready: a previous
+// launch on the stream put them there), then dq (overwritten, times
 // grad_scale) and the dk/dv accumulators (incremented). ws_bytes decides the
 // dQ pass: with room for the dS^T blocks after the required part (bf16), the
-// dK/dV pass stores dS and dQ = dS K streams it; otherwise dQ recomputes dS.
+// dK/dV pass stores dS and dQ = dS K streams it; otherwise dQ recomputes dS,
+// in the same launch as dK/dV. `next`, if given, is computed by the same
+// launch (by a launch of its own on the dS path).
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, float grad_scale,
-                      float* dq, float* dk, float* dv, float* ws, size_t ws_bytes, hipStream_t st);
+                      float* dq, float* dk, float* dv, float* ws, size_t ws_bytes, hipStream_t st,
+                      bool stats_ready = false, const NextStats& next = NextStats{});
 
 // Allocation-free backward: the row statistics live in a static device array
 // of kScratchBytes per device (attention.hip). scratch_address() returns the

@@ -10,7 +10,7 @@ hipError_t launch_fwd(const Shape&, const void*, const void*, const void*, void*
   return hipErrorNotSupported;
 }
 hipError_t launch_bwd(const Shape&, const void*, const void*, const void*, const void*, const float*, const void*,
-                      float, float*, float*, float*, float*, size_t, hipStream_t) {
+                      float, float*, float*, float*, float*, size_t, hipStream_t, bool, const NextStats&) {
   return hipErrorNotSupported;
 }
 hipError_t scratch_address(void**) { return hipErrorNotSupported; }

@@ -127,7 +127,7 @@ def test_workspace_sizes_cover_the_ds_blocks():
         lo = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD)
         full = lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD_DS)
         assert full - lo == d.batch * d.n_q_heads * rows * keys * 2
-        assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_SPARSE_BWD) == lo
+        assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_SPARSE_BWD) == 2 * lo  # two slots
         assert lib.chunk_attn_workspace_size(ctypes.byref(d), b.CA_OP_BWD_MIN) == lo
         f32 = desc(dtype=b.CA_F32, **kw)
         assert (lib.chunk_attn_workspace_size(ctypes.byref(f32), b.CA_OP_BWD_DS)
@@ -135,17 +135,18 @@ def test_workspace_sizes_cover_the_ds_blocks():
 
 
 def test_backward_workspace_is_bounded_by_the_chunk():
-    # The backward's workspace (CA_OP_BWD, CA_OP_SPARSE_BWD) depends only on the
-    # chunk's rows (8 bytes per row of batch * Hq * C, rounded up), not on the
-    # sequence length or the capacities. 32B layer (Hq 64, C 2048): 1 MiB at
-    # T = 32768 and at T = 131072.
-    sizes = set()
+    # The backward's workspace (CA_OP_BWD; CA_OP_SPARSE_BWD holds two such
+    # slots) depends only on the chunk's rows (8 bytes per row of batch * Hq *
+    # C, rounded up), not on the sequence length or the capacities. 32B layer
+    # (Hq 64, C 2048): 1 MiB (2 MiB) at T = 32768 and at T = 131072.
+    sizes = {b.CA_OP_BWD: set(), b.CA_OP_SPARSE_BWD: set()}
     for T in (32768, 131072):
         d = desc(n_q_heads=64, n_kv_heads=8, q_capacity=T, kv_capacity=T, chunk_start=0, chunk_len=2048)
-        for op in (b.CA_OP_BWD, b.CA_OP_SPARSE_BWD):
-            sizes.add(lib.chunk_attn_workspace_size(ctypes.byref(d), op))
-    assert sizes == {2 * 64 * 2048 * 4}
-    assert max(sizes) <= 256 << 20
+        for op in sizes:
+            sizes[op].add(lib.chunk_attn_workspace_size(ctypes.byref(d), op))
+    assert sizes[b.CA_OP_BWD] == {2 * 64 * 2048 * 4}
+    assert sizes[b.CA_OP_SPARSE_BWD] == {2 * 2 * 64 * 2048 * 4}
+    assert max(sizes[b.CA_OP_SPARSE_BWD]) <= 256 << 20
 
 
 def test_accumulate_errors():

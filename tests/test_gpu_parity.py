@@ -151,16 +151,21 @@ def test_bf16_tile_and_tail_cases(T, C, Hq, Hkv, d, spike, scale):
     check_dense(custom("bf16_var", T, C, Hq, Hkv, d, "bf16", seed=T * 3 + C, scale=scale, spike=spike))
 
 
+@pytest.mark.parametrize("ds", [False, True])
 @pytest.mark.parametrize("d", [128, 64])
-def test_bf16_dkdv_launch_plan_with_six_kv_heads(d):
-    # Six kv heads: the 2048-key prefix of chunk 0 runs on half-size key tiles
-    # (192 workgroups), chunk 1 on full tiles, and chunk 2 (48 full tiles per
-    # head, 288 workgroups) on 42 full tiles per head followed by a launch of
-    # half-size tiles from key 5376 on: the split falls inside the chunk's own
-    # diagonal block and off any multiple of the chunk size. 12 query heads
-    # also put the forward and the dQ pass on 64-row tiles.
+def test_bf16_dkdv_launch_plan_with_six_kv_heads(d, ds):
+    # Six kv heads. The default backward launches dQ and dK/dV together: 192
+    # dQ workgroups and 96/192/288 key-tile workgroups, dK/dV first in chunks 0
+    # and 1 and dQ first in chunk 2 (sub-grids that are not multiples of the 8
+    # XCDs come up in the randomized cases). With the dS hand-over the dK/dV
+    # pass runs alone: the 2048-key
+    # prefix of chunk 0 on half-size key tiles (192 workgroups), chunk 1 on
+    # full tiles, and chunk 2 (48 full tiles per head, 288 workgroups) on 42
+    # full tiles per head followed by a launch of half-size tiles from key 5376
+    # on, a split inside the chunk's own diagonal block and off any multiple of
+    # the chunk size. 12 query heads also put the forward on 64-row tiles.
     wl = custom("bf16_plan6", 6144, 2048, 12, 6, d, "bf16", seed=61 + d, spike=1)
-    check_dense(wl, heads=[0, 1, 10, 11])
+    check_dense(wl, heads=[0, 1, 10, 11], ds=ds)
 
 
 @pytest.mark.parametrize("T,C,Hq,Hkv,d,spike,scale", [
@@ -310,6 +315,53 @@ def test_sweeps_equal_per_chunk_calls(dtype, ds):
     bar = 1e-5 if dtype == "f32" else 2e-2
     for got, ref in zip(outs[0][2:], (rdq, rdk, rdv)):
         assert rel_inf(got.double().numpy(), 0.5 * ref) <= bar
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_driver_stat_slots(dtype):
+    # With a CA_OP_SPARSE_BWD workspace (two slots of row statistics) each
+    # chunk's launch of the drivers also computes the next chunk's statistics;
+    # with only a CA_OP_BWD one they get a launch of their own per chunk. Both
+    # bitwise equal, for the dense sweep and for the sparse driver (t < k,
+    # ragged last chunk).
+    B = binding()
+    wl = custom("slots", 1000, 192, 4, 2, 128, dtype, seed=17, spike=1)
+    inp = W.make_inputs(wl)
+    t = to_dev(inp)
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    B.chunked_forward(q, k, v, o, lse, chunk=192)
+    desc = B.make_desc(q, k, chunk_start=0, chunk_len=192)
+    one = B.chunk_attn_workspace_size(desc, B.CA_OP_BWD)
+    two = B.chunk_attn_workspace_size(desc, B.CA_OP_SPARSE_BWD)
+    assert two == 2 * one
+    note(f"[case] driver stat slots {dtype}: {one} / {two} bytes")
+    outs = {}
+    for nbytes in (one, two):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        res = []
+        dq = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=DEV)
+        dv = torch.zeros(v.shape, dtype=torch.float32, device=DEV)
+        B.chunked_backward(q, k, v, o, lse, do, dq, dk, dv, chunk=192, grad_scale=0.75, workspace=ws)
+        res += [dq.clone(), dk.clone(), dv.clone()]
+        sel = B.sparse_chunk_bwd(q, k, v, o, lse, do, dq, dk, dv, seq_len=1000, chunk=192, t=3, seed=5,
+                                 workspace=ws)
+        torch.cuda.synchronize()
+        res += [dq.cpu(), dk.cpu(), dv.cpu()]
+        outs[nbytes] = ([x.cpu() for x in res], sel)
+    assert outs[one][1] == outs[two][1] == select_chunks(wl.n_chunks, 3, 5)
+    for a, b_ in zip(outs[one][0], outs[two][0]):
+        assert torch.equal(a, b_)
+    f = inp.f64
+    rdq, rdk, rdv = A.backward(f["q"], f["k"], f["v"], f["do"], 1.0)
+    bar = 1e-5 if dtype == "f32" else 2e-2
+    for got, ref in zip(outs[two][0][:3], (rdq, rdk, rdv)):
+        assert rel_inf(got.double().numpy(), 0.75 * ref) <= bar
+    sdq, sdk, sdv = A.sparse_backward(f["q"], f["k"], f["v"], f["do"], 1.0, 192, outs[two][1], wl.n_chunks)
+    for got, ref in zip(outs[two][0][3:], (sdq, sdk, sdv)):
+        assert rel_inf(got.double().numpy(), ref) <= bar
 
 
 @pytest.mark.parametrize("ds", [False, True])
