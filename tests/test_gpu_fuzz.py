@@ -6,8 +6,9 @@ included), a signed softmax scale, whether keys get the low-rank spike, which
 dQ pass the backward takes, and one of three drivers: the whole-sequence
 sweeps, per-chunk calls whose query-side tensors hold only the current chunk
 (q_row_offset 0, q_capacity = the chunk's rows), or the sparse (SpaCO)
-backward over t of the k chunks with a drawn t and selection seed. Every element of O, LSE, dQ, dK and dV is compared at the parity bar:
-1e-5 (float32) / 2e-2 (bf16), relative to the tensor's largest magnitude; LSE
+backward over t of the k chunks with a drawn t and selection seed. Every
+element of O, LSE, dQ, dK and dV is compared at the parity bar: 1e-5
+(float32) / 2e-2 (bf16), relative to the tensor's largest magnitude; LSE
 relative to max(1, its largest magnitude), since float32 holds LSE to a relative
 precision and the drawn scales and key spikes put it anywhere from 1 to ~20.
 """
@@ -111,7 +112,8 @@ def test_random_tiles_and_tails(i):
         assert sel == select_chunks(wl.n_chunks, sparse[0], sparse[1])
         rdq, rdk, rdv = A.sparse_backward(f["q"], f["k"], f["v"], f["do"], wl.softmax_scale, wl.chunk, sel,
                                           wl.n_chunks)
-    errs = {"o": rel_inf(got["o"], ro), "lse": float(np.abs(got["lse"] - rlse).max() / max(1.0, np.abs(rlse).max())),
+    lse_err = float(np.abs(got["lse"] - rlse).max() / max(1.0, np.abs(rlse).max()))
+    errs = {"o": rel_inf(got["o"], ro), "lse": lse_err,
             "dq": rel_inf(got["dq"], rdq), "dk": rel_inf(got["dk"], rdk), "dv": rel_inf(got["dv"], rdv)}
     print(f"          errors {errs}", flush=True)
     bar = 1e-5 if wl.dtype == "f32" else 2e-2
