@@ -240,20 +240,31 @@ typedef __attribute__((address_space(3))) void lds_void;
 // weight (keys past the prefix are causally masked).
 // SRC_STRIDE: elements between consecutive source rows (a tile may be a
 // column slice of a wider row-major matrix).
+// The loads use the buffer form of the instruction. The compiler tracks that
+// form on the vector-memory counter alone; the global form is a flat access,
+// and while one is in flight the compiler waits for every outstanding LDS
+// read before each use, so no read can run ahead of the products. The buffer
+// starts at the first row the tile reads and spans only the rows it reads,
+// so offsets stay small for a head of any length.
 template <typename T, int ROWS, int D, int NW, int SRC_STRIDE = D>
 __device__ __forceinline__ void stage_tile(T* lds, const T* head, int row0, int limit, int wave, int lane) {
   using Lt = SwzLay<T, D>;
   constexpr int CH = Lt::CH, RPI = 64 / CH, PER_WAVE = ROWS / NW;
   static_assert(CH <= 64 && PER_WAVE % RPI == 0, "tile rows per wave must fill whole instructions");
+  static_assert((long long)ROWS * SRC_STRIDE * sizeof(T) < (1LL << 31), "tile span fits a 32-bit offset");
 #if defined(__HIP_DEVICE_COMPILE__)  // the LDS-loading builtin exists only in the device pass
+  const int b0 = min(row0, limit - 1);
+  const int nrec = (min(row0 + ROWS, limit) - b0) * SRC_STRIDE * (int)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(head + (size_t)b0 * SRC_STRIDE), (short)0, nrec, 0x00020000);
   const int rl = lane / CH, slot = lane % CH;
 #pragma unroll
   for (int i = 0; i < PER_WAVE / RPI; ++i) {
     const int rb = wave * PER_WAVE + i * RPI;  // wave-uniform first row of this instruction
     const int r = rb + rl;
     const int c = slot ^ Lt::swz(r);
-    const T* src = head + (size_t)min(row0 + r, limit - 1) * SRC_STRIDE + c * Lt::EPC;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + rb * D), 16, 0, 0);
+    const int voff = ((min(row0 + r, limit - 1) - b0) * SRC_STRIDE + c * Lt::EPC) * (int)sizeof(T);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + rb * D), 16, voff, 0, 0, 0);
   }
 #endif
 }
