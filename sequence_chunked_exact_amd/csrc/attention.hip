@@ -75,18 +75,22 @@ hipError_t scratch_address(void** ptr) {
 namespace {
 
 // ----------------------------------------------------------------------------
-// Forward. 1-D grid over (batch, q head, query tile). A workgroup has two
+// Forward. 1-D grid over (batch, q head, query tile). A workgroup has NG
 // groups of NW waves; wave w of each group owns the same NQT*16 query rows
-// (held as B fragments of S^T = K Q^T), and group 0 takes the even key tiles
-// while group 1 takes the odd ones, so each SIMD runs two waves (one's LDS
-// reads and softmax overlap the other's MFMAs) without more LDS traffic per
-// product. Pairs of key tiles stream into double-buffered LDS by direct
-// global->LDS loads issued one pair ahead; the two buffers are separate
-// arrays named statically (the loop is unrolled by two), which lets the
-// compiler see that reads of one buffer do not depend on the loads into the
-// other. At the end group 1 hands its running maximum, row sums and O^T to
-// group 0 through LDS, which merges and stores. Tiles past a wave's rows are
-// skipped; only diagonal tiles are masked.
+// (held as B fragments of S^T = K Q^T), and group g takes key tiles NG i + g,
+// so each SIMD runs two waves (one's LDS reads and softmax overlap the
+// other's MFMAs) without more LDS traffic per product. Long chunks run two
+// groups of four waves on 64-key tiles; a chunk too short to give every
+// compute unit a 128-row tile runs 64-row tiles as four groups of two waves
+// on 32-key tiles, which keeps 32 rows per wave (16-row waves would read
+// every tile from LDS twice as often per product). The NG tiles of a step
+// stream into double-buffered LDS by direct global->LDS loads issued one step
+// ahead; the two buffers are separate arrays named statically (the loop is
+// unrolled by two), which lets the compiler see that reads of one buffer do
+// not depend on the loads into the other. At the end groups 1..NG-1 in turn
+// hand their running maximum, row sums and O^T to group 0 through LDS, which
+// merges and stores. Tiles past a wave's rows are skipped; only diagonal
+// tiles are masked.
 // ----------------------------------------------------------------------------
 struct FwdParams {
   const void* q;
@@ -99,19 +103,19 @@ struct FwdParams {
   int neg;   // softmax scale < 0: queries enter S negated
 };
 
-template <typename T, int D, int NQT, int BK, int NW>
-__global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
+template <typename T, int D, int NQT, int BK, int NW, int NG = 2>
+__global__ __launch_bounds__(NG * NW * 64) void fwd_kernel(FwdParams p) {
   using E = Elt<T>;
   using frag = typename E::frag;
   using Lt = SwzLay<T, D>;
   constexpr int BQ = NW * NQT * 16;
   constexpr int DK = D / 32, MD = D / 16, MK = BK / 16, KB2 = BK / 32;
-  // Pair i uses buffer i & 1: K tiles 2i, 2i+1 in Kb<i&1> (rows [0, BK) and
-  // [BK, 2BK)), V tiles likewise in Vb<i&1>.
-  __shared__ __attribute__((aligned(16))) T Kb0[2 * BK * D];
-  __shared__ __attribute__((aligned(16))) T Vb0[2 * BK * D];
-  __shared__ __attribute__((aligned(16))) T Kb1[2 * BK * D];
-  __shared__ __attribute__((aligned(16))) T Vb1[2 * BK * D];
+  // Step i uses buffer i & 1: K tiles NG i .. NG i + NG - 1 in Kb<i&1> (tile
+  // NG i + g at rows [g BK, (g + 1) BK)), V tiles likewise in Vb<i&1>.
+  __shared__ __attribute__((aligned(16))) T Kb0[NG * BK * D];
+  __shared__ __attribute__((aligned(16))) T Vb0[NG * BK * D];
+  __shared__ __attribute__((aligned(16))) T Kb1[NG * BK * D];
+  __shared__ __attribute__((aligned(16))) T Vb1[NG * BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   const int L = p.start + p.len;
   const int r0 = qt * BQ;
   const int n_tiles = (p.start + min(r0 + BQ, p.len) - 1) / BK + 1;
-  const int n_pairs = (n_tiles + 1) / 2;
+  const int n_pairs = (n_tiles + NG - 1) / NG;
   const int wr0 = r0 + wq * NQT * 16;
   const bool active = wr0 < p.len;
   const int wq_lo = p.start + wr0;
@@ -136,8 +140,8 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   const float c2 = p.c2;
 
   auto stage = [&](T* kd, T* vd, int pair) {
-    stage_tile<T, 2 * BK, D, 2 * NW>(kd, K, 2 * pair * BK, L, wave, lane);
-    stage_tile<T, 2 * BK, D, 2 * NW>(vd, V, 2 * pair * BK, L, wave, lane);
+    stage_tile<T, NG * BK, D, NG * NW>(kd, K, NG * pair * BK, L, wave, lane);
+    stage_tile<T, NG * BK, D, NG * NW>(vd, V, NG * pair * BK, L, wave, lane);
   };
   stage(Kb0, Vb0, 0);
 
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   // Pair i from the buffer (Kc, Vc); the next pair streams into (Kn, Vn).
   auto pair_step = [&](int i, const T* Kc, const T* Vc, T* Kn, T* Vn) {
     if (i + 1 < n_pairs) stage(Kn, Vn, i + 1);
-    const int j = 2 * i + grp;  // this group's key tile
+    const int j = NG * i + grp;  // this group's key tile
     const int kb0 = j * BK;
     if (active && j < n_tiles && kb0 <= wq_hi) {
       const T* Kt = Kc + grp * BK * D;
@@ -272,41 +276,49 @@ __global__ __launch_bounds__(2 * NW * 64) void fwd_kernel(FwdParams p) {
   float* xo0 = (float*)Kb0;
   float* xo1 = (float*)Vb0;
   float* xs = (float*)Kb1;
-  if (grp == 1) {
+  for (int src = 1; src < NG; ++src) {  // groups 1 .. NG-1 in turn
+    if (grp == src) {
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-      const size_t slot = (size_t)(nt * NW + wq);
-      xs[(slot * 2 + 0) * 64 + lane] = m2[nt];
-      xs[(slot * 2 + 1) * 64 + lane] = lacc[nt][0];
+      for (int nt = 0; nt < NQT; ++nt) {
+        const size_t slot = (size_t)(nt * NW + wq);
+        xs[(slot * 2 + 0) * 64 + lane] = m2[nt];
+        xs[(slot * 2 + 1) * 64 + lane] = lacc[nt][0];
 #pragma unroll
-      for (int md = 0; md < MD; ++md)
+        for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float* x = md < MD / 2 ? xo0 : xo1;
-          x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane] = oacc[md][nt][e];
-        }
+          for (int e = 0; e < 4; ++e) {
+            float* x = md < MD / 2 ? xo0 : xo1;
+            x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane] = oacc[md][nt][e];
+          }
+      }
     }
+    __syncthreads();
+    if (grp == 0 && active) {
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) {
+        const size_t slot = (size_t)(nt * NW + wq);
+        const float mb = xs[(slot * 2 + 0) * 64 + lane];
+        const float mnew = fmaxf(m2[nt], mb);
+        // group 0's maximum is finite for every visible row (its tile 0 holds
+        // key 0); another group's is -inf where it saw no key of the row
+        const float fa = fexp2(m2[nt] - mnew), fb = mb == -kInf ? 0.f : fexp2(mb - mnew);
+        lacc[nt][0] = lacc[nt][0] * fa + xs[(slot * 2 + 1) * 64 + lane] * fb;
+        m2[nt] = mnew;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float* x = md < MD / 2 ? xo0 : xo1;
+            oacc[md][nt][e] = oacc[md][nt][e] * fa + x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane] * fb;
+          }
+      }
+    }
+    if (src + 1 < NG) __syncthreads();  // the next group overwrites the exchange area
   }
-  __syncthreads();
-  if (grp == 1 || !active) return;
+  if (grp != 0 || !active) return;
   float lrow[NQT];
 #pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    const size_t slot = (size_t)(nt * NW + wq);
-    const float mb = xs[(slot * 2 + 0) * 64 + lane];
-    const float mnew = fmaxf(m2[nt], mb);
-    // both maxima are finite for every visible row: tile 0 (group 0) holds key 0
-    const float fa = fexp2(m2[nt] - mnew), fb = mb == -kInf ? 0.f : fexp2(mb - mnew);
-    lrow[nt] = lacc[nt][0] * fa + xs[(slot * 2 + 1) * 64 + lane] * fb;
-    m2[nt] = mnew;
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float* x = md < MD / 2 ? xo0 : xo1;
-        oacc[md][nt][e] = oacc[md][nt][e] * fa + x[(slot * HALF + (md % (MD / 2)) * 4 + e) * 64 + lane] * fb;
-      }
-  }
+  for (int nt = 0; nt < NQT; ++nt) lrow[nt] = lacc[nt][0];
   T* O = (T*)p.o + ((size_t)(b * p.hq + h) * p.q_cap + p.q_off) * D;
   float* LSE = p.lse + (size_t)(b * p.hq + h) * p.q_cap + p.q_off;
 #pragma unroll
@@ -1163,14 +1175,17 @@ hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v,
   FwdParams p{q,     k,     v,       o,        lse,     s.hq,    s.hkv, s.q_cap, s.kv_cap, s.q_off,
               s.start, s.len, exp2_coef(s.scale), s.scale < 0.f ? 1 : 0};
   // A chunk too short to give every compute unit a 128-row tile (e.g. 500
-  // rows x 32 heads = 128 tiles) runs 64-row tiles, one 16-row tile per wave.
-  if (C::FWD_NQT > 1 && q_tiles<C::FWD_NW, C::FWD_NQT>(s) < device_cus()) {
-    CA_LAUNCH(CA_KERNEL_FWD, (fwd_kernel<T, D, 1, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, 1>(s)),
-                       dim3(2 * C::FWD_NW * 64), 0, st, p);
-  } else {
-    CA_LAUNCH(CA_KERNEL_FWD, (fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, C::FWD_NQT>(s)),
-                       dim3(2 * C::FWD_NW * 64), 0, st, p);
+  // rows x 32 heads = 128 tiles) runs 64-row tiles: four groups of two
+  // 32-row waves on 32-key tiles.
+  if constexpr (C::FWD_NQT > 1) {
+    if (q_tiles<C::FWD_NW, C::FWD_NQT>(s) < device_cus()) {
+      CA_LAUNCH(CA_KERNEL_FWD, (fwd_kernel<T, D, C::FWD_NQT, 32, 2, 4>), dim3(q_tiles<2, C::FWD_NQT>(s)),
+                dim3(4 * 2 * 64), 0, st, p);
+      return hipGetLastError();
+    }
   }
+  CA_LAUNCH(CA_KERNEL_FWD, (fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, C::FWD_NQT>(s)),
+            dim3(2 * C::FWD_NW * 64), 0, st, p);
   return hipGetLastError();
 }
 
