@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(HERE, "libchunk_attn.so")
 
 CA_F32, CA_BF16 = 0, 1
 CA_OP_FWD, CA_OP_BWD, CA_OP_SPARSE_BWD, CA_OP_BWD_MIN, CA_OP_BWD_DS = 0, 1, 2, 3, 4
-KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7, "residual": 8, "head": 9, "head_aux": 10, "bwd": 11}
+KERNELS = {"fwd": 0, "delta": 1, "dkdv": 2, "dq": 3, "accumulate": 4, "zero": 5, "proj": 6, "proj_prep": 7,
+           "residual": 8, "head": 9, "head_aux": 10, "bwd": 11}
 ERRORS = {0: "CA_OK", -1: "CA_ERR_NULL", -2: "CA_ERR_SHAPE", -3: "CA_ERR_DTYPE", -4: "CA_ERR_ALIGN",
           -5: "CA_ERR_WORKSPACE", -6: "CA_ERR_UNSUPPORTED", -7: "CA_ERR_HIP"}
 

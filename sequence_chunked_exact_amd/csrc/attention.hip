@@ -1184,8 +1184,8 @@ hipError_t fwd_impl(const Shape& s, const void* q, const void* k, const void* v,
       return hipGetLastError();
     }
   }
-  CA_LAUNCH(CA_KERNEL_FWD, (fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>), dim3(q_tiles<C::FWD_NW, C::FWD_NQT>(s)),
-            dim3(2 * C::FWD_NW * 64), 0, st, p);
+  CA_LAUNCH(CA_KERNEL_FWD, (fwd_kernel<T, D, C::FWD_NQT, C::FWD_BK, C::FWD_NW>),
+            dim3(q_tiles<C::FWD_NW, C::FWD_NQT>(s)), dim3(2 * C::FWD_NW * 64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1274,8 +1274,8 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.ds_nqb * s.hq * s.batch < cus) {  // short chunk: 64-column workgroups
-      CA_LAUNCH(CA_KERNEL_DQ, (dqs_kernel<D, 1, 64, 4>), dim3(((s.len + 63) / 64) * s.hq * s.batch),
-                dim3(2 * 4 * 64), 0, st, p);
+      CA_LAUNCH(CA_KERNEL_DQ, (dqs_kernel<D, 1, 64, 4>), dim3(((s.len + 63) / 64) * s.hq * s.batch), dim3(2 * 4 * 64),
+                0, st, p);
     } else {
       CA_LAUNCH(CA_KERNEL_DQ, (dqs_kernel<D, 2, 64, 4>), dim3(p.ds_nqb * s.hq * s.batch), dim3(2 * 4 * 64), 0, st, p);
     }
@@ -1316,7 +1316,7 @@ hipError_t launch_accumulate(float* acc, const float* src, int batch, int heads,
   if (total == 0) return hipSuccess;
   const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
   CA_LAUNCH(CA_KERNEL_ACCUMULATE, accumulate_kernel, dim3(blocks), dim3(256), 0, st, acc, src, batch * heads, acc_cap,
-                     src_cap, head_dim / 4, rows, scale);
+            src_cap, head_dim / 4, rows, scale);
   return hipGetLastError();
 }
 

@@ -153,8 +153,8 @@ size_t head_ws_bytes(const HeadShape& s) {
 }
 
 hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hipStream_t st) {
-  CA_LAUNCH(CA_KERNEL_HEAD_AUX, wt_head_kernel, dim3((s.vocab / 64) * (s.d_model / 64)), dim3(256), 0, st, (const bf16*)w,
-                     (bf16*)wt, s.vocab, s.d_model);
+  CA_LAUNCH(CA_KERNEL_HEAD_AUX, wt_head_kernel, dim3((s.vocab / 64) * (s.d_model / 64)), dim3(256), 0, st,
+            (const bf16*)w, (bf16*)wt, s.vocab, s.d_model);
   return hipGetLastError();
 }
 
@@ -238,7 +238,7 @@ hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zer
     const long long n4 = (long long)rows * dm / 4;
     const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
     CA_LAUNCH(CA_KERNEL_HEAD_AUX, splitk_sum_kernel, dim3(blocks), dim3(256), 0, st, part,
-                       dh + ((size_t)b * s.capacity + s0) * dm, S, rows, dm);
+              dh + ((size_t)b * s.capacity + s0) * dm, S, rows, dm);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

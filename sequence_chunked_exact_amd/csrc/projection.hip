@@ -288,8 +288,8 @@ __global__ __launch_bounds__(256) void wt_kernel(WtParams p) {
 
 template <typename T, typename SA, typename SB, bool A_MN, bool B_MN, bool OUT_F32>
 hipError_t gemm_launch(const GemmParams& p, int batch, hipStream_t st) {
-  CA_LAUNCH(CA_KERNEL_PROJ, (gemm_kernel<T, SA, SB, A_MN, B_MN, OUT_F32>), dim3((p.N + 127) / 128, (p.M + 127) / 128, batch),
-                     dim3(256), 0, st, p);
+  CA_LAUNCH(CA_KERNEL_PROJ, (gemm_kernel<T, SA, SB, A_MN, B_MN, OUT_F32>),
+            dim3((p.N + 127) / 128, (p.M + 127) / 128, batch), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 constexpr int kNoSplit = 1 << 30;

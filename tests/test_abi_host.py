@@ -239,7 +239,8 @@ def test_stack_errors():
     assert bwd_(chunks=(ctypes.c_int32 * 3)(0, 8, 5)) == -2   # index out of range
     assert bwd_(chunks=(ctypes.c_int32 * 3)(1, 3, 1)) == -2   # repeated
     assert bwd_(seq_len=2048) == -2                           # past the caches
-    assert bwd_(dd=desc(chunk_len=128, q_capacity=64, n_q_heads=2, n_kv_heads=1, kv_capacity=1024)) == -2  # q_capacity < C
+    # q_capacity < C
+    assert bwd_(dd=desc(chunk_len=128, q_capacity=64, n_q_heads=2, n_kv_heads=1, kv_capacity=1024)) == -2
     lay[1].dwk = None
     assert bwd_() == -1
     assert lib.spaco_stack_forward(ctypes.byref(d), 1024, 2, lay, FAKE, 1024, FAKE, need - 1, None) == -5
