@@ -644,6 +644,10 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
   auto& Ds = sm.Ds;
   auto& stat_s = sm.stat_s;
   auto& Ps = sm.Ps;
+  // Ring-buffer slot of block i, made wave-uniform and opaque to the
+  // compiler: otherwise it strength-reduces i % NB across the loop into one
+  // induction variable per LDS address (two instructions per read).
+  auto slot = [](int i, int nb) { return __builtin_amdgcn_readfirstlane(i % nb); };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -688,9 +692,10 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
   // (The +inf substitution waits until here so that the fetch never waits
   // on its own loads.)
   auto publish = [&](int blk) {
-    qreg.store(Qs[blk % NBQ], tid);
-    dreg.store(Ds[blk % NB], tid);
-    if (tid < 2 * BQ) stat_s[blk % NB][tid] = past ? kInf : stat;
+    const int sq = slot(blk, NBQ), sd = slot(blk, NB);
+    qreg.store(Qs[sq], tid);
+    dreg.store(Ds[sd], tid);
+    if (tid < 2 * BQ) stat_s[sd][tid] = past ? kInf : stat;
   };
 
   // K (P/dV waves, negated for a negative scale) or V (dS/dK waves) rows of
@@ -739,8 +744,9 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
         const int q_lo = p.start + q0, q_hi = p.start + min(q0 + BQ, p.len) - 1;
         qv = next_qt(qv);
         if (wk0 <= q_hi) {
-          const T* A = Qs[it % NBQ];
-          const T* X = Ds[it % NB];
+          const int sd = slot(it, NB);
+          const T* A = Qs[slot(it, NBQ)];
+          const T* X = Ds[sd];
           f32x4 s[MQ][NKT];
 #pragma unroll
           for (int mq = 0; mq < MQ; ++mq)
@@ -756,7 +762,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
             }
 #pragma unroll
           for (int mq = 0; mq < MQ; ++mq) {
-            const f32x4 l4 = *(const f32x4*)&stat_s[it % NB][mq * 16 + 4 * g];
+            const f32x4 l4 = *(const f32x4*)&stat_s[sd][mq * 16 + 4 * g];
 #pragma unroll
             for (int nk = 0; nk < NKT; ++nk)
 #pragma unroll
@@ -777,7 +783,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
 #pragma unroll
             for (int nk = 0; nk < NKT; ++nk) {
               wf[kq][nk] = pack44<T>(s[2 * kq][nk], s[2 * kq + 1][nk]);
-              Ps[it & 1][pair][kq][nk][lane] = wf[kq][nk];
+              Ps[slot(it, 2)][pair][kq][nk][lane] = wf[kq][nk];
             }
 #pragma unroll
           for (int kq = 0; kq < KQ; ++kq)
@@ -802,7 +808,7 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
     frag dsp[KQ][NKT];
     for (int it = 0; it <= iters + 1; ++it) {
       if (have_prev) {  // dK += dS^T Q for block it - 2
-        const T* X = Qs[(it - 2) % NBQ];
+        const T* X = Qs[slot(it - 2, NBQ)];
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq)
 #pragma unroll
@@ -819,7 +825,8 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
         const int q_hi = p.start + min(q0 + BQ, p.len) - 1;
         qv = next_qt(qv);
         if (wk0 <= q_hi) {
-          const T* A = Ds[blk % NB];
+          const int sd = slot(blk, NB);
+          const T* A = Ds[sd];
           f32x4 s[MQ][NKT];
 #pragma unroll
           for (int mq = 0; mq < MQ; ++mq)
@@ -835,11 +842,11 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
             }
 #pragma unroll
           for (int kq = 0; kq < KQ; ++kq) {
-            const f32x4 d4lo = *(const f32x4*)&stat_s[blk % NB][BQ + kq * 32 + 4 * g];
-            const f32x4 d4hi = *(const f32x4*)&stat_s[blk % NB][BQ + kq * 32 + 16 + 4 * g];
+            const f32x4 d4lo = *(const f32x4*)&stat_s[sd][BQ + kq * 32 + 4 * g];
+            const f32x4 d4hi = *(const f32x4*)&stat_s[sd][BQ + kq * 32 + 16 + 4 * g];
 #pragma unroll
             for (int nk = 0; nk < NKT; ++nk) {
-              const frag pf = Ps[blk & 1][pair][kq][nk][lane];
+              const frag pf = Ps[slot(blk, 2)][pair][kq][nk][lane];
               f32x4 lo, hi;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
