@@ -272,11 +272,11 @@ __device__ __forceinline__ void stage_tile(T* lds, const T* head, int row0, int 
 // A [ROWS][D] tile staged through registers: thread tid fetches R rows of
 // one 16-byte column vector and later writes them into a PadLay LDS tile
 // (threads beyond the tile's ROWS * D / VEC vectors fetch a duplicate and
-// store nothing). Rows at or beyond `limit` (>= 1) re-read row limit-1;
-// every consumer gives such rows zero weight (keys past the prefix are
-// causally masked, query rows past the chunk get LSE = +inf). Plain loads
-// into registers let the next tile's fetch overlap the current tile's math
-// without any LDS ordering.
+// store nothing). The loads go through a buffer over the head's first
+// `limit` rows, so rows at or beyond it read as zero (with 32-bit offsets and
+// no clamp per row); every consumer gives such rows zero weight (query rows
+// past the chunk get LSE = +inf). Plain loads into registers let the next
+// tile's fetch overlap the current tile's math without any LDS ordering.
 template <typename T, int ROWS, int D, int NT>
 struct RegTile {
   using V = typename Elt<T>::vec;
@@ -290,9 +290,14 @@ struct RegTile {
 
   __device__ __forceinline__ void load(const T* head, int row0, int limit, int tid) {
     const int dv = tid % NDV, grp = SPARE ? min(tid / NDV, ROWS - 1) : tid / NDV;
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, limit * D * (int)sizeof(T), 0x00020000);
 #pragma unroll
     for (int i = 0; i < R; ++i)
-      r[i] = *(const V*)(head + (size_t)min(row0 + grp * R + i, limit - 1) * D + dv * VEC);
+      r[i] = __builtin_bit_cast(
+          V, __builtin_amdgcn_raw_buffer_load_b128(rsrc, ((row0 + grp * R + i) * D + dv * VEC) * (int)sizeof(T), 0, 0));
+#endif
   }
   __device__ __forceinline__ void store(T* lds, int tid) const {
     const int dv = tid % NDV, grp = tid / NDV;
