@@ -916,44 +916,73 @@ __global__ __launch_bounds__(2 * NP * 64) void dkdv_kernel(BwdParams p) {
   dkdv_body<T, D, NKT, BQ, NP>(p, blockIdx.x, gridDim.x, sm);
 }
 
-template <typename A, typename B>
+template <typename A, typename B, typename C>
 union LdsUnion {
   A a;
   B b;
+  C c;
 };
 
 // The chunk's dQ (recomputing dS) and dK/dV passes in one launch: a sub-grid
-// of n_dq query-tile workgroups and one of n_kv key-tile workgroups (and,
-// last, next.blocks workgroups computing another chunk's row statistics, which
-// nothing in this launch reads). The
-// sub-grid whose longest workgroup carries more work goes first, and the
-// other's workgroups fill the compute units it leaves idle in its last round.
-// Both read the same inputs and write disjoint outputs (dQ rows; dK/dV keys,
-// each owned by one workgroup), so the result does not depend on how their
-// workgroups interleave. Their LDS layouts share one allocation. The first
-// sub-grid is padded to a multiple of the 8 XCDs (padding workgroups exit at
-// once) so that each keeps the XCD-aware order of its own grid.
+// of n_dq query-tile workgroups, one of n_kv key-tile workgroups over keys
+// [0, kv_split) and one of n_kvh half-size key-tile workgroups (NKT = 1) over
+// [kv_split, L), and last, next.blocks workgroups computing another chunk's
+// row statistics, which nothing in this launch reads. The dQ sub-grid goes
+// first or last: first when its longest workgroup carries more work than the
+// longest key tile, so that the key tiles fill the compute units it leaves
+// idle in its last round. All read the same inputs and write disjoint outputs
+// (dQ rows; dK/dV keys, each owned by one workgroup), so the result does not
+// depend on how their workgroups interleave. Their LDS layouts share one
+// allocation. Each sub-grid is padded to a multiple of the 8 XCDs (padding
+// workgroups exit at once) so that each keeps the XCD-aware order of its own
+// grid.
 template <typename T, int D, int NQT, int BK, int NW, int NKT, int BQ, int NP>
-__global__ __launch_bounds__(2 * NW * 64) void bwd_kernel(BwdParams p, int n_dq, int n_kv, int dq_first,
-                                                          StatsArgs next) {
+__global__ __launch_bounds__(2 * NW * 64) void bwd_kernel(BwdParams p, int n_dq, int n_kv, int n_kvh, int kv_split,
+                                                          int dq_first, StatsArgs next) {
   static_assert(NW == NP, "one workgroup shape for both passes");
-  __shared__ LdsUnion<DqLds<T, D, BK>, DkdvLds<T, D, NKT, BQ, NP>> sm;
-  const int first_pad = ((dq_first ? n_dq : n_kv) + 7) / 8 * 8;
-  const int second = dq_first ? n_kv : n_dq;
+  __shared__ LdsUnion<DqLds<T, D, BK>, DkdvLds<T, D, NKT, BQ, NP>, DkdvLds<T, D, 1, BQ, NP>> sm;
+  const int pad_dq = (n_dq + 7) / 8 * 8, pad_kv = (n_kv + 7) / 8 * 8, pad_kvh = (n_kvh + 7) / 8 * 8;
   int blk = blockIdx.x;
-  if (blk >= first_pad + second) {  // row statistics of the driver's next chunk
-    row_stats<T, D, 2 * NW * 64>(next, blk - first_pad - second, next.blocks);
-    return;
-  }
-  const bool in_first = blk < first_pad;
-  if (!in_first) blk -= first_pad;
-  const bool is_dq = in_first == (dq_first != 0);
-  const int nb = is_dq ? n_dq : n_kv;
-  if (blk >= nb) return;
-  if (is_dq) {
-    dq_body<T, D, NQT, BK, NW>(p, blk, nb, sm.a);
+  int kind;  // 0: dQ, 1: key tiles, 2: half-size key tiles, 3: row statistics
+  if (dq_first) {
+    if (blk < pad_dq) {
+      kind = 0;
+    } else if ((blk -= pad_dq) < pad_kv) {
+      kind = 1;
+    } else if ((blk -= pad_kv) < pad_kvh) {
+      kind = 2;
+    } else {
+      blk -= pad_kvh;
+      kind = 3;
+    }
   } else {
-    dkdv_body<T, D, NKT, BQ, NP>(p, blk, nb, sm.b);
+    if (blk < pad_kv) {
+      kind = 1;
+    } else if ((blk -= pad_kv) < pad_kvh) {
+      kind = 2;
+    } else if ((blk -= pad_kvh) < pad_dq) {
+      kind = 0;
+    } else {
+      blk -= pad_dq;
+      kind = 3;
+    }
+  }
+  if (kind == 3) {
+    row_stats<T, D, 2 * NW * 64>(next, blk, next.blocks);
+  } else if (kind == 0) {
+    if (blk < n_dq) dq_body<T, D, NQT, BK, NW>(p, blk, n_dq, sm.a);
+  } else if (kind == 1) {
+    if (blk < n_kv) {
+      BwdParams q = p;
+      q.kv_end = kv_split;
+      dkdv_body<T, D, NKT, BQ, NP>(q, blk, n_kv, sm.b);
+    }
+  } else if constexpr (NKT > 1) {
+    if (blk < n_kvh) {
+      BwdParams q = p;
+      q.kv_first = kv_split;
+      dkdv_body<T, D, 1, BQ, NP>(q, blk, n_kvh, sm.c);
+    }
   }
 }
 
@@ -1236,16 +1265,30 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
     // with four, so the dQ sub-grid goes first once 3 L >= 4 G len.
     constexpr int BQD = C::DQ_NW * C::DQ_NQT * 16;
     const int n_dq = (s.len + BQD - 1) / BQD * s.hq * s.batch;
-    const int n_kv = tiles * heads;
     const int dq_first = 3LL * L >= 4LL * (s.hq / s.hkv) * s.len ? 1 : 0;
+    // Key tiles in whole rounds of one per compute unit; a remainder that
+    // half-size tiles (~3/4 of the time each) cover in one round goes to them.
+    const int cus = device_cus();
+    int tiles_a = tiles, n_kvh = 0;
+    if (C::KV_NKT > 1) {
+      const int ta = tiles * heads / cus * cus / heads;
+      const int nh = (L - ta * BKV + BKV1 - 1) / BKV1 * heads;
+      if (ta < tiles && nh <= cus) {
+        tiles_a = ta;
+        n_kvh = nh;
+      }
+    }
+    const int n_kv = tiles_a * heads;
+    const int kv_split = n_kvh > 0 ? tiles_a * BKV : L;
     // The next chunk's row statistics, if asked for, go to at most one
     // workgroup per compute unit at the end of the grid, where they fill the
     // units the last round leaves idle.
     constexpr int RPB = 2 * C::DQ_NW * 64 / LPR;
-    if (next.len > 0) nx.blocks = std::min((nx.rows + RPB - 1) / RPB, device_cus());
-    const int grid = ((dq_first ? n_dq : n_kv) + 7) / 8 * 8 + (dq_first ? n_kv : n_dq) + nx.blocks;
+    if (next.len > 0) nx.blocks = std::min((nx.rows + RPB - 1) / RPB, cus);
+    auto pad8 = [](int n) { return (n + 7) / 8 * 8; };
+    const int grid = pad8(n_dq) + pad8(n_kv) + pad8(n_kvh) + nx.blocks;
     CA_LAUNCH(CA_KERNEL_BWD, (bwd_kernel<T, D, C::DQ_NQT, C::DQ_BK, C::DQ_NW, C::KV_NKT, C::KV_BQ, C::KV_NP>),
-              dim3(grid), dim3(2 * C::DQ_NW * 64), 0, st, p, n_dq, n_kv, dq_first, nx);
+              dim3(grid), dim3(2 * C::DQ_NW * 64), 0, st, p, n_dq, n_kv, n_kvh, kv_split, dq_first, nx);
     return hipGetLastError();
   }
   if constexpr (sizeof(T) == 2) {
