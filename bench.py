@@ -4,7 +4,10 @@ One step is one pass of the whole hot path over one sequence: the forward of
 every chunk in ascending order (SeCO's inference-mode pass), then the backward
 of every chunk in descending order into zeroed float32 dK/dV accumulators (for
 the sparse workload: the t selected chunks, scaled by k/t). Inputs are resident
-in HBM before timing starts. Prints one JSON line on stdout.
+in HBM before timing starts. Prints one JSON line on stdout. The default run
+(8b_layer) also measures the 4b_layer, 32b_layer and sparse_64k workloads
+with fewer steps and reports them in the same line under "other_workloads";
+--no-others skips them.
 
 FLOPs are causal only: 4*d per visible (query, key) pair and q head for the
 forward (S and PV) and 10*d for the backward (S recompute, dP, dV, dQ, dK).
@@ -29,6 +32,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "chunked causal attn fwd+bwd tokens/s and TFLOP/s (% bf16 MFMA peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+# The default run's line also carries these configurations of the same step.
+OTHER_WORKLOADS = ("4b_layer", "32b_layer", "sparse_64k")
+OTHER_STEPS, OTHER_WARMUP = 10, 2
 PEAK_HBM_GBS = 8000.0
 
 
@@ -567,6 +573,8 @@ def main():
                     help="measure SpaCO's step on a stack of attention layers (relayed cache gradients)")
     ap.add_argument("--seed", type=int, default=0, help="chunk draw seed for --stack")
     ap.add_argument("--head", action="store_true", help="measure the streamed LM head (SFT) step")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads that the default 8b_layer run also measures")
     ap.add_argument("--ds-handover", action="store_true",
                     help="give the backward the CA_OP_BWD_DS workspace (dS handed to the dQ pass; memory grows "
                          "with the sequence) instead of the bounded one")
@@ -583,12 +591,43 @@ def main():
     if args.head:
         return head_main(args)
 
+    import torch
+
+    from sequence_chunked_exact_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    out, inp = measure_attention(wl, args.steps, args.warmup, args.ds_handover)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = with_host(cpu_baseline(wl, inp.raw))
+    else:
+        out["cpu_baseline"] = None
+    del inp
+    # The other configurations of the same step, measured in the same run
+    # with fewer steps (the line's value stays the one workload's).
+    if not args.no_others and args.workload == "8b_layer" and not args.ds_handover:
+        others = {}
+        for name in OTHER_WORKLOADS:
+            torch.cuda.empty_cache()
+            o, _ = measure_attention(W.WORKLOADS[name], OTHER_STEPS, OTHER_WARMUP, False)
+            others[name] = {k_: o[k_] for k_ in ("value", "unit", "steps", "warmup", "ms_per_step", "tflops",
+                                                  "pct_bf16_peak", "tflops_fwd", "tflops_bwd", "kernels")}
+            others[name]["config"] = o["config"]
+            others[name]["roofline"] = {k_: o["roofline"].get(k_) for k_ in ("kernel", "frac", "achieved",
+                                                                            "avg_launch_us", "traffic")}
+        out["other_workloads"] = others
+    print(json.dumps(out), flush=True)
+
+
+def measure_attention(wl, steps, warmup, ds_handover):
+    """One workload's attention step (every chunk's forward, then the backward
+    of every chunk or of the drawn ones): the bench line without the CPU
+    baseline, and the inputs."""
     import numpy as np
     import torch
     from sequence_chunked_exact_amd import binding as B
     from sequence_chunked_exact_amd import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     log(f"[bench] generating {wl.name} inputs")
@@ -604,7 +643,7 @@ def main():
     # The backward's workspace: the bounded one (the chunk's row statistics; the
     # dQ pass recomputes dS), or with --ds-handover room for dS^T of a chunk
     # against the whole prefix (memory that grows with the sequence).
-    ws_op = B.CA_OP_BWD_DS if args.ds_handover else B.CA_OP_SPARSE_BWD
+    ws_op = B.CA_OP_BWD_DS if ds_handover else B.CA_OP_SPARSE_BWD
     ws_bytes = B.chunk_attn_workspace_size(desc, ws_op)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     sparse = wl.sparse_t > 0
@@ -616,12 +655,12 @@ def main():
         return B.sparse_chunk_bwd(q, k, v, o, lse, do, dq, dk, dv, seq_len=T, chunk=C, t=t_sel, seed=seed,
                                   softmax_scale=wl.softmax_scale, workspace=ws)
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"[bench] {wl.name}: warmup {warmup}")
+    for _ in range(warmup):
         selected = step()
     torch.cuda.synchronize()
 
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] {wl.name}: timing {steps} steps")
     sel = {}
 
     def run():
@@ -633,10 +672,11 @@ def main():
     # and dQ together: 10d; recomputed products are not counted)
     t_wall = time.perf_counter()
     ms, per_step, kernels, dom, (n_launch, tot_ms) = timed_steps(
-        B, torch, run, args.steps, lambda k_: max(k_, key=lambda n_: k_[n_]["ms_per_step"]))
+        B, torch, run, steps, lambda k_: max(k_, key=lambda n_: k_[n_]["ms_per_step"]))
     wall = time.perf_counter() - t_wall
     selected = sel["v"]
-    log(f"[bench] {ms:.3f} ms/step (wall incl. the profiled steps {wall / (args.steps + 2) * 1e3:.3f} ms/step)")
+    log(f"[bench] {wl.name}: {ms:.3f} ms/step (wall incl. the profiled steps {wall / (steps + 2) * 1e3:.3f} "
+        "ms/step)")
     log("[bench] kernels " + json.dumps(kernels))
 
     plan = flop_plan(wl, selected if sparse else None)
@@ -646,7 +686,7 @@ def main():
     roof = {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": None, "traffic": None}
     if dom_flops is not None:
-        per_launch_flops = dom_flops / (n_launch / args.steps)
+        per_launch_flops = dom_flops / (n_launch / steps)
         avg_s = tot_ms / n_launch * 1e-3
         achieved = per_launch_flops / avg_s / 1e12
         roof.update({"achieved": achieved, "frac": achieved / PEAK_BF16_TFLOPS,
@@ -661,8 +701,8 @@ def main():
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms,
         "ms_per_step_median": float(np.median(per_step)),
         "ms_per_step_min": float(min(per_step)),
@@ -681,16 +721,12 @@ def main():
                    "key_spike": (f"rank {wl.spike_rank} amplitude {wl.spike_amp}" if wl.spike_rank else None),
                    "sparse_t": wl.sparse_t or None, "selected_chunks": selected if sparse else None,
                    "causal_flops_per_step": total_flops, "workspace_bytes": ws_bytes,
-                   "dq_pass": "stored dS (CA_OP_BWD_DS)" if args.ds_handover else "recompute (CA_OP_SPARSE_BWD)"},
+                   "dq_pass": "stored dS (CA_OP_BWD_DS)" if ds_handover else "recompute (CA_OP_SPARSE_BWD)"},
         "kernels": kernels,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = with_host(cpu_baseline(wl, inp.raw))
-    else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    return out, inp
 
 
 if __name__ == "__main__":

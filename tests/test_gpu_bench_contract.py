@@ -1,6 +1,7 @@
 """bench.py's output contract, on the GPU: one JSON line per mode with the
 metric, value, timing, roofline and cpu_baseline fields (a one-step run
-without the CPU baseline)."""
+without the CPU baseline); the default mode's line also carries the other
+workloads' measurements."""
 import json
 import os
 import subprocess
@@ -31,4 +32,9 @@ def test_bench_prints_one_json_line(mode):
     r = d["roofline"]
     assert r["bound"] in ("hbm", "mfma", "alu") and r["peak"] > 0 and 0 < r["frac"] < 1
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-9
-
+    if not mode:
+        others = d["other_workloads"]
+        assert sorted(others) == ["32b_layer", "4b_layer", "sparse_64k"]
+        for name, o in others.items():
+            assert o["config"]["workload"] == name and o["value"] > 0 and o["ms_per_step"] > 0
+            assert 0 < o["pct_bf16_peak"] < 100 and 0 < o["roofline"]["frac"] < 1
