@@ -6,7 +6,7 @@
 //
 //   Z  = H W^T                       [rows][vocab] float32     (PG_DH GEMM over W^T)
 //   per row: lse = logsumexp(Z), loss = lse - Z[y]; dZ = scale (softmax(Z) - onehot(y))
-//                                    [rows_pad][vocab] bf16     (ce_kernel)
+//                                    [rows_pad][vocab] bf16     (ce_stats_kernel, ce_dz_kernel)
 //   dH = dZ W                        float32, overwritten      (PG_DH GEMM over W)
 //   dW += dZ^T H                     float32, incremented      (PG_DW GEMM)
 //
@@ -15,6 +15,8 @@
 // the workspace): added per partition, its float32 read-modify-write (8 bytes
 // per weight) dominates the step. W^T [d_model][vocab] is written once per
 // step by wt_head_kernel: the logits product reads it along k.
+#include <algorithm>
+
 #include "gemm_bf16.h"
 
 namespace ca {
@@ -28,29 +30,52 @@ struct CeParams {
   bf16* dz;              // partition's first dZ row of batch entry b at dz + b * dz_bs
   long long dz_bs;
   float* row_loss;       // partition's first row of batch entry b at row_loss + b * lab_bs
+  float* part;           // [batch][rows_pad][nseg] (max, exponential sum) of each row segment
   float scale;
   int rows, rows_pad, vocab, batch;  // rows [rows, rows_pad) of dZ are zeroed
+  int nseg;                          // segments per row
 };
 
-// One workgroup per (batch entry, row of rows_pad): a pass for the row's max
-// and exponential sum (each thread over a strided quarter-vector set, then a
-// workgroup reduction), then a pass writing dZ. Padding rows write zeros.
-__global__ __launch_bounds__(256) void ce_kernel(CeParams p) {
-  __shared__ float red_m[4], red_s[4];
-  const int r = blockIdx.x % p.rows_pad, b = blockIdx.x / p.rows_pad;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  bf16* dz = p.dz + b * p.dz_bs + (long long)r * p.vocab;
+// Each row's vocabulary runs as nseg segments, one workgroup each, so that a
+// partition of ~100 rows still spreads over the whole GPU: a first launch
+// finds every segment's maximum and exponential sum, a second combines a
+// row's segments (in segment order) into its log-sum-exp and writes the
+// segment's dZ.
+constexpr int kCeSegMax = 16;
+int ce_segments(int vocab) { return std::max(1, std::min(kCeSegMax, vocab / 4 / 1024)); }
+
+struct CeRow {
+  int b, r, seg, y;  // y < 0: padding row or not a target
+  int v0, v1;        // the segment's 4-element vectors [v0, v1)
+};
+__device__ __forceinline__ CeRow ce_row(const CeParams& p) {
+  CeRow c;
+  c.seg = blockIdx.x % p.nseg;
+  const int rr = blockIdx.x / p.nseg;
+  c.r = rr % p.rows_pad;
+  c.b = rr / p.rows_pad;
+  c.y = c.r < p.rows ? p.labels[c.b * p.lab_bs + c.r] : -1;
+  if (c.y >= p.vocab) c.y = -1;  // not a target
   const int nv = p.vocab / 4;
-  int y = r < p.rows ? p.labels[b * p.lab_bs + r] : -1;
-  if (y >= p.vocab) y = -1;  // not a target
-  if (y < 0) {
-    for (int i = tid; i < nv; i += 256) *(bf16x4*)(dz + 4 * i) = bf16x4{};
-    if (r < p.rows && tid == 0) p.row_loss[b * p.lab_bs + r] = 0.f;
-    return;
-  }
-  const float* z = p.z + ((long long)b * p.rows + r) * p.vocab;
+  c.v0 = (int)((long long)nv * c.seg / p.nseg);
+  c.v1 = (int)((long long)nv * (c.seg + 1) / p.nseg);
+  return c;
+}
+// (m, s) and (m2, s2) merged: the exponential sum taken against the larger maximum.
+__device__ __forceinline__ void ce_merge(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  s = (m == -kInf ? 0.f : s * fexp2((m - mm) * kLog2e)) + (m2 == -kInf ? 0.f : s2 * fexp2((m2 - mm) * kLog2e));
+  m = mm;
+}
+
+__global__ __launch_bounds__(256) void ce_stats_kernel(CeParams p) {
+  __shared__ float red_m[4], red_s[4];
+  const CeRow c = ce_row(p);
+  if (c.y < 0) return;  // the dZ launch zeroes such rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* z = p.z + ((long long)c.b * p.rows + c.r) * p.vocab;
   float m = -kInf, s = 0.f;
-  for (int i = tid; i < nv; i += 256) {
+  for (int i = c.v0 + tid; i < c.v1; i += 256) {
     const f32x4 v = *(const f32x4*)(z + 4 * i);
     const float mv = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
     if (mv > m) {
@@ -62,33 +87,45 @@ __global__ __launch_bounds__(256) void ce_kernel(CeParams p) {
   }
   // reduce (m, s) over the wave, then over the 4 waves
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-    const float mm = fmaxf(m, m2);
-    s = (m == -kInf ? 0.f : s * fexp2((m - mm) * kLog2e)) + (m2 == -kInf ? 0.f : s2 * fexp2((m2 - mm) * kLog2e));
-    m = mm;
-  }
+  for (int o = 32; o >= 1; o >>= 1) ce_merge(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
   if (lane == 0) {
     red_m[wave] = m;
     red_s[wave] = s;
   }
   __syncthreads();
-  float M = red_m[0];
+  if (tid == 0) {
+    float M = red_m[0], S = red_s[0];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w]);
-  float S = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) S += red_s[w] * fexp2((red_m[w] - M) * kLog2e);
+    for (int w = 1; w < 4; ++w) ce_merge(M, S, red_m[w], red_s[w]);
+    float* out = p.part + ((long long)(c.b * p.rows_pad + c.r) * p.nseg + c.seg) * 2;
+    out[0] = M;
+    out[1] = S;
+  }
+}
+
+__global__ __launch_bounds__(256) void ce_dz_kernel(CeParams p) {
+  const CeRow c = ce_row(p);
+  const int tid = threadIdx.x;
+  bf16* dz = p.dz + c.b * p.dz_bs + (long long)c.r * p.vocab;
+  if (c.y < 0) {
+    for (int i = c.v0 + tid; i < c.v1; i += 256) *(bf16x4*)(dz + 4 * i) = bf16x4{};
+    if (c.r < p.rows && c.seg == 0 && tid == 0) p.row_loss[c.b * p.lab_bs + c.r] = 0.f;
+    return;
+  }
+  const float* part = p.part + (long long)(c.b * p.rows_pad + c.r) * p.nseg * 2;
+  float M = part[0], S = part[1];
+  for (int k = 1; k < p.nseg; ++k) ce_merge(M, S, part[2 * k], part[2 * k + 1]);
   const float lse = M + __logf(S);
-  if (tid == 0) p.row_loss[b * p.lab_bs + r] = lse - z[y];
-  const float scale = p.weight ? p.scale * p.weight[b * p.lab_bs + r] : p.scale;
-  for (int i = tid; i < nv; i += 256) {
+  const float* z = p.z + ((long long)c.b * p.rows + c.r) * p.vocab;
+  if (c.seg == 0 && tid == 0) p.row_loss[c.b * p.lab_bs + c.r] = lse - z[c.y];
+  const float scale = p.weight ? p.scale * p.weight[c.b * p.lab_bs + c.r] : p.scale;
+  for (int i = c.v0 + tid; i < c.v1; i += 256) {
     const f32x4 v = *(const f32x4*)(z + 4 * i);
     bf16x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float g = fexp2((v[e] - lse) * kLog2e);
-      if (4 * i + e == y) g -= 1.f;
+      if (4 * i + e == c.y) g -= 1.f;
       o[e] = (bf16)(scale * g);
     }
     *(bf16x4*)(dz + 4 * i) = o;
@@ -141,15 +178,20 @@ int head_splits(int vocab) {
 
 // Workspace: logits [batch][ps][vocab] float32; dZ of a group of partitions
 // [batch][pad64(group * ps)][vocab] bf16; split-k partials of dH
-// [splits][ps][d_model] float32; each on a 256-byte boundary.
+// [splits][ps][d_model] float32; the row segments' (max, exponential sum)
+// [batch][ps + 64][kCeSegMax] float32 pairs; each on a 256-byte boundary.
 size_t head_z_bytes(const HeadShape& s) { return ((size_t)s.batch * s.ps * s.vocab * sizeof(float) + 255) / 256 * 256; }
 int head_group_rows(const HeadShape& s) { return pg_rows_pad(s.ps * s.group); }
 size_t head_dz_bytes(const HeadShape& s) {
   return ((size_t)s.batch * head_group_rows(s) * s.vocab * sizeof(bf16) + 255) / 256 * 256;
 }
 
+size_t head_part_bytes(const HeadShape& s) {
+  return ((size_t)head_splits(s.vocab) * s.ps * s.d_model * sizeof(float) + 255) / 256 * 256;
+}
 size_t head_ws_bytes(const HeadShape& s) {
-  return head_z_bytes(s) + head_dz_bytes(s) + (size_t)head_splits(s.vocab) * s.ps * s.d_model * sizeof(float);
+  return head_z_bytes(s) + head_dz_bytes(s) + head_part_bytes(s) +
+         (size_t)s.batch * (s.ps + 64) * kCeSegMax * 2 * sizeof(float);
 }
 
 hipError_t launch_head_transpose(const HeadShape& s, const void* w, void* wt, hipStream_t st) {
@@ -208,7 +250,12 @@ hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zer
   cp.rows_pad = zero_to;
   cp.vocab = V;
   cp.batch = s.batch;
-  CA_LAUNCH(CA_KERNEL_HEAD_AUX, ce_kernel, dim3(s.batch * zero_to), dim3(256), 0, st, cp);
+  cp.nseg = ce_segments(V);
+  cp.part = (float*)(ws + head_z_bytes(s) + head_dz_bytes(s) + head_part_bytes(s));
+  const dim3 ce_grid(s.batch * zero_to * cp.nseg);
+  CA_LAUNCH(CA_KERNEL_HEAD_AUX, ce_stats_kernel, ce_grid, dim3(256), 0, st, cp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  CA_LAUNCH(CA_KERNEL_HEAD_AUX, ce_dz_kernel, ce_grid, dim3(256), 0, st, cp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -251,8 +251,9 @@ def test_lm_head_errors():
     d = HD(1, 1024, 256, 1024, b.CA_BF16)
     size = lib.lm_head_sft_workspace_size
     need = size(ctypes.byref(d), 100)
-    # logits (float32) + dZ (bf16, rows padded to 64) + 16 split-k partials of dH
-    assert need == (100 * 1024 * 4 + 255) // 256 * 256 + 128 * 1024 * 2 + 16 * 100 * 256 * 4
+    # logits (float32) + dZ (bf16, rows padded to 64) + 16 split-k partials of dH + the (max,
+    # exponential sum) pairs of up to 16 segments of ps + 64 rows
+    assert need == (100 * 1024 * 4 + 255) // 256 * 256 + 128 * 1024 * 2 + 16 * 100 * 256 * 4 + 164 * 16 * 2 * 4
     assert size(ctypes.byref(HD(1, 1024, 256, 1000, b.CA_BF16)), 100) == 0   # vocab % 64
     assert size(ctypes.byref(d), 0) == 0
 
