@@ -154,16 +154,17 @@ def test_bf16_tile_and_tail_cases(T, C, Hq, Hkv, d, spike, scale):
 @pytest.mark.parametrize("ds", [False, True])
 @pytest.mark.parametrize("d", [128, 64])
 def test_bf16_dkdv_launch_plan_with_six_kv_heads(d, ds):
-    # Six kv heads. The default backward launches dQ and dK/dV together: 192
-    # dQ workgroups and 96/192/288 key-tile workgroups, dK/dV first in chunks 0
-    # and 1 and dQ first in chunk 2 (sub-grids that are not multiples of the 8
-    # XCDs come up in the randomized cases). With the dS hand-over the dK/dV
-    # pass runs alone: the 2048-key
-    # prefix of chunk 0 on half-size key tiles (192 workgroups), chunk 1 on
-    # full tiles, and chunk 2 (48 full tiles per head, 288 workgroups) on 42
-    # full tiles per head followed by a launch of half-size tiles from key 5376
-    # on, a split inside the chunk's own diagonal block and off any multiple of
-    # the chunk size. 12 query heads also put the forward on 64-row tiles.
+    # Six kv heads. Both backward paths take the same key-tile plan: the
+    # 2048-key prefix of chunk 0 on half-size key tiles (192 workgroups),
+    # chunk 1 on full tiles (192), and chunk 2 (48 full tiles per head, 288
+    # workgroups) on 42 full tiles per head followed by half-size tiles from
+    # key 5376 on (72 workgroups), a split inside the chunk's own diagonal
+    # block and off any multiple of the chunk size. The default backward runs
+    # those as sub-grids of one launch with 192 dQ workgroups (dK/dV first in
+    # chunks 0 and 1, dQ first in chunk 2; sub-grids that are not multiples of
+    # the 8 XCDs come up in the randomized cases); the dS hand-over runs the
+    # dK/dV pass alone, the split as two launches. 12 query heads also put the
+    # forward on 64-row tiles.
     wl = custom("bf16_plan6", 6144, 2048, 12, 6, d, "bf16", seed=61 + d, spike=1)
     check_dense(wl, heads=[0, 1, 10, 11], ds=ds)
 
