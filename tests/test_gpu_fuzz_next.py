@@ -10,6 +10,13 @@ cases: loss to 1e-3 relative, row losses, dH and dW to 2e-2 of their largest mag
 Projections around the chunk attention: the batch, sequence length, chunk size (ragged last chunks included),
 d_model, kv heads and group size, head size and storage type; the whole chunked layer (projections, chunk
 forward, chunk backward, projection backward) against the dense oracle at 1e-5 (float32) / 2e-2 (bf16).
+
+Stacks of attention layers with SpaCO's relay: the batch, sequence length, chunk size, number of layers, kv
+heads and group size, head size, storage type, how many of the k chunks are drawn (t, with a drawn selection
+seed; t = k with relay factor 1 is SeCO's exact backward) and the relay factor; the weight gradients of every
+layer and dH_0 against the oracle's estimate at the same bars. bf16 rounding compounds with depth (each
+layer's activations and gradients pass through bf16): a three-layer bf16 stack of 17 positions here reaches
+1.7e-2 of the largest magnitude on its deepest weight gradients, against 2-6e-3 for one or two layers.
 """
 import numpy as np
 import pytest
@@ -21,10 +28,13 @@ from sequence_chunked_exact_amd import workloads as W
 
 import test_gpu_lm_head as TH
 import test_gpu_proj as TP
+import test_gpu_stack as TS
+from oracle import selection
+from oracle import stack as S
 
 pytestmark = pytest.mark.gpu
 
-N_HEAD, N_PROJ = 12, 12
+N_HEAD, N_PROJ, N_STACK = 12, 12, 8
 
 
 def draw_head(i):
@@ -100,3 +110,40 @@ def test_random_projection_layers(i):
     tol = 1e-5 if dtype == "f32" else 2e-2
     for n, e in errs.items():
         assert e <= tol, (n, e)
+
+
+def draw_stack(i):
+    r = np.random.default_rng(10000 + i)
+    dtype = "f32" if r.random() < 0.3 else "bf16"
+    B = int(r.integers(1, 3))
+    T = int(r.integers(1, 321))
+    C = max(1, min(T, int(r.integers(1, T + 1)) if r.random() < 0.6 else int(r.choice([32, 64, 128]))))
+    L = int(r.integers(1, 4))
+    hkv = int(r.integers(1, 3))
+    G = int(r.integers(1, 3))
+    d = int(r.choice([64, 128]))
+    k = -(-T // C)
+    t = int(r.integers(1, k + 1))
+    seed = int(r.integers(0, 2**31))
+    gamma = float(r.choice([1.0, 1.5, 2.0, k / t]))
+    return B, T, C, L, hkv * G, hkv, d, dtype, t, seed, gamma
+
+
+@pytest.mark.parametrize("i", range(N_STACK))
+def test_random_stacks(i):
+    B, T, C, L, Hq, Hkv, d, dtype, t, seed, gamma = draw_stack(i)
+    print(f"[case stack {i}] B={B} T={T} C={C} layers={L} Hq={Hq} Hkv={Hkv} d={d} {dtype} t={t} seed={seed} "
+          f"gamma={gamma:.3g}", flush=True)
+    wl = W.StackWorkload(f"fuzz_stack{i}", B, T, C, L, Hq, Hkv, d, dtype, t, None, seed=11000 + i)
+    inp = W.make_stack_inputs(wl)
+    k = wl.n_chunks
+    chunks = selection.select_chunks(k, t, seed)
+    g = TS.GpuStack(wl, inp)
+    g.forward()
+    got = g.backward(chunks, gamma)
+    args = TS.oracle_args(wl, inp)
+    if len(chunks) == k and gamma == 1.0:
+        ref = S.stack_dense_grad(*args)
+    else:
+        ref = S.spaco_estimate(*args, C, chunks, gamma)
+    TS.compare(got, ref, 1e-5 if dtype == "f32" else 2e-2, f"          fuzz_stack{i}")
