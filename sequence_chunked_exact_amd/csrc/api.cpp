@@ -393,8 +393,14 @@ int sparse_chunk_bwd(const chunk_attn_desc* d, int32_t seq_len, int32_t t, uint6
   // dq rows of the selected chunks are overwritten: with every chunk selected
   // and no rows past seq_len, nothing is left to zero
   hipError_t e = (t < kch || seq_len < d->q_capacity) ? ca::launch_zero(dq, nq, st) : hipSuccess;
-  if (e == hipSuccess) e = ca::launch_zero(dk, nkv, st);
-  if (e == hipSuccess) e = ca::launch_zero(dv, nkv, st);
+  // The first launch (the last selected chunk) stores dk/dv rows [0, its
+  // prefix end) instead of adding to them; only rows past that prefix, which
+  // no launch writes, are zeroed (none when it ends at kv_capacity).
+  const int32_t first_end = std::min((sel[t - 1] + 1) * C, seq_len);
+  if (first_end < d->kv_capacity) {
+    if (e == hipSuccess) e = ca::launch_zero(dk, nkv, st);
+    if (e == hipSuccess) e = ca::launch_zero(dv, nkv, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "sparse_chunk_bwd zero");
 
   ca::Shape s = shape_of(d);
@@ -412,6 +418,7 @@ int sparse_chunk_bwd(const chunk_attn_desc* d, int32_t seq_len, int32_t t, uint6
       nx.len = std::min(C, seq_len - nx.q_off);
       nx.ws = slot_of(idx - 1);
     }
+    s.acc_store = idx == t - 1;
     e = ca::launch_bwd(s, q, k, v, o, lse, dout, gamma, dq, dk, dv, slot_of(idx), two ? slot : ws_bytes, st,
                        two && idx < t - 1, nx);
     if (e != hipSuccess) return hip_fail(e, "sparse_chunk_bwd chunk launch");

@@ -406,6 +406,7 @@ struct BwdParams {
   void* ds;
   int ds_nqb, ds_keys;
   int kv_first, kv_end;  // dK/dV pass: the launch's key tiles cover keys [kv_first, kv_end)
+  int acc_store;         // dK/dV pass: store the prefix rows instead of adding to them
 };
 
 // dQ pass. Same walk, split and staging as the forward: two groups of NW
@@ -885,9 +886,22 @@ __device__ __forceinline__ void dkdv_body(const BwdParams& p, int block, int nbl
   }
 
   // Read-modify-write of the fp32 accumulator, 16 keys at a time: all reads
-  // are issued before any write.
+  // are issued before any write (or, for a launch that stores, no reads).
   float* dst = (pv_wave ? p.dv : p.dk) + (size_t)(b * p.hkv + hk) * p.kv_cap * D;
   const float scale = pv_wave ? p.dv_scale : p.dk_scale;
+  if (p.acc_store) {
+#pragma unroll
+    for (int nk = 0; nk < NKT; ++nk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = wk0 + nk * 16 + 4 * g + i;
+        if (key < L) {
+#pragma unroll
+          for (int md = 0; md < MD; ++md) dst[(size_t)key * D + md * 16 + n] = scale * acc[nk][md][i];
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int nk = 0; nk < NKT; ++nk) {
     f32x4 old[MD];
@@ -1254,7 +1268,8 @@ hipError_t bwd_impl(const Shape& s, const void* q, const void* k, const void* v,
               dv,    s.hq,  s.hkv,   s.q_cap,  s.kv_cap, s.q_off, s.start, s.len,
               exp2_coef(s.scale), s.scale < 0.f ? 1 : 0, gs * s.scale, gs * s.scale, gs,
               use_ds ? (void*)((char*)ws + bwd_ws_base(rows)) : nullptr,
-              (s.len + kDsCols - 1) / kDsCols, (L + kDsKeyPad - 1) / kDsKeyPad * kDsKeyPad, 0, L};
+              (s.len + kDsCols - 1) / kDsCols, (L + kDsKeyPad - 1) / kDsKeyPad * kDsKeyPad, 0, L,
+              s.acc_store ? 1 : 0};
   constexpr int BKV = C::KV_NP * C::KV_NKT * 16, BKV1 = C::KV_NP * 16;
   const int heads = s.hkv * s.batch;
   const int tiles = (L + BKV - 1) / BKV;

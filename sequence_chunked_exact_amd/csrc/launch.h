@@ -15,6 +15,9 @@ struct Shape {
   int start, len;       // chunk: first global position and number of rows
   float scale;          // softmax scale
   int dtype;            // CA_F32 / CA_BF16
+  // Backward: the dk/dv rows of the prefix are stored, not added to (the
+  // caller's accumulators hold nothing yet, e.g. a sweep's first launch).
+  bool acc_store = false;
 };
 
 // Forward: o, lse for the chunk's rows.
