@@ -5,9 +5,10 @@ every chunk in ascending order (SeCO's inference-mode pass), then the backward
 of every chunk in descending order into zeroed float32 dK/dV accumulators (for
 the sparse workload: the t selected chunks, scaled by k/t). Inputs are resident
 in HBM before timing starts. Prints one JSON line on stdout. The default run
-(8b_layer) also measures the 4b_layer, 32b_layer and sparse_64k workloads
-with fewer steps and reports them in the same line under "other_workloads";
---no-others skips them.
+(8b_layer, no --workload given) also measures the 4b_layer, 32b_layer and
+sparse_64k workloads with fewer steps and reports them in the same line under
+"other_workloads"; --no-others skips them, and --workload NAME measures that
+workload alone.
 
 FLOPs are causal only: 4*d per visible (query, key) pair and q head for the
 forward (S and PV) and 10*d for the backward (S recompute, dP, dV, dQ, dK).
@@ -565,7 +566,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8b_layer")
+    ap.add_argument("--workload", default=None,
+                    help="measure this workload only (default: 8b_layer, plus the other workloads in the same line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layer", action="store_true",
                     help="measure the whole attention layer step (QKV projections + attention)")
@@ -595,7 +597,7 @@ def main():
 
     from sequence_chunked_exact_amd import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
+    wl = W.WORKLOADS[args.workload or "8b_layer"]
     out, inp = measure_attention(wl, args.steps, args.warmup, args.ds_handover)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
@@ -605,7 +607,7 @@ def main():
     del inp
     # The other configurations of the same step, measured in the same run
     # with fewer steps (the line's value stays the one workload's).
-    if not args.no_others and args.workload == "8b_layer" and not args.ds_handover:
+    if not args.no_others and args.workload is None and not args.ds_handover:
         others = {}
         for name in OTHER_WORKLOADS:
             torch.cuda.empty_cache()
