@@ -33,7 +33,7 @@ CSRC = os.path.join(HERE, "csrc")
 COPY_BYTES = 1 << 30
 N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 
-SHORT = {"fwd_kernel": "fwd", "bwd_kernel": "bwd", "dkdv_kernel": "dkdv", "dq_kernel": "dq", "dqs_kernel": "dq",
+SHORT = {"fwd_kernel": "fwd", "bwd_kernel": "bwd", "dkdv_kernel": "dkdv", "dqs_kernel": "dq",
          "delta_kernel": "delta", "zero_kernel": "zero", "accumulate_kernel": "accumulate", "gemm_kernel": "proj",
          "residual_fwd_kernel": "residual_fwd", "residual_bwd_kernel": "residual_bwd", "wt_kernel": "proj_prep",
          "gcat_kernel": "proj_prep"}
