@@ -72,16 +72,18 @@ def run_case(wl, ds, mode, sparse):
                                  seed=sparse[1], softmax_scale=sc, ds_handover=ds)
     else:
         # query-side tensors of one chunk at a time: rows [s, s + c) copied out, computed, copied back
+        # (clone, not contiguous(): a slice that is already contiguous would stay a view at an
+        # offset the library's 16-byte alignment check rejects)
         for s, c in chunks:
-            qc = q[:, :, s:s + c].contiguous()
+            qc = q[:, :, s:s + c].clone()
             oc = torch.empty_like(qc)
             lc = torch.empty(qc.shape[:3], dtype=torch.float32, device=DEV)
             B.chunk_attn_fwd(qc, k, v, oc, lc, chunk_start=s, chunk_len=c, softmax_scale=sc)
             o[:, :, s:s + c] = oc
             lse[:, :, s:s + c] = lc
         for s, c in reversed(chunks):
-            qc, oc, lc = (x[:, :, s:s + c].contiguous() for x in (q, o, lse))
-            doc = do[:, :, s:s + c].contiguous()
+            qc, oc, lc = (x[:, :, s:s + c].clone() for x in (q, o, lse))
+            doc = do[:, :, s:s + c].clone()
             dqc = torch.empty(qc.shape, dtype=torch.float32, device=DEV)
             B.chunk_attn_bwd(qc, k, v, oc, lc, doc, dqc, dk, dv, chunk_start=s, chunk_len=c, softmax_scale=sc,
                              ds_handover=ds)
