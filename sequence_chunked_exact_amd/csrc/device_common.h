@@ -289,8 +289,8 @@ struct RegTile {
   V r[R];
 
   __device__ __forceinline__ void load(const T* head, int row0, int limit, int tid) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer-load builtins exist only in the device pass
     const int dv = tid % NDV, grp = SPARE ? min(tid / NDV, ROWS - 1) : tid / NDV;
-#if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)head, (short)0, limit * D * (int)sizeof(T), 0x00020000);
 #pragma unroll
