@@ -394,8 +394,10 @@ int sparse_chunk_bwd(const chunk_attn_desc* d, int32_t seq_len, int32_t t, uint6
   // and no rows past seq_len, nothing is left to zero
   hipError_t e = (t < kch || seq_len < d->q_capacity) ? ca::launch_zero(dq, nq, st) : hipSuccess;
   // The first launch (the last selected chunk) stores dk/dv rows [0, its
-  // prefix end) instead of adding to them; only rows past that prefix, which
-  // no launch writes, are zeroed (none when it ends at kv_capacity).
+  // prefix end) instead of adding to them. Rows past that prefix are written
+  // by no launch: when there are any (the prefix ends before kv_capacity),
+  // the whole of dk and dv is zeroed first, and the first launch's stores
+  // then overwrite its prefix rows.
   const int32_t first_end = std::min((sel[t - 1] + 1) * C, seq_len);
   if (first_end < d->kv_capacity) {
     if (e == hipSuccess) e = ca::launch_zero(dk, nkv, st);
