@@ -112,7 +112,16 @@ __global__ __launch_bounds__(NG * 256) __attribute__((amdgpu_waves_per_eu(2))) v
   const int mt = (p.M + 127) / 128, ntl = (p.N + 127) / 128;
   const int id = xcd_order(blockIdx.x, gridDim.x);
   const int bz = id / (mt * ntl), rem = id % (mt * ntl);
-  const int m0 = (rem % mt) * 128, n0 = (rem / mt) * 128;
+  // Weight gradient: the grid walks runs of GM row blocks, each run taking
+  // every column block before the next starts. An A block (a slice of dZ^T or
+  // H^T), which every column block reads, is then reused from L2 within its
+  // run; with row blocks fastest over the whole range, each column pass
+  // streamed all of A again (for the LM head's dW, 13 GB of 15.5 GB fetched).
+  constexpr int GM = 8;
+  const int run = rem / (GM * ntl), in_run = rem % (GM * ntl);
+  const int gm = MODE == PG_DW ? min(GM, mt - run * GM) : mt;
+  const int m0 = (MODE == PG_DW ? run * GM + in_run % gm : rem % mt) * 128;
+  const int n0 = (MODE == PG_DW ? in_run / gm : rem / mt) * 128;
   const int nks = p.K / 64;
   const int nk = MODE == PG_DW ? nks * p.batch : nks;
   const int n_pairs = (nk + NG - 1) / NG;  // steps of NG slices
