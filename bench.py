@@ -240,7 +240,11 @@ def layer_main(args):
     starts = list(range(0, T, C))
     desc = B.make_desc(q, k, chunk_start=0, chunk_len=C)
     ws = torch.empty(max(B.chunk_attn_workspace_size(desc, B.CA_OP_BWD), 256), dtype=torch.uint8, device=dev)
-    pws = torch.empty(max(B.qkv_proj_bwd_workspace_size(desc, dm), 256), dtype=torch.uint8, device=dev)
+    # bf16 layers: the weights' transpose is written once per backward sweep (qkv_proj_weights_t),
+    # so each chunk's projection backward needs only the gradient part of its workspace
+    wt_bytes = B.qkv_proj_weights_t_bytes(desc, dm)
+    wcat_t = torch.empty(max(wt_bytes, 16), dtype=torch.uint8, device=dev) if wt_bytes else None
+    pws = torch.empty(max(B.qkv_proj_bwd_workspace_size(desc, dm) - wt_bytes, 256), dtype=torch.uint8, device=dev)
 
     def step():
         for s in starts:
@@ -249,12 +253,14 @@ def layer_main(args):
             B.chunk_attn_fwd(q, k, v, o, lse, chunk_start=s, chunk_len=c, q_row_offset=s, softmax_scale=sc)
         for t_ in (dk, dv, dwq, dwk, dwv):
             t_.zero_()
+        if wcat_t is not None:
+            B.qkv_proj_weights_t(wq, wk, wv, q, k, out=wcat_t)
         for s in reversed(starts):
             c = min(C, T - s)
             B.chunk_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, chunk_start=s, chunk_len=c, q_row_offset=s,
                              softmax_scale=sc, workspace=ws)
             B.qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, chunk_start=s, chunk_len=c,
-                           q_row_offset=s, workspace=pws)
+                           q_row_offset=s, workspace=pws, w_cat_t=wcat_t)
 
     log(f"[bench] layer warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -241,6 +241,33 @@ int qkv_proj_bwd(const chunk_attn_desc* desc, int32_t d_model, int32_t h_capacit
                  const float* dk_acc, const float* dv_acc, float* dwq, float* dwk, float* dwv, float* dh,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* The bf16 backward's input gradient reads the weights transposed, W_cat^T =
+ * [wq | wk | wv]^T ((n_q_heads + 2 n_kv_heads) * head_dim rows of d_model,
+ * bf16); qkv_proj_bwd writes that transpose into its workspace on every call.
+ * A backward sweep over a layer's chunks (the StreamBP review, major comment 1:
+ * every chunk's gradients meet the same weights) can instead write it once
+ * with qkv_proj_weights_t and hand it to qkv_proj_bwd_wt for each chunk.
+ *
+ * qkv_proj_weights_t_bytes: bytes of W_cat^T for a bf16 layer (0 for float32
+ * layers and for invalid arguments).
+ * qkv_proj_weights_t: writes W_cat^T of wq, wk, wv (layouts as above) into
+ * w_cat_t (qkv_proj_weights_t_bytes bytes of device memory, 16-byte aligned,
+ * owned by the caller). bf16 layers only (CA_ERR_DTYPE otherwise); other errors
+ * as for qkv_proj_fwd.
+ * qkv_proj_bwd_wt: qkv_proj_bwd with the transpose given. For a bf16 layer,
+ * w_cat_t must hold what qkv_proj_weights_t wrote for these same weights (the
+ * call reads it and never checks it; stale contents give wrong dh), and ws
+ * needs only qkv_proj_bwd_workspace_size - qkv_proj_weights_t_bytes bytes.
+ * For a float32 layer w_cat_t is ignored (may be NULL) and the call is
+ * qkv_proj_bwd. Results equal qkv_proj_bwd's bit for bit. */
+size_t qkv_proj_weights_t_bytes(const chunk_attn_desc* desc, int32_t d_model);
+int qkv_proj_weights_t(const chunk_attn_desc* desc, int32_t d_model, const void* wq, const void* wk, const void* wv,
+                       void* w_cat_t, void* stream);
+int qkv_proj_bwd_wt(const chunk_attn_desc* desc, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
+                    const void* h, const void* wq, const void* wk, const void* wv, const void* w_cat_t,
+                    const float* dq, const float* dk_acc, const float* dv_acc, float* dwq, float* dwk, float* dwv,
+                    float* dh, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- SpaCO over a stack of attention layers ------------------------------
  *
  * The relay of SpaCO's Algorithm 2 (SeCO/SpaCO review, Referee Report major

@@ -84,6 +84,9 @@ def _load() -> ctypes.CDLL:
         "qkv_proj_bwd_workspace_size": (SZ, [D, I32]),
         "qkv_proj_fwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P]),
         "qkv_proj_bwd": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "qkv_proj_weights_t_bytes": (SZ, [D, I32]),
+        "qkv_proj_weights_t": (ctypes.c_int, [D, I32, P, P, P, P, P]),
+        "qkv_proj_bwd_wt": (ctypes.c_int, [D, I32, I32, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "spaco_stack_workspace_size": (SZ, [D, I32]),
         "spaco_stack_forward": (ctypes.c_int, [D, I32, I32, ctypes.POINTER(SpacoLayer), P, I32, P, SZ, P]),
         "spaco_stack_backward": (ctypes.c_int, [D, I32, I32, ctypes.POINTER(SpacoLayer), P, P, P, I32,
@@ -227,22 +230,52 @@ def qkv_proj_fwd(h, wq, wk, wv, q, k, v, *, chunk_start: int, chunk_len: int, q_
                             _ptr(q), _ptr(k), _ptr(v), _stream(q)))
 
 
+def qkv_proj_weights_t_bytes(desc: Desc, d_model: int) -> int:
+    return int(lib.qkv_proj_weights_t_bytes(ctypes.byref(desc), int(d_model)))
+
+
+def qkv_proj_weights_t(wq, wk, wv, q, k, out=None):
+    """W_cat^T = [wq | wk | wv]^T (bf16, [(Hq + 2 Hkv) d, d_model]) for qkv_proj_bwd(..., w_cat_t=)
+    over a backward sweep with these weights. q and k only give the descriptor's shapes."""
+    _contig(wq, wk, wv)
+    desc = make_desc(q, k, chunk_start=0, chunk_len=1)
+    dm = wq.shape[0]
+    if out is None:
+        import torch
+        out = torch.empty(wq.shape[1] + wk.shape[1] + wv.shape[1], dm, dtype=wq.dtype, device=wq.device)
+    _contig(out)
+    _check(lib.qkv_proj_weights_t(ctypes.byref(desc), dm, _ptr(wq), _ptr(wk), _ptr(wv), _ptr(out), _stream(wq)))
+    return out
+
+
 def qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh, *, chunk_start: int,
-                 chunk_len: int, q_row_offset: int = 0, h_row_offset: Optional[int] = None, workspace=None):
+                 chunk_len: int, q_row_offset: int = 0, h_row_offset: Optional[int] = None, workspace=None,
+                 w_cat_t=None):
     """Projection gradients of one chunk: dW += H_in^T (dQ, dK, dV rows of the chunk), dh rows of
-    the chunk = dQ Wq^T + dK Wk^T + dV Wv^T. q and k only give the descriptor's shapes."""
+    the chunk = dQ Wq^T + dK Wk^T + dV Wv^T. q and k only give the descriptor's shapes. w_cat_t:
+    the weights' transpose from qkv_proj_weights_t (bf16 layers), written once per sweep instead
+    of by every call."""
     _contig(h, wq, wk, wv, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh)
     desc = make_desc(q, k, chunk_start=chunk_start, chunk_len=chunk_len, q_row_offset=q_row_offset)
     B, Th, dm = h.shape
     hoff = chunk_start if h_row_offset is None else h_row_offset
     need = qkv_proj_bwd_workspace_size(desc, dm)
+    if w_cat_t is not None:
+        need -= qkv_proj_weights_t_bytes(desc, dm)
     if workspace is None and need > 0:
         import torch
         workspace = torch.empty(need, dtype=torch.uint8, device=h.device)
     ws, nbytes = workspace, (0 if workspace is None else workspace.numel() * workspace.element_size())
-    _check(lib.qkv_proj_bwd(ctypes.byref(desc), dm, Th, int(hoff), _ptr(h), _ptr(wq), _ptr(wk), _ptr(wv),
-                            _ptr(dq), _ptr(dk_acc), _ptr(dv_acc), _ptr(dwq), _ptr(dwk), _ptr(dwv), _ptr(dh),
-                            None if ws is None else _ptr(ws), nbytes, _stream(h)))
+    wsp = None if ws is None else _ptr(ws)
+    if w_cat_t is None:
+        _check(lib.qkv_proj_bwd(ctypes.byref(desc), dm, Th, int(hoff), _ptr(h), _ptr(wq), _ptr(wk), _ptr(wv),
+                                _ptr(dq), _ptr(dk_acc), _ptr(dv_acc), _ptr(dwq), _ptr(dwk), _ptr(dwv), _ptr(dh),
+                                wsp, nbytes, _stream(h)))
+    else:
+        _contig(w_cat_t)
+        _check(lib.qkv_proj_bwd_wt(ctypes.byref(desc), dm, Th, int(hoff), _ptr(h), _ptr(wq), _ptr(wk), _ptr(wv),
+                                   _ptr(w_cat_t), _ptr(dq), _ptr(dk_acc), _ptr(dv_acc), _ptr(dwq), _ptr(dwk),
+                                   _ptr(dwv), _ptr(dh), wsp, nbytes, _stream(h)))
 
 
 def chunk_select(k: int, t: int, seed: int) -> list:

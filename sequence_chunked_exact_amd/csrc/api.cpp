@@ -339,6 +339,38 @@ int qkv_proj_fwd(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, 
   return e == hipSuccess ? CA_OK : hip_fail(e, "qkv_proj_fwd launch");
 }
 
+size_t qkv_proj_weights_t_bytes(const chunk_attn_desc* d, int32_t d_model) {
+  if (check_proj(d, d_model, d ? d->chunk_len : 1, 0) != CA_OK) return 0;
+  return ca::proj_wt_bytes(proj_shape(d, d_model, d->chunk_len, 0));
+}
+
+int qkv_proj_weights_t(const chunk_attn_desc* d, int32_t d_model, const void* wq, const void* wk, const void* wv,
+                       void* w_cat_t, void* stream) {
+  int rc = check_proj(d, d_model, d ? d->chunk_len : 1, 0);
+  if (rc) return rc;
+  if (d->dtype != CA_BF16) return fail(CA_ERR_DTYPE, "qkv_proj_weights_t: bf16 layers only");
+  if ((rc = check_ptrs({wq, wk, wv, w_cat_t}))) return rc;
+  hipError_t e = ca::launch_proj_wt(proj_shape(d, d_model, d->chunk_len, 0), wq, wk, wv, w_cat_t,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? CA_OK : hip_fail(e, "qkv_proj_weights_t launch");
+}
+
+int qkv_proj_bwd_wt(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
+                    const void* h, const void* wq, const void* wk, const void* wv, const void* w_cat_t,
+                    const float* dq, const float* dk_acc, const float* dv_acc, float* dwq, float* dwk, float* dwv,
+                    float* dh, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_proj(d, d_model, h_capacity, h_row_offset);
+  if (rc) return rc;
+  if ((rc = check_ptrs({h, wq, wk, wv, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh}))) return rc;
+  const bool use_wt = d->dtype == CA_BF16;  // float32 layers read the weights directly
+  if (use_wt && (rc = check_ptrs({w_cat_t}))) return rc;
+  const ca::ProjShape ps = proj_shape(d, d_model, h_capacity, h_row_offset);
+  if ((rc = check_ws(ws, ws_bytes, ca::proj_bwd_ws_bytes(ps, use_wt)))) return rc;
+  hipError_t e = ca::launch_proj_bwd(ps, h, wq, wk, wv, dq, dk_acc, dv_acc, dwq, dwk, dwv, dh, ws,
+                                     (hipStream_t)stream, use_wt ? w_cat_t : nullptr);
+  return e == hipSuccess ? CA_OK : hip_fail(e, "qkv_proj_bwd_wt launch");
+}
+
 int qkv_proj_bwd(const chunk_attn_desc* d, int32_t d_model, int32_t h_capacity, int32_t h_row_offset,
                  const void* h, const void* wq, const void* wk, const void* wv, const float* dq,
                  const float* dk_acc, const float* dv_acc, float* dwq, float* dwk, float* dwv, float* dh,

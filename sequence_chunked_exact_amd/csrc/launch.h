@@ -90,12 +90,18 @@ struct ProjShape {
 hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
                            void* q, void* k, void* v, hipStream_t st);
 // dW += H^(i)^T G for G = dq, dk, dv rows of the chunk; dh rows of the chunk
-// = dq wq^T + dk wk^T + dv wv^T (float32). ws: proj_bwd_ws_bytes(s) bytes,
-// 256-byte aligned (bf16 layers hold the chunk's gradients there as bf16).
-size_t proj_bwd_ws_bytes(const ProjShape& s);
+// = dq wq^T + dk wk^T + dv wv^T (float32). ws: proj_bwd_ws_bytes(s, wt != 0)
+// bytes, 256-byte aligned (bf16 layers hold the chunk's gradients there as
+// bf16, and the weights' transpose unless wt gives it).
+size_t proj_bwd_ws_bytes(const ProjShape& s, bool have_wt = false);
 hipError_t launch_proj_bwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
                            const float* dq, const float* dk, const float* dv, float* dwq, float* dwk, float* dwv,
-                           float* dh, void* ws, hipStream_t st);
+                           float* dh, void* ws, hipStream_t st, const void* wt = nullptr);
+// W_cat^T = [wq | wk | wv]^T of a bf16 layer into out (proj_wt_bytes(s) bytes;
+// 0 for float32 layers, which need none).
+size_t proj_wt_bytes(const ProjShape& s);
+hipError_t launch_proj_wt(const ProjShape& s, const void* wq, const void* wk, const void* wv, void* out,
+                          hipStream_t st);
 
 // Residual connections of a layer stack over one chunk's rows (d_model =
 // hq * head_dim). Row-major operands are [batch][cap][d_model] with the chunk

@@ -383,13 +383,32 @@ hipError_t pg_fwd(const ProjShape& s, const void* h, const void* const w[3], voi
   return pg_launch<PG_FWD>(p, s.batch, CA_KERNEL_PROJ, st);
 }
 
+// W_cat^T of the three weights into out ((Hq + 2 Hkv) d rows of d_model).
+hipError_t pg_wt(const ProjShape& s, const void* const w[3], bf16* out, hipStream_t st) {
+  const int d = s.head_dim;
+  const int H[3] = {s.hq, s.hkv, s.hkv};
+  const int N = (s.hq + 2 * s.hkv) * d;
+  WtParams tp{};
+  for (int t = 0; t < 3; ++t) {
+    tp.w[t] = (const bf16*)w[t];
+    tp.w_w[t] = H[t] * d;
+  }
+  tp.d_model = s.d_model;
+  tp.ncols = N;
+  tp.out = out;
+  CA_LAUNCH(CA_KERNEL_PROJ_PREP, wt_kernel, dim3((N / 64) * (s.d_model / 64)), dim3(256), 0, st, tp);
+  return hipGetLastError();
+}
+
 hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], const float* const g[3],
-                  float* const dw[3], float* dh, void* ws, hipStream_t st) {
+                  float* const dw[3], float* dh, void* ws, const void* wt_given, hipStream_t st) {
   const int d = s.head_dim;
   const int H[3] = {s.hq, s.hkv, s.hkv};
   const int N = (s.hq + 2 * s.hkv) * d, rows_pad = pg_rows_pad(s.len);
   bf16* gcat = (bf16*)ws;
-  bf16* wt = (bf16*)((char*)ws + pg_gcat_bytes(s));
+  // W_cat^T: the caller's (written by launch_proj_wt for these weights), or
+  // transposed here into the workspace behind the gradients.
+  const bf16* wt = wt_given ? (const bf16*)wt_given : (const bf16*)((char*)ws + pg_gcat_bytes(s));
   GcatParams gp{};
   for (int t = 0; t < 3; ++t) {
     const int cap = t == 0 ? s.q_cap : s.kv_cap, off = t == 0 ? s.q_off : s.start;
@@ -410,17 +429,7 @@ hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], con
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  WtParams tp{};
-  for (int t = 0; t < 3; ++t) {
-    tp.w[t] = (const bf16*)w[t];
-    tp.w_w[t] = H[t] * d;
-  }
-  tp.d_model = s.d_model;
-  tp.ncols = N;
-  tp.out = wt;
-  CA_LAUNCH(CA_KERNEL_PROJ_PREP, wt_kernel, dim3((N / 64) * (s.d_model / 64)), dim3(256), 0, st, tp);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!wt_given && (e = pg_wt(s, w, (bf16*)wt, st)) != hipSuccess) return e;
 
   // dW_cat += H_in^(i)^T G_cat, the batch summed along k.
   ProjGemmParams p{};
@@ -471,9 +480,20 @@ hipError_t pg_bwd(const ProjShape& s, const void* h, const void* const w[3], con
 }
 }  // namespace
 
-size_t proj_bwd_ws_bytes(const ProjShape& s) {
+size_t proj_wt_bytes(const ProjShape& s) {
   if (s.dtype != CA_BF16) return 0;
-  return pg_gcat_bytes(s) + (size_t)(s.hq + 2 * s.hkv) * s.head_dim * s.d_model * sizeof(bf16);
+  return (size_t)(s.hq + 2 * s.hkv) * s.head_dim * s.d_model * sizeof(bf16);
+}
+
+size_t proj_bwd_ws_bytes(const ProjShape& s, bool have_wt) {
+  if (s.dtype != CA_BF16) return 0;
+  return pg_gcat_bytes(s) + (have_wt ? 0 : proj_wt_bytes(s));
+}
+
+hipError_t launch_proj_wt(const ProjShape& s, const void* wq, const void* wk, const void* wv, void* out,
+                          hipStream_t st) {
+  const void* const w[3] = {wq, wk, wv};
+  return pg_wt(s, w, (bf16*)out, st);
 }
 
 hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
@@ -485,11 +505,12 @@ hipError_t launch_proj_fwd(const ProjShape& s, const void* h, const void* wq, co
 
 hipError_t launch_proj_bwd(const ProjShape& s, const void* h, const void* wq, const void* wk, const void* wv,
                            const float* dq, const float* dk, const float* dv, float* dwq, float* dwk, float* dwv,
-                           float* dh, void* ws, hipStream_t st) {
+                           float* dh, void* ws, hipStream_t st, const void* wt) {
   const void* const w[3] = {wq, wk, wv};
   const float* const g[3] = {dq, dk, dv};
   float* const dw[3] = {dwq, dwk, dwv};
-  return s.dtype == CA_BF16 ? pg_bwd(s, h, w, g, dw, dh, ws, st) : proj_bwd_impl<float>(s, h, w, g, dw, dh, st);
+  return s.dtype == CA_BF16 ? pg_bwd(s, h, w, g, dw, dh, ws, wt, st)
+                            : proj_bwd_impl<float>(s, h, w, g, dw, dh, st);
 }
 
 }  // namespace ca

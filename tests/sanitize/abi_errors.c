@@ -176,6 +176,22 @@ static void projection_stack_head_errors(void) {
   EXPECT(PB(256, 700, FAKE, FAKE, 1 << 26) == CA_ERR_SHAPE);
   EXPECT(PB(256, 1024, NULL, FAKE, 1 << 26) == CA_ERR_NULL);
 #undef PB
+  EXPECT(qkv_proj_weights_t_bytes(&d, 256) > 0);
+  EXPECT(qkv_proj_weights_t_bytes(NULL, 256) == 0);
+  EXPECT(qkv_proj_weights_t(&d, 96, FAKE, FAKE, FAKE, FAKE, NULL) == CA_ERR_SHAPE);
+  EXPECT(qkv_proj_weights_t(&d, 256, FAKE, FAKE, FAKE, NULL, NULL) == CA_ERR_NULL);
+  EXPECT(qkv_proj_weights_t(NULL, 256, FAKE, FAKE, FAKE, FAKE, NULL) == CA_ERR_NULL);
+  {
+    chunk_attn_desc f = base();
+    f.dtype = CA_F32;
+    EXPECT(qkv_proj_weights_t(&f, 256, FAKE, FAKE, FAKE, FAKE, NULL) == CA_ERR_DTYPE);
+  }
+#define PBW(wt, wsp, wsb) \
+  qkv_proj_bwd_wt(&d, 256, 1024, 512, FAKE, FAKE, FAKE, FAKE, wt, F, F, F, F, F, F, F, wsp, wsb, NULL)
+  EXPECT(PBW(NULL, FAKE, 1 << 26) == CA_ERR_NULL);
+  EXPECT(PBW(MIS, FAKE, 1 << 26) == CA_ERR_ALIGN);
+  EXPECT(PBW(FAKE, NULL, 0) == CA_ERR_WORKSPACE);
+#undef PBW
   EXPECT(qkv_proj_fwd(&d, 96, 1024, 512, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == CA_ERR_SHAPE);
   EXPECT(qkv_proj_fwd(&d, 256, 1024, 512, FAKE, FAKE, MIS, FAKE, FAKE, FAKE, FAKE, NULL) == CA_ERR_ALIGN);
 

@@ -17,13 +17,18 @@ hipError_t scratch_address(void**) { return hipErrorNotSupported; }
 hipError_t launch_accumulate(float*, const float*, int, int, int, int, int, int, float, hipStream_t) {
   return hipErrorNotSupported;
 }
-size_t proj_bwd_ws_bytes(const ProjShape&) { return 4096; }
+size_t proj_bwd_ws_bytes(const ProjShape&, bool have_wt) { return have_wt ? 2048 : 4096; }
+size_t proj_wt_bytes(const ProjShape&) { return 2048; }
+hipError_t launch_proj_wt(const ProjShape&, const void*, const void*, const void*, void*, hipStream_t) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_proj_fwd(const ProjShape&, const void*, const void*, const void*, const void*, void*, void*, void*,
                            hipStream_t) {
   return hipErrorNotSupported;
 }
 hipError_t launch_proj_bwd(const ProjShape&, const void*, const void*, const void*, const void*, const float*,
-                           const float*, const float*, float*, float*, float*, float*, void*, hipStream_t) {
+                           const float*, const float*, float*, float*, float*, float*, void*, hipStream_t,
+                           const void*) {
   return hipErrorNotSupported;
 }
 hipError_t launch_residual_fwd(const ResidualShape&, const void*, const void*, void*, hipStream_t) {

@@ -215,6 +215,37 @@ def test_projection_workspace_and_errors():
     assert proj_bwd(desc(head_dim=96)) == -6
 
 
+def proj_bwd_wt(d, dm=256, hcap=1024, hoff=512, ws=FAKE, ws_bytes=1 << 26, wt=FAKE):
+    return lib.qkv_proj_bwd_wt(ctypes.byref(d), dm, hcap, hoff, FAKE, FAKE, FAKE, FAKE, wt, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_projection_transpose_sizes_and_errors():
+    d = desc()   # bf16, Hq 4, Hkv 2, d 128, chunk 256 rows
+    wt = 8 * 128 * 256 * 2                            # (Hq + 2 Hkv) d x d_model, bf16
+    assert lib.qkv_proj_weights_t_bytes(ctypes.byref(d), 256) == wt
+    assert lib.qkv_proj_weights_t_bytes(ctypes.byref(desc(dtype=b.CA_F32)), 256) == 0
+    assert lib.qkv_proj_weights_t_bytes(ctypes.byref(d), 96) == 0
+    grads = lib.qkv_proj_bwd_workspace_size(ctypes.byref(d), 256) - wt   # the gradient part alone
+    assert grads == 256 * 8 * 128 * 2
+    # the transpose: bf16 only, every pointer checked
+    wtf = lib.qkv_proj_weights_t
+    assert wtf(ctypes.byref(desc(dtype=b.CA_F32)), 256, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert wtf(ctypes.byref(d), 96, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert wtf(ctypes.byref(d), 256, FAKE, FAKE, FAKE, None, None) == -1
+    assert wtf(ctypes.byref(d), 256, FAKE, MISALIGNED, FAKE, FAKE, None) == -4
+    assert wtf(None, 256, FAKE, FAKE, FAKE, FAKE, None) == -1
+    # the backward with the transpose given needs only the gradient part of the workspace
+    assert proj_bwd_wt(d, ws_bytes=grads - 1) == -5
+    assert proj_bwd_wt(d, ws=None) == -5
+    assert proj_bwd_wt(d, wt=None) == -1              # bf16 layers need it
+    assert proj_bwd_wt(d, wt=MISALIGNED) == -4
+    assert proj_bwd_wt(d, dm=96) == -2
+    assert proj_bwd_wt(desc(head_dim=96)) == -6
+    # the backward without it still needs the whole workspace
+    assert proj_bwd(d, ws_bytes=grads) == -5
+
+
 def test_stack_errors():
     d = desc(chunk_start=0, chunk_len=128, q_capacity=128, n_q_heads=2, n_kv_heads=1, kv_capacity=1024)
     lay = (b.SpacoLayer * 2)()

@@ -22,7 +22,9 @@ def rel(a, b):
     return float(np.abs(np.asarray(a, np.float64) - b).max() / max(np.abs(b).max(), 1e-30))
 
 
-def run_layer(wl, inp):
+def run_layer(wl, inp, transpose_once=False):
+    """The chunked layer through the C ABI. transpose_once: the weights' transpose is written once
+    for the backward sweep (qkv_proj_weights_t) and handed to every chunk (qkv_proj_bwd_wt)."""
     import torch
     from sequence_chunked_exact_amd import binding as Bn
     dev = "cuda:0"
@@ -49,13 +51,14 @@ def run_layer(wl, inp):
     dwk = torch.zeros(dm, Hkv * d, dtype=f32, device=dev)
     dwv = torch.zeros_like(dwk)
     dh = torch.full((B, T, dm), float("nan"), dtype=f32, device=dev)
+    wcat_t = Bn.qkv_proj_weights_t(wq, wk, wv, q, k) if transpose_once else None
     for s in reversed(starts):
         c = min(C, T - s)
         print(f"[case] {wl.name} chunk {s // C} bwd", flush=True)
         Bn.chunk_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, chunk_start=s, chunk_len=c, q_row_offset=s,
                           softmax_scale=sc)
         Bn.qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, chunk_start=s, chunk_len=c,
-                        q_row_offset=s)
+                        q_row_offset=s, w_cat_t=wcat_t)
     torch.cuda.synchronize()
     out = {n: t.float().cpu().numpy().astype(np.float64)
            for n, t in dict(q=q, k=k, v=v, o=o, dwq=dwq, dwk=dwk, dwv=dwv, dh=dh).items()}
@@ -94,6 +97,23 @@ def test_layer_parity(case):
     print(name, {k_: f"{v_:.2e}" for k_, v_ in errs.items()}, flush=True)
     for n_, e in errs.items():
         assert e <= tol, (n_, e)
+
+
+BF16_CASES = [c for c in CASES if c[8] == "bf16"]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_layer_weights_transposed_once(case):
+    """qkv_proj_bwd_wt with the transpose written once per sweep gives qkv_proj_bwd's results bit for
+    bit (the same kernels read the same W_cat^T), over ragged sweeps, batch 2 and the 8B dims."""
+    name, B, T, C, dm, Hq, Hkv, d, dtype = case
+    print(f"[case] {name} transpose once", flush=True)
+    wl = W.LayerWorkload(name, B, T, C, dm, Hq, Hkv, d, dtype, seed=13)
+    inp = W.make_layer_inputs(wl)
+    a = run_layer(wl, inp)
+    b_ = run_layer(wl, inp, transpose_once=True)
+    for n_ in a:
+        assert np.array_equal(a[n_], b_[n_]), n_
 
 
 def test_layer_full_size_sampled():
