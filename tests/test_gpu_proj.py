@@ -22,9 +22,21 @@ def rel(a, b):
     return float(np.abs(np.asarray(a, np.float64) - b).max() / max(np.abs(b).max(), 1e-30))
 
 
+def proj_bwd_wt_null(Bn, h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, s, c):
+    """qkv_proj_bwd_wt called with a NULL transpose (what a float32 layer may pass)."""
+    import ctypes
+    desc = Bn.make_desc(q, k, chunk_start=s, chunk_len=c, q_row_offset=s)
+    _, Th, dm = h.shape
+    rc = Bn.lib.qkv_proj_bwd_wt(ctypes.byref(desc), dm, Th, s, h.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+                                wv.data_ptr(), None, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dwq.data_ptr(),
+                                dwk.data_ptr(), dwv.data_ptr(), dh.data_ptr(), None, 0, None)
+    assert rc == 0, Bn.lib.chunk_attn_last_error()
+
+
 def run_layer(wl, inp, transpose_once=False):
     """The chunked layer through the C ABI. transpose_once: the weights' transpose is written once
-    for the backward sweep (qkv_proj_weights_t) and handed to every chunk (qkv_proj_bwd_wt)."""
+    for the backward sweep (qkv_proj_weights_t) and handed to every chunk (qkv_proj_bwd_wt); a
+    float32 layer, which needs no transpose, calls qkv_proj_bwd_wt with NULL instead."""
     import torch
     from sequence_chunked_exact_amd import binding as Bn
     dev = "cuda:0"
@@ -51,14 +63,18 @@ def run_layer(wl, inp, transpose_once=False):
     dwk = torch.zeros(dm, Hkv * d, dtype=f32, device=dev)
     dwv = torch.zeros_like(dwk)
     dh = torch.full((B, T, dm), float("nan"), dtype=f32, device=dev)
-    wcat_t = Bn.qkv_proj_weights_t(wq, wk, wv, q, k) if transpose_once else None
+    f32_layer = dt == torch.float32
+    wcat_t = Bn.qkv_proj_weights_t(wq, wk, wv, q, k) if transpose_once and not f32_layer else None
     for s in reversed(starts):
         c = min(C, T - s)
         print(f"[case] {wl.name} chunk {s // C} bwd", flush=True)
         Bn.chunk_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, chunk_start=s, chunk_len=c, q_row_offset=s,
                           softmax_scale=sc)
-        Bn.qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, chunk_start=s, chunk_len=c,
-                        q_row_offset=s, w_cat_t=wcat_t)
+        if transpose_once and f32_layer:
+            proj_bwd_wt_null(Bn, h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, s, c)
+        else:
+            Bn.qkv_proj_bwd(h, wq, wk, wv, q, k, dq, dk, dv, dwq, dwk, dwv, dh, chunk_start=s, chunk_len=c,
+                            q_row_offset=s, w_cat_t=wcat_t)
     torch.cuda.synchronize()
     out = {n: t.float().cpu().numpy().astype(np.float64)
            for n, t in dict(q=q, k=k, v=v, o=o, dwq=dwq, dwk=dwk, dwv=dwv, dh=dh).items()}
@@ -99,13 +115,11 @@ def test_layer_parity(case):
         assert e <= tol, (n_, e)
 
 
-BF16_CASES = [c for c in CASES if c[8] == "bf16"]
-
-
-@pytest.mark.parametrize("case", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_layer_weights_transposed_once(case):
     """qkv_proj_bwd_wt with the transpose written once per sweep gives qkv_proj_bwd's results bit for
-    bit (the same kernels read the same W_cat^T), over ragged sweeps, batch 2 and the 8B dims."""
+    bit (the same kernels read the same W_cat^T), over ragged sweeps, batch 2 and the 8B dims; for
+    float32 layers, called with a NULL transpose, it is qkv_proj_bwd."""
     name, B, T, C, dm, Hq, Hkv, d, dtype = case
     print(f"[case] {name} transpose once", flush=True)
     wl = W.LayerWorkload(name, B, T, C, dm, Hq, Hkv, d, dtype, seed=13)
