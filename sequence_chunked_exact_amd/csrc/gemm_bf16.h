@@ -50,6 +50,7 @@ struct ProjGemmParams {
   int a_rows;                // rows of A (forward, dH; dW: k rows of A) that exist: reads clamp to them
   int b_rows;                // dW: k rows of B per batch entry that exist (reads clamp to them)
   int batch;                 // forward, dH: batch entries in the grid; dW: summed along k
+  int k_last;                // forward, dH: K of the last batch entry when > 0 (a shorter split-k tail)
 };
 
 // Segment of a column given three widths.
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(NG * 256) __attribute__((amdgpu_waves_per_eu(2))) v
   const int gm = MODE == PG_DW ? min(GM, mt - run * GM) : mt;
   const int m0 = (MODE == PG_DW ? run * GM + in_run % gm : rem % mt) * 128;
   const int n0 = (MODE == PG_DW ? in_run / gm : rem / mt) * 128;
-  const int nks = p.K / 64;
+  const int nks = (MODE != PG_DW && p.k_last > 0 && bz == p.batch - 1 ? p.k_last : p.K) / 64;
   const int nk = MODE == PG_DW ? nks * p.batch : nks;
   const int n_pairs = (nk + NG - 1) / NG;  // steps of NG slices
 

@@ -165,14 +165,21 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float* part, floa
 
 constexpr int kWide = 1 << 30;
 
-// Split of the dH product's k range (the vocabulary) into a divisor of its
-// 64-wide slices, so that its few output tiles (rows x d_model) fill the GPU.
+// Split of the dH product's k range (the vocabulary, in 64-wide slices) into
+// S parts of head_kpart elements, the last one shorter where S does not divide
+// the slices: the product has few output tiles (rows x d_model; 32 for a
+// 4096-wide model), and 16 splits make them 512 workgroups, two on every
+// compute unit. (An exact divisor of the LLaMA3 vocabulary's 2004 slices gave
+// at most 12, i.e. 384 workgroups: half the units streamed twice the weight
+// rows of the other half.) S is the largest count up to 16 whose parts are
+// all non-empty.
 int head_splits(int vocab) {
   const int slices = vocab / 64;
   for (int s = 16; s > 1; --s)
-    if (slices % s == 0) return s;
+    if ((s - 1) * ((slices + s - 1) / s) < slices) return s;
   return 1;
 }
+int head_kpart(int vocab, int splits) { return (vocab / 64 + splits - 1) / splits * 64; }
 
 }  // namespace
 
@@ -211,7 +218,7 @@ hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zer
   float* z = (float*)ws;
   bf16* dzg = (bf16*)(ws + head_z_bytes(s));
   float* part = (float*)(ws + head_z_bytes(s) + head_dz_bytes(s));
-  const int S = head_splits(V), kpart = V / S;
+  const int S = head_splits(V), kpart = head_kpart(V, S), klast = V - (S - 1) * kpart;
   const bf16* hp = (const bf16*)h + (size_t)s0 * dm;
 
   // Z = H W^T
@@ -278,6 +285,7 @@ hipError_t head_partition(const HeadShape& s, int s0, int rows, int off, int zer
     hq.M = rows;
     hq.N = dm;
     hq.K = kpart;
+    hq.k_last = klast;
     hq.a_rows = rows;
     hq.batch = S;
     e = pg_launch<PG_DH>(hq, S, CA_KERNEL_HEAD, st);
