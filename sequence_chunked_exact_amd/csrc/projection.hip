@@ -10,8 +10,10 @@
 //   input    dH_in^(i) = G_cat W_cat^T
 // with G_cat the chunk rows of dQ | dK | dV, first rounded to bf16 in a
 // workspace by gcat_kernel (rows up to a multiple of 64, the tail zero), and
-// W_cat^T written there by wt_kernel: read along its rows in 128-byte pieces,
-// W_cat streamed several times slower than its transpose read along k. A
+// W_cat^T written there by wt_kernel, or handed in by the caller, who wrote it
+// once for a whole backward sweep (launch_proj_wt): read along its rows in
+// 128-byte pieces, W_cat streamed several times slower than its transpose read
+// along k. A
 // workgroup of 8 waves owns a 128x128 output tile: two groups of 4 waves (2x2
 // waves of 64x64) take the even and odd 64-deep k slices of slice pairs, which
 // stream by direct global->LDS loads one pair ahead into two statically named
