@@ -286,6 +286,9 @@ def test_lm_head_errors():
     # exponential sum) pairs of up to 16 segments of ps + 64 rows
     assert need == (100 * 1024 * 4 + 255) // 256 * 256 + 128 * 1024 * 2 + 16 * 100 * 256 * 4 + 164 * 16 * 2 * 4
     assert size(ctypes.byref(HD(1, 1024, 256, 1000, b.CA_BF16)), 100) == 0   # vocab % 64
+    # 17 slices of 64: dH in 9 split-k parts (the last one shorter), so 9 partial slabs
+    assert size(ctypes.byref(HD(1, 1024, 256, 1088, b.CA_BF16)), 100) == \
+        (100 * 1088 * 4 + 255) // 256 * 256 + 128 * 1088 * 2 + 9 * 100 * 256 * 4 + 164 * 16 * 2 * 4
     assert size(ctypes.byref(d), 0) == 0
 
     def part(dd=d, row_start=0, rows=100, ws_bytes=need, labels=FAKE, scale=1.0):

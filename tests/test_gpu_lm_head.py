@@ -44,6 +44,9 @@ CASES = [
     ("one_partition_all_rows", 2, 70, 192, 448, 100, 5, 1),
     ("grouped_dw_short_last_group", 1, 250, 256, 1024, 40, 10, 3),
     ("grouped_dw_batch2_group_exceeds_sequence", 2, 130, 128, 512, 32, 0, 8),
+    # 17 vocabulary slices of 64: dH splits into 9 parts of 2 slices, the last of 1 (the GEMM's
+    # shorter last split-k entry)
+    ("uneven_split_vocab_1088", 1, 120, 128, 1088, 50, 4, 1),
 ]
 
 
