@@ -457,12 +457,14 @@ def head_bytes(T, dm, V, ps, group, B=1):
     """Algorithmic HBM bytes of the head's three products over one step: per
     partition of r positions, the logits product reads W^T and H rows and writes
     the float32 logits; dH reads dZ (bf16) and W and writes its split-k partials
-    (12 splits for the LLaMA3 vocabulary); per group of partitions, dW reads dZ
+    (16 splits for the LLaMA3 vocabulary: the largest count up to 16 whose parts of
+    whole 64-wide vocabulary slices are all non-empty); per group of partitions, dW reads dZ
     and H rows and reads + writes the float32 weight gradient. At these sizes
     (about 125 FLOP per byte, under MI355X's ~310 FLOP/B balance of bf16 MFMA to
     HBM) the head is bound by memory."""
     wbytes = V * dm * 2
-    splits = next(s for s in range(16, 0, -1) if (V // 64) % s == 0)
+    n = V // 64
+    splits = next((s for s in range(16, 1, -1) if (s - 1) * ((n + s - 1) // s) < n), 1)
     total = 0
     for s0 in range(0, T, ps):
         r = min(ps, T - s0)
