@@ -361,3 +361,25 @@ def test_sweep_errors():
     assert bwd_(ws=None, ws_bytes=0) == -5
     assert bwd_(ws_bytes=16) == -5
     assert bwd_(dq=None) == -1
+
+
+def test_bench_head_bytes_use_the_library_split_count():
+    # The library's head workspace holds one float32 partial slab of dH per split-k part, so its
+    # size gives the split count; bench.head_bytes must count the same number of partials.
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(__file__))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    HD = b.HeadDesc
+    ps, dm, cap = 100, 256, 1024
+    for V in (64, 448, 1024, 1088, 2048, 2240, 64 * 167, 32000 // 64 * 64, 128256):
+        base = (ps * V * 4 + 255) // 256 * 256 + 128 * V * 2 + 164 * 16 * 2 * 4
+        need = lib.lm_head_sft_workspace_size(ctypes.byref(HD(1, cap, dm, V, b.CA_BF16)), ps)
+        slab = ps * dm * 4
+        lib_splits = (need - base) // slab
+        assert need == base + (lib_splits * slab + 255) // 256 * 256, V
+        # bench's bytes with T = ps (one partition, one dW group) minus everything but the partials
+        t = bench.head_bytes(ps, dm, V, ps, 1)
+        rest = 2 * V * dm * 2 + ps * dm * 2 + ps * V * 4 + ps * V * 2 + ps * V * 2 + ps * dm * 2 + 2 * V * dm * 4
+        assert (t - rest) == lib_splits * ps * dm * 4, (V, lib_splits, (t - rest) // (ps * dm * 4))
